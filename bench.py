@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the OSCAR INT2 decode-attention hot path on one MI355X.
+
+A step is one decode-attention pass (oscar_decode_attention: q rotation,
+INT2 history split-K, BF16 sink/recent, LSE merge) of one layer for the whole
+batch; the demote workload adds one oscar_append_demote per step.  The pools
+are built on the GPU by the library's own write path (oscar_quantize_pack,
+oscar_write_bf16) from seeded synthetic tensors.
+
+Timing protocol: the pool working set of one step (58.7 MB at 100K tokens)
+fits the 256 MB Infinity Cache, so steps rotate through independent pool
+copies totalling >= 2 GiB (cold-cache); the K timed steps are replayed from
+a HIP graph and bracketed by HIP events on the launch stream.  The median of
+several repeats is reported; warm (single copy) and eager-launch numbers are
+reported beside it.
+
+Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "INT2 decode-attn KV GB/s & tokens/s at 100K ctx; % of HBM peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3-8b-l100k")
+    ap.add_argument("--cold-bytes", type=float, default=2 * 2**30)
+    ap.add_argument("--repeats", type=int, default=5)
+    ap.add_argument("--no-bf16", action="store_true", help="skip the BF16-only comparator")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run N eager decode steps on one copy (for rocprofv3), print nothing else")
+    return ap.parse_args()
+
+
+class Decoder:
+    """Pre-marshalled oscar_decode_attention calls, one per pool copy."""
+
+    def __init__(self, oscar, pool, wl, q, lens, copies, int2_pool, bf16_pool, r_k, out, ws, bf16_only=False):
+        import torch
+        lib = oscar.load()
+        self.lib = lib
+        self.bf16_only = bf16_only
+        self.torch = torch
+        self.args = []
+        for c in copies:
+            if bf16_only:
+                self.args.append((pool.handle, wl.batch, max(wl.seq_lens), q.data_ptr(), lens.data_ptr(),
+                                  c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], bf16_pool.shape[0],
+                                  bf16_pool.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()))
+            else:
+                self.args.append((pool.handle, wl.batch, max(wl.seq_lens), q.data_ptr(), lens.data_ptr(),
+                                  c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], bf16_pool.shape[0],
+                                  c["int2_pt"].data_ptr(), c["int2_pt"].shape[1], int2_pool.shape[0],
+                                  bf16_pool.data_ptr(), int2_pool.data_ptr(), r_k.data_ptr(), None,
+                                  out.data_ptr(), ws.data_ptr(), ws.numel()))
+        self.fn = lib.oscar_bf16_decode_attention if bf16_only else lib.oscar_decode_attention
+
+    def __call__(self, i):
+        # launch on the current stream (the capture stream inside a graph capture)
+        st = self.fn(*self.args[i % len(self.args)], self.torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(self.lib.oscar_last_error().decode())
+
+
+def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0):
+    """n_copies independent pools of one workload, written by the library."""
+    import numpy as np
+    import torch
+    hkv, d = wl.num_kv_heads, wl.head_dim
+    rng = np.random.Generator(np.random.PCG64(seed + 300))
+    c = inp.calib
+    r_k = torch.as_tensor(c.r_k).cuda()
+    tau_k = torch.as_tensor(c.tau_k).cuda()
+    tau_v = torch.as_tensor(c.tau_v).cuda()
+    max_pages = max((L + 15) // 16 for L in wl.seq_lens)
+    b16_lists, i2_counts = [], []
+    for L in wl.seq_lens:
+        if bf16_only:
+            b16_lists.append(list(range((L + 15) // 16)))
+            i2_counts.append(0)
+        else:
+            r0 = max(wl.sink, L - wl.recent)
+            b16_lists.append([p for p in range((L + 15) // 16)
+                              if p * 16 < min(L, wl.sink) or ((p + 1) * 16 > r0 and p * 16 < L)])
+            i2_counts.append((wl.hist_len(L) + 15) // 16)
+    n16 = sum(len(x) for x in b16_lists) * n_copies
+    n2 = sum(i2_counts) * n_copies
+    bf16_pool = torch.empty((max(n16, 1), pool.bf16_page_bytes), dtype=torch.uint8, device="cuda")
+    int2_pool = torch.empty((max(n2, 1), pool.int2_page_bytes), dtype=torch.uint8, device="cuda")
+    perm16 = rng.permutation(max(n16, 1))
+    perm2 = rng.permutation(max(n2, 1))
+    p16 = p2 = 0
+    copies = []
+    for _ in range(n_copies):
+        bpt = np.full((wl.batch, max_pages + 1), -1, np.int32)
+        ipt = np.full((wl.batch, max(max(i2_counts), 1)), -1, np.int32)
+        for b in range(wl.batch):
+            for lp in b16_lists[b]:
+                bpt[b, lp] = perm16[p16]
+                p16 += 1
+            for lp in range(i2_counts[b]):
+                ipt[b, lp] = perm2[p2]
+                p2 += 1
+        cp = {"bf16_pt": torch.from_numpy(bpt).cuda(), "int2_pt": torch.from_numpy(ipt).cuda()}
+        for b, L in enumerate(wl.seq_lens):
+            k, v = inp.k[b], inp.v[b]
+            if bf16_only:
+                oscar.oscar_write_bf16(pool, k[:L].contiguous(), v[:L].contiguous(), 0, cp["bf16_pt"][b], bf16_pool)
+                continue
+            sink = min(L, wl.sink)
+            oscar.oscar_write_bf16(pool, k[:sink].contiguous(), v[:sink].contiguous(), 0, cp["bf16_pt"][b], bf16_pool)
+            r0 = wl.recent_start(L)
+            if r0 < L:
+                oscar.oscar_write_bf16(pool, k[r0:L].contiguous(), v[r0:L].contiguous(), r0, cp["bf16_pt"][b],
+                                       bf16_pool)
+            h = wl.hist_len(L)
+            if h:
+                oscar.oscar_quantize_pack(pool, k[wl.sink:wl.sink + h].contiguous(), v[wl.sink:wl.sink + h].contiguous(),
+                                          cp["int2_pt"][b, :i2_counts[b]].contiguous(), int2_pool, r_k, tau_k, tau_v)
+        copies.append(cp)
+    torch.cuda.synchronize()
+    return copies, int2_pool, bf16_pool, r_k
+
+
+def time_steps(step, n_steps, warmup, repeats, use_graph=True):
+    """Median and min ms per step over `repeats` runs of n_steps steps."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in range(n_steps):
+                    step(warmup + i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(n_steps):
+                step(warmup + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / n_steps)
+    return statistics.median(times), min(times)
+
+
+def copy_ceiling_gbps():
+    import torch
+    n = 2 * 2**30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 5
+    del x, y
+    return 2 * n / ms / 1e6
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.h", "kernels.h"):
+        h.update(open(os.path.join(ROOT, "long_context_decode_oscar_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, if they
+    were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_source_sha") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp):
+    """The oracle's decode (R1-R3) timed on this host on a bounded sample:
+    two of the KV heads (their query heads) over the full context."""
+    import numpy as np
+    import oracle
+    n_kv = 2
+    g = wl.gqa
+    seqs = []
+    L = wl.seq_lens[0]
+    c = inp.calib
+    k = inp.k[0][:, :n_kv].float().cpu().numpy()
+    v = inp.v[0][:, :n_kv].float().cpu().numpy()
+    s = oracle.SeqPool(n_kv, wl.head_dim, wl.group_size, wl.sink, wl.recent)
+    s.prefill(k, v, c.r_k[:n_kv], c.tau_k[:n_kv], c.tau_v[:n_kv])
+    seqs.append(s)
+    q = inp.q[:1, : n_kv * g].float().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.decode_attention(seqs, q, c.r_k[:n_kv])
+    dt = time.perf_counter() - t0
+    kv = wl.kv_bytes()
+    sample_bytes = kv["total"] * n_kv / wl.num_kv_heads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle decode (dequantize, inverse-rotate, one softmax) of {n_kv} of "
+                      f"{wl.num_kv_heads} KV heads ({n_kv * g} query heads) at {L} tokens; KV bytes of that "
+                      f"share / wall time {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_decode_oscar_amd as oscar
+    from synthetic import CONFIGS, draw_inputs
+
+    oscar.load()
+    wl = CONFIGS[args.workload]
+    kv = wl.kv_bytes()
+    log(f"workload {wl.name}: KV bytes/step {kv['total']:,} (INT2 {kv['int2']:,}, BF16 {kv['bf16']:,})")
+    inp = draw_inputs(wl, device="cuda")
+    pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
+                                            wl.sink, wl.recent, 1, 0.0))
+    n_copies = max(1, math.ceil(args.cold_bytes / kv["total"]))
+    if args.profile_steps:
+        n_copies = 1
+    copies, int2_pool, bf16_pool, r_k = build_pools(oscar, pool, wl, inp, n_copies, seed=wl.seed)
+    log(f"built {n_copies} pool copies ({n_copies * kv['total'] / 2**30:.2f} GiB of KV)")
+    q = inp.q.contiguous()
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = pool.alloc_workspace(wl.batch, max(wl.seq_lens))
+    dec = Decoder(oscar, pool, wl, q, lens, copies, int2_pool, bf16_pool, r_k, out, ws)
+    if args.profile_steps:
+        for i in range(args.profile_steps):
+            dec(i)
+        torch.cuda.synchronize()
+        log(f"profile run: {args.profile_steps} decode steps done")
+        return
+
+    ms, ms_min = time_steps(dec, args.steps, args.warmup, args.repeats, use_graph=True)
+    log(f"INT2 decode (graph, cold): {ms * 1e3:.2f} us/step (min {ms_min * 1e3:.2f})")
+    ms_eager, _ = time_steps(dec, args.steps, args.warmup, 3, use_graph=False)
+    log(f"INT2 decode (eager, cold): {ms_eager * 1e3:.2f} us/step")
+    warm = Decoder(oscar, pool, wl, q, lens, copies[:1], int2_pool, bf16_pool, r_k, out, ws)
+    ms_warm, _ = time_steps(warm, args.steps, args.warmup, 3, use_graph=True)
+    log(f"INT2 decode (graph, warm single copy): {ms_warm * 1e3:.2f} us/step")
+
+    gbps = kv["total"] / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int2-kv/int8+bf16-mfma/fp32-acc", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "group_size": wl.group_size, "context": list(wl.seq_lens)[:4],
+                   "sink": wl.sink, "recent": wl.recent, "page_size": 16, "pool_copies": n_copies,
+                   "timing": "HIP-graph replay of the timed steps, cold cache (rotating pool copies)"},
+        "tokens_per_s": round(wl.batch / (ms * 1e-3), 1),
+        "kv_tokens_scanned_per_s": round(sum(wl.seq_lens) / (ms * 1e-3), 1),
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "kv_bytes_per_step": kv["total"],
+        "eager_ms_per_step": round(ms_eager, 6),
+        "warm_ms_per_step": round(ms_warm, 6),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_for(wl.name),
+                     "kernel": "k_decode (INT2 split-K + BF16 sink/recent + LSE merge, one launch per step)"},
+    }
+    if not args.no_bf16:
+        del copies
+        torch.cuda.empty_cache()
+        n16 = max(1, math.ceil(args.cold_bytes / kv["bf16_only_total"]))
+        bcopies, _, bpool, _ = build_pools(oscar, pool, wl, inp, n16, bf16_only=True, seed=wl.seed + 1)
+        bws = pool.alloc_workspace(wl.batch, max(wl.seq_lens), bf16_only=True)
+        bdec = Decoder(oscar, pool, wl, q, lens, bcopies, int2_pool, bpool, r_k, out, bws, bf16_only=True)
+        ms16, _ = time_steps(bdec, max(20, args.steps // 4), args.warmup, args.repeats, use_graph=True)
+        log(f"BF16-only decode (graph, cold): {ms16 * 1e3:.2f} us/step")
+        result["bf16_comparator"] = {"ms_per_step": round(ms16, 6),
+                                     "kv_GBps": round(kv["bf16_only_total"] / (ms16 * 1e-3) / 1e9, 2),
+                                     "kv_bytes_per_step": kv["bf16_only_total"], "pool_copies": n16,
+                                     "int2_speedup": round(ms16 / ms, 3)}
+        del bcopies, bpool
+        torch.cuda.empty_cache()
+    result["copy_ceiling_GBps"] = round(copy_ceiling_gbps(), 1)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

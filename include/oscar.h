@@ -1,0 +1,220 @@
+/*
+ * oscar.h -- C ABI of the OSCAR INT2 KV-cache decode library for AMD MI355X
+ * (gfx950).
+ *
+ * The method (MarkTechPost article on OSCAR, "The Serving System"; ModelScope/
+ * CSDN page, design section): every sequence keeps a three-segment token pool,
+ *   BF16 sink (first S0 tokens) | INT2 history | BF16 recent (last W tokens),
+ * new tokens enter the recent window and the oldest recent token is rotated by
+ * R_K (keys), clipped to a per-head threshold, quantized per token to 2-bit
+ * codes with a bf16 scale and zero per group of G channels, packed 4 codes per
+ * byte and demoted into the history.  Decode attends the INT2 and BF16
+ * segments separately and merges the partial results by online softmax.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Device pointers are HIP device memory owned by the caller; the library
+ *    never allocates or frees device memory.  Host pointers are marked "host".
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream).  Kernel faults surface at the caller's next synchronization.
+ *  - bf16 tensors are uint16 bit patterns (IEEE binary32 upper halves).
+ *  - Row-vector convention: a rotated vector is x' = x R with R stored
+ *    row-major [D_in][D_out] as fp32, one matrix per KV head: R[Hkv][D][D].
+ *  - Query head h reads KV head h / (Hq / Hkv).
+ *  - Positions of a sequence of length L (L counts every stored token):
+ *      sink [0, min(L, S0)), history [S0, max(S0, L-W)),
+ *      recent [max(S0, L-W), L).
+ *    Keys in the BF16 segments are unrotated; values are stored in the pool's
+ *    V basis in every segment (R_V absorbed into the projection weights,
+ *    MarkTechPost article, "The Serving System"), and decode output is in that
+ *    basis.
+ *  - Errors: functions return an oscar_status; arguments are validated on the
+ *    host before anything is launched, and nothing is launched on error.
+ *    oscar_last_error() gives a human-readable reason (thread-local).
+ *
+ * Pool layout (16-token pages, all KV heads of a page together)
+ * -------------------------------------------------------------
+ * BF16 pool: page p occupies bf16_page_bytes = Hkv * 64*D bytes; head k's
+ *   block starts at (p*Hkv + k) * 64*D and holds
+ *     K: [16 tokens][D] bf16 (32*D bytes), then
+ *     V: [4 token quads][D channels][4 tokens] bf16 (32*D bytes)
+ *   (token s of the page is quad s/4, slot s%4).  A sequence's BF16 page table
+ *   maps logical page pos/16 to a physical page; only logical pages that
+ *   overlap the sink or recent segment are read or written.
+ *
+ * INT2 pool: page p occupies int2_page_bytes = Hkv * (8*D + 128*n_g) bytes
+ *   (n_g = D/G); head k's block starts at (p*Hkv + k) * (8*D + 128*n_g):
+ *     codes: 64 records of D/8 bytes.  Record lam = 16*j + r (j = 0..3,
+ *       r = 0..15) holds
+ *       - K part, D/64 little-endian 32-bit words: word w holds the K codes of
+ *         token r for channels w*64 + j*16 + m, m = 0..15, in bits 2m..2m+1;
+ *       - V part, D/64 words: word w holds the V codes of tokens 4j..4j+3 for
+ *         channels c = (4w + b)*16 + r, b = 0..3; token 4j+i of channel block
+ *         b sits in bits 16*(i&1) + 2*(2b + (i>>1)).
+ *     scales: [4 token quads][K: 4 tokens][n_g][scale, zero] bf16, then
+ *       [V: 4 tokens][n_g][scale, zero] bf16, i.e. 32*n_g bytes per quad.
+ *   A dequantized value is scale * (code - zero).  The history token at
+ *   position pos lives in logical INT2 page (pos - S0)/16, slot (pos - S0)%16.
+ *   Bytes per history token and head: 2*D/4 + 8*n_g (72 at D = G = 128,
+ *   2.25 bits per element).
+ *
+ * Page tables are int32 [batch][stride] (host value -1 or any id outside
+ * [0, num_pages) marks an absent page: its tokens are skipped, never read).
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OSCAR_OK = 0,
+  OSCAR_ERR_INVALID = 1,     /* null pointer, bad shape, misaligned buffer */
+  OSCAR_ERR_UNSUPPORTED = 2, /* valid request outside what this build implements */
+  OSCAR_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  OSCAR_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} oscar_status;
+
+/* Configuration of one attention layer's pool.
+ * Supported: head_dim 64 or 128; group_size 64 or 128 dividing head_dim;
+ * num_q_heads / num_kv_heads in {2, 4, 8}; page_size 16; sink_tokens a
+ * multiple of 16 (64 by default, MarkTechPost article, "The Serving System");
+ * recent_tokens >= 1 (256 by default, same section); v_absorbed = 1. */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t group_size;
+  int32_t page_size;
+  int32_t sink_tokens;
+  int32_t recent_tokens;
+  int32_t v_absorbed;
+  float sm_scale; /* softmax scale; 0 selects 1/sqrt(head_dim) */
+} oscar_config;
+
+/* Byte sizes of the pool layout described above, filled by oscar_pool_create. */
+typedef struct {
+  size_t int2_page_bytes;       /* one INT2 page, all KV heads */
+  size_t bf16_page_bytes;       /* one BF16 page, all KV heads */
+  size_t int2_head_block_bytes; /* one KV head's block inside an INT2 page */
+  size_t bf16_head_block_bytes; /* one KV head's block inside a BF16 page */
+} oscar_layout;
+
+/* Opaque host-side handle holding a validated, immutable configuration. */
+typedef struct oscar_pool oscar_pool;
+
+/* Validate `cfg` and create a handle (host memory only).  `layout` may be
+ * NULL.  Errors: OSCAR_ERR_INVALID for null/negative fields,
+ * OSCAR_ERR_UNSUPPORTED for shapes outside the supported set. */
+oscar_status oscar_pool_create(const oscar_config* cfg, oscar_pool** out, oscar_layout* layout);
+void oscar_pool_destroy(oscar_pool* pool);
+
+/* Bytes of device workspace oscar_decode_attention (bf16_only = 0) or
+ * oscar_bf16_decode_attention (bf16_only = 1) needs for `batch` sequences of
+ * at most `max_seq_len` tokens.  The workspace must be zero-filled before its
+ * first use; each successful call leaves its counters zero again, so one
+ * zero-fill serves every later call.  Calls that share a workspace must not
+ * overlap in time. */
+oscar_status oscar_decode_workspace_bytes(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
+                                          int32_t bf16_only, size_t* bytes);
+
+/* Decode-time write path (ModelScope/CSDN page, design section: new tokens
+ * are written to the recent window; the oldest recent token is rotated,
+ * clipped, quantized, packed and demoted into the INT2 history).
+ * For every sequence b with length L_b = seq_lens[b] BEFORE the call:
+ *   - writes k_new[b], v_new[b] (bf16 [batch][Hkv][D]; v_new in the pool's V
+ *     basis) at position L_b of the BF16 pool;
+ *   - if d = L_b - W >= S0, reads token d's K and V from the BF16 pool and
+ *     writes  k_d R_K[k]  (fp32 accumulation) and  v_d  (absorbed), each
+ *     clipped to +-tau[k] and quantized with bf16 scale = bf16((max-min)/3)
+ *     (1 if max = min) and zero = bf16(-min/scale), code =
+ *     clamp(rne(c/scale + zero), 0, 3), into INT2 history slot d - S0.
+ * seq_lens is not advanced; the caller owns lengths.  r_k: fp32 [Hkv][D][D];
+ * r_v must be NULL (absorbed V); tau_k, tau_v: fp32 [Hkv] (+inf disables).
+ * Page tables must hold a valid entry for every page written.  Sequences that
+ * share a page must not demote into it in the same call. */
+oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const void* k_new, const void* v_new,
+                                 const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                 int32_t bf16_pt_stride, int32_t bf16_num_pages,
+                                 const int32_t* int2_page_table, int32_t int2_pt_stride,
+                                 int32_t int2_num_pages, void* bf16_pool, void* int2_pool, const float* r_k,
+                                 const float* r_v, const float* tau_k, const float* tau_v, void* stream);
+
+/* Decode attention over the three-segment pool (ModelScope/CSDN page, design
+ * section: INT2 kernel unpacks and dequantizes, BF16 kernel handles sink and
+ * recent, online-softmax merge; MarkTechPost article, "Outcome": the online
+ * rotation is absorbed into the decode kernels).  For each sequence b and
+ * query head h:
+ *   out[b][h] = softmax_t(sm * q.k_t) . v_t  over all L_b tokens,
+ * with history keys k^ = s(code - z) R_K^T (computed as q' = q R_K against
+ * the codes) and history values s(code - z).
+ * q: bf16 [batch][Hq][D] (model basis); seq_lens: int32 [batch] device, L_b
+ * counting the current token, at most max_seq_len (longer lengths are
+ * clamped to what the page tables can address); out: bf16 [batch][Hq][D].
+ * workspace: oscar_decode_workspace_bytes(pool, batch, max_seq_len, 0) bytes,
+ * 256-byte aligned, zero-filled before first use. */
+oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
+                                    const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                    int32_t bf16_pt_stride, int32_t bf16_num_pages,
+                                    const int32_t* int2_page_table, int32_t int2_pt_stride,
+                                    int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
+                                    const float* r_k, const float* r_v, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Log-sum-exp merge of partial attentions (ModelScope/CSDN page, design
+ * section, online-softmax merge).  Row i (0 <= i < rows) merges partials
+ * row_offsets[i] .. row_offsets[i+1]-1:
+ *   out[i] = sum_j exp(lse_j - LSE) o_j,  LSE = ln sum_j exp(lse_j);
+ * a partial with lse = -inf contributes nothing; a row with no finite lse is
+ * written as zeros.  row_offsets: int32 [rows+1] device (non-decreasing,
+ * row_offsets[0] = 0); o_partials: fp32 [nnz][head_dim] normalized outputs;
+ * lse_partials: fp32 [nnz] natural log; out: bf16 [rows][head_dim].
+ * head_dim must be 64 or 128. */
+oscar_status oscar_merge(int32_t rows, int32_t head_dim, const int32_t* row_offsets, const float* o_partials,
+                         const float* lse_partials, void* out, void* stream);
+
+/* Bulk write path (prefill of history): quantizes tokens 0..num_tokens-1 of
+ * dense K and V (bf16 [num_tokens][Hkv][D]; V already in the pool's V basis)
+ * exactly as oscar_append_demote quantizes one token, with K rotated by R_K
+ * on the matrix cores, and writes token t to slot t%16 of INT2 page
+ * page_ids[t/16] (int32 device [ceil(num_tokens/16)]).  Pages are written
+ * whole; token slots past num_tokens in the last page are zero-filled. */
+oscar_status oscar_quantize_pack(const oscar_pool* pool, int32_t num_tokens, const void* k, const void* v,
+                                 const int32_t* page_ids, int32_t int2_num_pages, void* int2_pool,
+                                 const float* r_k, const float* r_v, const float* tau_k, const float* tau_v,
+                                 void* stream);
+
+/* Prefill of BF16 pages: writes tokens t = 0..num_tokens-1 of dense k and v
+ * (bf16 [num_tokens][Hkv][D], v in the pool's V basis) to positions
+ * first_position + t of one sequence, i.e. to slot (first_position + t) % 16
+ * of BF16 page bf16_page_table[(first_position + t) / 16] (int32 device
+ * [bf16_pt_stride]).  Tokens whose page entry is outside [0, bf16_num_pages)
+ * or past the table are skipped.  Used to stage the sink and recent windows
+ * (and, for the BF16-only comparator, whole sequences). */
+oscar_status oscar_write_bf16(const oscar_pool* pool, int32_t num_tokens, int32_t first_position, const void* k,
+                              const void* v, const int32_t* bf16_page_table, int32_t bf16_pt_stride,
+                              int32_t bf16_num_pages, void* bf16_pool, void* stream);
+
+/* All-BF16 paged decode (the comparator for the INT2 path): plain softmax
+ * attention over every position 0..L_b-1 stored in the BF16 pool (layout
+ * above), through bf16_page_table.  Arguments as oscar_decode_attention;
+ * workspace from oscar_decode_workspace_bytes(..., bf16_only = 1). */
+oscar_status oscar_bf16_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
+                                         const void* q, const int32_t* seq_lens,
+                                         const int32_t* bf16_page_table, int32_t bf16_pt_stride,
+                                         int32_t bf16_num_pages, const void* bf16_pool, void* out,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+const char* oscar_status_string(oscar_status status);
+/* Reason for the last error returned on this thread ("" if none). */
+const char* oscar_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

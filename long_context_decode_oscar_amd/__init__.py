@@ -1,0 +1,240 @@
+"""Python binding of liboscar, the OSCAR INT2 KV-cache decode library for
+AMD MI355X (gfx950).
+
+The binding only marshals arguments: it checks dtypes, shapes and devices of
+torch tensors, passes their device pointers and the current HIP stream to the
+C ABI (include/oscar.h), and raises on a non-OK status.  Every step of the
+hot path runs in the library's HIP kernels.  The shared library must have
+been built (``python -m long_context_decode_oscar_amd.build``); nothing falls
+back to another implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboscar.so")
+
+OSCAR_OK, OSCAR_ERR_INVALID, OSCAR_ERR_UNSUPPORTED, OSCAR_ERR_WORKSPACE, OSCAR_ERR_HIP = range(5)
+
+EXPORTED = (
+    "oscar_pool_create", "oscar_pool_destroy", "oscar_decode_workspace_bytes", "oscar_append_demote",
+    "oscar_decode_attention", "oscar_merge", "oscar_quantize_pack", "oscar_bf16_decode_attention",
+    "oscar_write_bf16", "oscar_status_string", "oscar_last_error",
+)
+
+
+class OscarError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        self.status = status
+        super().__init__(f"{func}: status {status} ({msg})")
+
+
+class CConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("group_size", ctypes.c_int32), ("page_size", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
+        ("recent_tokens", ctypes.c_int32), ("v_absorbed", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+    ]
+
+
+class CLayout(ctypes.Structure):
+    _fields_ = [
+        ("int2_page_bytes", ctypes.c_size_t), ("bf16_page_bytes", ctypes.c_size_t),
+        ("int2_head_block_bytes", ctypes.c_size_t), ("bf16_head_block_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load liboscar.so and declare the C prototypes.  Raises if missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"liboscar.so not built at {path}; run python -m long_context_decode_oscar_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I, S, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    lib.oscar_pool_create.argtypes = [ctypes.POINTER(CConfig), ctypes.POINTER(P), ctypes.POINTER(CLayout)]
+    lib.oscar_pool_destroy.argtypes = [P]
+    lib.oscar_pool_destroy.restype = None
+    lib.oscar_decode_workspace_bytes.argtypes = [P, I, I, I, ctypes.POINTER(S)]
+    lib.oscar_append_demote.argtypes = [P, I, P, P, P, P, I, I, P, I, I, P, P, P, P, P, P, P]
+    lib.oscar_decode_attention.argtypes = [P, I, I, P, P, P, I, I, P, I, I, P, P, P, P, P, P, S, P]
+    lib.oscar_merge.argtypes = [I, I, P, P, P, P, P]
+    lib.oscar_quantize_pack.argtypes = [P, I, P, P, P, I, P, P, P, P, P, P]
+    lib.oscar_bf16_decode_attention.argtypes = [P, I, I, P, P, P, I, I, P, P, P, S, P]
+    lib.oscar_write_bf16.argtypes = [P, I, I, P, P, P, I, I, P, P]
+    lib.oscar_status_string.argtypes = [ctypes.c_int]
+    lib.oscar_status_string.restype = ctypes.c_char_p
+    lib.oscar_last_error.argtypes = []
+    lib.oscar_last_error.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name not in ("oscar_pool_destroy", "oscar_status_string", "oscar_last_error"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, func: str):
+    if status != OSCAR_OK:
+        lib = load()
+        raise OscarError(status, func, lib.oscar_last_error().decode() or lib.oscar_status_string(status).decode())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t, name, dtype=None, device_needed=True):
+    import torch
+    if t is None:
+        return None
+    if device_needed and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+@dataclasses.dataclass(frozen=True)
+class PoolConfig:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    group_size: int
+    page_size: int = 16
+    sink_tokens: int = 64
+    recent_tokens: int = 256
+    v_absorbed: int = 1
+    sm_scale: float = 0.0
+
+
+class OscarPool:
+    """Handle from oscar_pool_create (host-only, immutable configuration)."""
+
+    def __init__(self, cfg: PoolConfig):
+        lib = load()
+        self.cfg = cfg
+        self._c = CConfig(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.group_size, cfg.page_size,
+                          cfg.sink_tokens, cfg.recent_tokens, cfg.v_absorbed, cfg.sm_scale)
+        h = ctypes.c_void_p()
+        lay = CLayout()
+        _check(lib.oscar_pool_create(ctypes.byref(self._c), ctypes.byref(h), ctypes.byref(lay)), "oscar_pool_create")
+        self.handle = h
+        self.int2_page_bytes = lay.int2_page_bytes
+        self.bf16_page_bytes = lay.bf16_page_bytes
+        self.int2_head_block_bytes = lay.int2_head_block_bytes
+        self.bf16_head_block_bytes = lay.bf16_head_block_bytes
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.oscar_pool_destroy(self.handle)
+            self.handle = None
+
+    def workspace_bytes(self, batch: int, max_seq_len: int, bf16_only: bool = False) -> int:
+        n = ctypes.c_size_t()
+        _check(load().oscar_decode_workspace_bytes(self.handle, batch, max_seq_len, int(bf16_only), ctypes.byref(n)),
+               "oscar_decode_workspace_bytes")
+        return n.value
+
+    def alloc_workspace(self, batch: int, max_seq_len: int, bf16_only: bool = False, device="cuda"):
+        import torch
+        n = self.workspace_bytes(batch, max_seq_len, bf16_only)
+        return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def oscar_pool_create(cfg: PoolConfig) -> OscarPool:
+    return OscarPool(cfg)
+
+
+def _pages(pool_tensor, page_bytes):
+    return pool_tensor.numel() // page_bytes
+
+
+def oscar_append_demote(pool: OscarPool, k_new, v_new, seq_lens, bf16_page_table, int2_page_table, bf16_pool,
+                        int2_pool, r_k, tau_k, tau_v, r_v=None, stream=None):
+    import torch
+    b = k_new.shape[0]
+    _check(load().oscar_append_demote(
+        pool.handle, b, _ptr(k_new, "k_new", torch.bfloat16), _ptr(v_new, "v_new", torch.bfloat16),
+        _ptr(seq_lens, "seq_lens", torch.int32),
+        _ptr(bf16_page_table, "bf16_page_table", torch.int32), bf16_page_table.shape[1],
+        _pages(bf16_pool, pool.bf16_page_bytes),
+        _ptr(int2_page_table, "int2_page_table", torch.int32), int2_page_table.shape[1],
+        _pages(int2_pool, pool.int2_page_bytes),
+        _ptr(bf16_pool, "bf16_pool", torch.uint8), _ptr(int2_pool, "int2_pool", torch.uint8),
+        _ptr(r_k, "r_k", torch.float32), _ptr(r_v, "r_v", torch.float32),
+        _ptr(tau_k, "tau_k", torch.float32), _ptr(tau_v, "tau_v", torch.float32), _stream(stream)),
+        "oscar_append_demote")
+
+
+def oscar_decode_attention(pool: OscarPool, q, seq_lens, max_seq_len: int, bf16_page_table, int2_page_table,
+                           bf16_pool, int2_pool, r_k, out, workspace, r_v=None, stream=None):
+    import torch
+    _check(load().oscar_decode_attention(
+        pool.handle, q.shape[0], int(max_seq_len), _ptr(q, "q", torch.bfloat16), _ptr(seq_lens, "seq_lens", torch.int32),
+        _ptr(bf16_page_table, "bf16_page_table", torch.int32), bf16_page_table.shape[1],
+        _pages(bf16_pool, pool.bf16_page_bytes),
+        _ptr(int2_page_table, "int2_page_table", torch.int32), int2_page_table.shape[1],
+        _pages(int2_pool, pool.int2_page_bytes),
+        _ptr(bf16_pool, "bf16_pool", torch.uint8), _ptr(int2_pool, "int2_pool", torch.uint8),
+        _ptr(r_k, "r_k", torch.float32), _ptr(r_v, "r_v", torch.float32), _ptr(out, "out", torch.bfloat16),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)),
+        "oscar_decode_attention")
+    return out
+
+
+def oscar_bf16_decode_attention(pool: OscarPool, q, seq_lens, max_seq_len: int, bf16_page_table, bf16_pool, out,
+                                workspace, stream=None):
+    import torch
+    _check(load().oscar_bf16_decode_attention(
+        pool.handle, q.shape[0], int(max_seq_len), _ptr(q, "q", torch.bfloat16), _ptr(seq_lens, "seq_lens", torch.int32),
+        _ptr(bf16_page_table, "bf16_page_table", torch.int32), bf16_page_table.shape[1],
+        _pages(bf16_pool, pool.bf16_page_bytes), _ptr(bf16_pool, "bf16_pool", torch.uint8),
+        _ptr(out, "out", torch.bfloat16), _ptr(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)),
+        "oscar_bf16_decode_attention")
+    return out
+
+
+def oscar_merge(row_offsets, o_partials, lse_partials, out, stream=None):
+    import torch
+    rows, d = out.shape
+    _check(load().oscar_merge(
+        rows, d, _ptr(row_offsets, "row_offsets", torch.int32), _ptr(o_partials, "o_partials", torch.float32),
+        _ptr(lse_partials, "lse_partials", torch.float32), _ptr(out, "out", torch.bfloat16), _stream(stream)),
+        "oscar_merge")
+    return out
+
+
+def oscar_quantize_pack(pool: OscarPool, k, v, page_ids, int2_pool, r_k, tau_k, tau_v, r_v=None, stream=None):
+    import torch
+    _check(load().oscar_quantize_pack(
+        pool.handle, k.shape[0], _ptr(k, "k", torch.bfloat16), _ptr(v, "v", torch.bfloat16),
+        _ptr(page_ids, "page_ids", torch.int32), _pages(int2_pool, pool.int2_page_bytes),
+        _ptr(int2_pool, "int2_pool", torch.uint8), _ptr(r_k, "r_k", torch.float32), _ptr(r_v, "r_v", torch.float32),
+        _ptr(tau_k, "tau_k", torch.float32), _ptr(tau_v, "tau_v", torch.float32), _stream(stream)),
+        "oscar_quantize_pack")
+
+
+def oscar_write_bf16(pool: OscarPool, k, v, first_position: int, bf16_page_table_row, bf16_pool, stream=None):
+    """Stage dense bf16 tokens k, v [T, Hkv, D] at positions first_position..
+    of one sequence (bf16_page_table_row: int32 [stride])."""
+    import torch
+    _check(load().oscar_write_bf16(
+        pool.handle, k.shape[0], int(first_position), _ptr(k, "k", torch.bfloat16), _ptr(v, "v", torch.bfloat16),
+        _ptr(bf16_page_table_row, "bf16_page_table_row", torch.int32), bf16_page_table_row.numel(),
+        _pages(bf16_pool, pool.bf16_page_bytes), _ptr(bf16_pool, "bf16_pool", torch.uint8), _stream(stream)),
+        "oscar_write_bf16")

@@ -1,0 +1,411 @@
+// Host side of liboscar: argument validation, pool layout, split-K planning,
+// workspace layout and kernel launches behind the C ABI of include/oscar.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <new>
+#include <string>
+
+#include "../../include/oscar.h"
+#include "common.h"
+#include "kernels.h"
+
+struct oscar_pool {
+  oscar_config cfg;
+  int n_groups;
+  int gqa;
+  float sm_scale;
+  oscar_layout layout;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+oscar_status fail(oscar_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+oscar_status ok() {
+  g_err.clear();
+  return OSCAR_OK;
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+oscar_status check_hip(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(OSCAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Number of compute units, for sizing the split-K grid (256 on MI355X).
+int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                 hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return (s && *s) ? atoi(s) : dflt;
+}
+
+constexpr int kMaxChunks = 1024;
+
+struct Plan {
+  int n_bf16_units, bf16_pages_per_unit, max_chunks, pages_per_chunk, units, grid;
+  size_t off_counters, off_lse, off_o, bytes;
+};
+
+int slots_for(int gqa) { return (16 / gqa) < 4 ? 16 / gqa : 4; }
+
+// Split-K plan.  Every (sequence, KV head) gets n_bf16_units workgroups for
+// its sink + recent pages and up to max_chunks INT2 chunks of
+// pages_per_chunk history pages; the chunk size is uniform so that shorter
+// sequences simply use fewer chunks.  The grid aims at `target` workgroups
+// (about one per compute unit, overridable with OSCAR_TARGET_WGS).
+Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
+  const oscar_config& c = pool->cfg;
+  Plan pl{};
+  const int hkv = c.num_kv_heads;
+  const int target = env_int("OSCAR_TARGET_WGS", num_cus());
+  const int slots = slots_for(pool->gqa);
+  max_len = max_len < 0 ? 0 : max_len;
+  if (bf16_only) {
+    const int npages = (max_len + oscar::kPage - 1) / oscar::kPage;
+    pl.n_bf16_units = 0;
+    pl.bf16_pages_per_unit = 0;
+    int want = target / (batch * hkv);
+    if (want < 1) want = 1;
+    int ppc = (npages + want - 1) / want;
+    ppc = ppc < 2 ? 2 : ((ppc + 1) / 2) * 2;
+    pl.pages_per_chunk = ppc;
+    pl.max_chunks = (npages + ppc - 1) / ppc;
+    if (pl.max_chunks < 1) pl.max_chunks = 1;
+  } else {
+    const int list_max = c.sink_tokens / 16 + (c.recent_tokens + 15) / 16 + 1;
+    const int per_unit = env_int("OSCAR_BF16_PAGES_PER_UNIT", 16);
+    pl.n_bf16_units = (list_max + per_unit - 1) / per_unit;
+    pl.bf16_pages_per_unit = (list_max + pl.n_bf16_units - 1) / pl.n_bf16_units;
+    const int r0 = max_len - c.recent_tokens > c.sink_tokens ? max_len - c.recent_tokens : c.sink_tokens;
+    const int hist_pages = (r0 - c.sink_tokens + 15) / 16;
+    // INT2 chunks per (sequence, KV head) so that BF16 units + chunks fill
+    // about `target` workgroups (one resident 8-wave workgroup per CU)
+    int want = (target - batch * hkv * pl.n_bf16_units) / (batch * hkv);
+    if (want < 1) want = 1;
+    int ppc = (hist_pages + want - 1) / want;
+    ppc = ((ppc + slots - 1) / slots) * slots;
+    if (ppc < slots) ppc = slots;
+    pl.pages_per_chunk = ppc;
+    pl.max_chunks = (hist_pages + ppc - 1) / ppc;
+  }
+  // the last workgroup keeps one merge weight per (unit, query head) in a
+  // D*D-float LDS table; the last chunk absorbs any remainder
+  int cap = c.head_dim * c.head_dim / pool->gqa - pl.n_bf16_units;
+  if (cap > kMaxChunks) cap = kMaxChunks;
+  if (pl.max_chunks > cap) pl.max_chunks = cap;
+  pl.units = pl.n_bf16_units + pl.max_chunks;
+  if (pl.units < 1) pl.units = 1;
+  pl.grid = batch * hkv * pl.units;
+  const size_t heads = (size_t)batch * hkv;
+  const size_t parts = heads * pl.units * pool->gqa;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  pl.off_counters = 0;
+  pl.off_lse = up(heads * sizeof(uint32_t));
+  pl.off_o = pl.off_lse + up(parts * sizeof(float));
+  pl.bytes = pl.off_o + up(parts * c.head_dim * sizeof(float));
+  return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* oscar_status_string(oscar_status s) {
+  switch (s) {
+    case OSCAR_OK: return "OSCAR_OK";
+    case OSCAR_ERR_INVALID: return "OSCAR_ERR_INVALID";
+    case OSCAR_ERR_UNSUPPORTED: return "OSCAR_ERR_UNSUPPORTED";
+    case OSCAR_ERR_WORKSPACE: return "OSCAR_ERR_WORKSPACE";
+    case OSCAR_ERR_HIP: return "OSCAR_ERR_HIP";
+  }
+  return "OSCAR_ERR_UNKNOWN";
+}
+
+const char* oscar_last_error(void) { return g_err.c_str(); }
+
+oscar_status oscar_pool_create(const oscar_config* cfg, oscar_pool** out, oscar_layout* layout) {
+  if (!cfg || !out) return fail(OSCAR_ERR_INVALID, "cfg and out must be non-null");
+  *out = nullptr;
+  const oscar_config& c = *cfg;
+  if (c.num_q_heads <= 0 || c.num_kv_heads <= 0 || c.head_dim <= 0 || c.group_size <= 0 || c.page_size <= 0 ||
+      c.sink_tokens < 0 || c.recent_tokens <= 0 || !(c.sm_scale >= 0.f) || !isfinite(c.sm_scale))
+    return fail(OSCAR_ERR_INVALID, "non-positive or non-finite configuration field");
+  if (c.num_q_heads % c.num_kv_heads != 0)
+    return fail(OSCAR_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d", c.num_q_heads,
+                c.num_kv_heads);
+  if (c.head_dim % c.group_size != 0)
+    return fail(OSCAR_ERR_INVALID, "group_size %d does not divide head_dim %d", c.group_size, c.head_dim);
+  if (c.sink_tokens % c.page_size != 0)
+    return fail(OSCAR_ERR_INVALID, "sink_tokens %d is not a multiple of page_size %d", c.sink_tokens, c.page_size);
+  const int gqa = c.num_q_heads / c.num_kv_heads;
+  if (c.page_size != 16) return fail(OSCAR_ERR_UNSUPPORTED, "page_size must be 16");
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c.group_size != 64 && c.group_size != 128) return fail(OSCAR_ERR_UNSUPPORTED, "group_size must be 64 or 128");
+  if (gqa != 2 && gqa != 4 && gqa != 8) return fail(OSCAR_ERR_UNSUPPORTED, "num_q_heads/num_kv_heads must be 2, 4 or 8");
+  if (c.v_absorbed != 1) return fail(OSCAR_ERR_UNSUPPORTED, "only v_absorbed = 1 is implemented");
+  oscar_pool* p = new (std::nothrow) oscar_pool;
+  if (!p) return fail(OSCAR_ERR_INVALID, "out of host memory");
+  p->cfg = c;
+  p->n_groups = c.head_dim / c.group_size;
+  p->gqa = gqa;
+  p->sm_scale = c.sm_scale > 0.f ? c.sm_scale : 1.f / sqrtf((float)c.head_dim);
+  p->layout.int2_head_block_bytes = (size_t)oscar::int2_block_bytes(c.head_dim, p->n_groups);
+  p->layout.bf16_head_block_bytes = (size_t)oscar::bf16_block_bytes(c.head_dim);
+  p->layout.int2_page_bytes = p->layout.int2_head_block_bytes * c.num_kv_heads;
+  p->layout.bf16_page_bytes = p->layout.bf16_head_block_bytes * c.num_kv_heads;
+  if (layout) *layout = p->layout;
+  *out = p;
+  return ok();
+}
+
+void oscar_pool_destroy(oscar_pool* pool) { delete pool; }
+
+oscar_status oscar_decode_workspace_bytes(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
+                                          int32_t bf16_only, size_t* bytes) {
+  if (!pool || !bytes) return fail(OSCAR_ERR_INVALID, "pool and bytes must be non-null");
+  if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID, "negative batch or max_seq_len");
+  *bytes = batch == 0 ? 0 : make_plan(pool, batch, max_seq_len, bf16_only != 0).bytes;
+  return ok();
+}
+
+static oscar_status check_tables(const int32_t* bf16_pt, int32_t bf16_stride, int32_t bf16_pages,
+                                 const int32_t* int2_pt, int32_t int2_stride, int32_t int2_pages, bool need_int2) {
+  if (!bf16_pt || bf16_stride <= 0 || bf16_pages <= 0)
+    return fail(OSCAR_ERR_INVALID, "BF16 page table, stride and page count must be given");
+  if (need_int2 && (!int2_pt || int2_stride <= 0 || int2_pages <= 0))
+    return fail(OSCAR_ERR_INVALID, "INT2 page table, stride and page count must be given");
+  return ok();
+}
+
+oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
+                                    const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                    int32_t bf16_pt_stride, int32_t bf16_num_pages,
+                                    const int32_t* int2_page_table, int32_t int2_pt_stride,
+                                    int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
+                                    const float* r_k, const float* r_v, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!pool) return fail(OSCAR_ERR_INVALID, "pool must be non-null");
+  if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID, "negative batch or max_seq_len");
+  if (batch == 0) return ok();
+  if (!q || !seq_lens || !bf16_pool || !int2_pool || !r_k || !out)
+    return fail(OSCAR_ERR_INVALID, "q, seq_lens, pools, r_k and out must be non-null");
+  if (r_v) return fail(OSCAR_ERR_UNSUPPORTED, "r_v must be NULL: values are stored in the absorbed V basis");
+  if (!aligned16(q) || !aligned16(bf16_pool) || !aligned16(int2_pool) || !aligned16(r_k))
+    return fail(OSCAR_ERR_INVALID, "q, pools and r_k must be 16-byte aligned");
+  oscar_status st = check_tables(bf16_page_table, bf16_pt_stride, bf16_num_pages, int2_page_table, int2_pt_stride,
+                                 int2_num_pages, true);
+  if (st != OSCAR_OK) return st;
+  const Plan pl = make_plan(pool, batch, max_seq_len, false);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes)
+    return fail(OSCAR_ERR_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes", pl.bytes);
+  const oscar_config& c = pool->cfg;
+  oscar::DecodeParams p{};
+  p.q = (const uint16_t*)q;
+  p.seq_lens = seq_lens;
+  p.bf16_pt = bf16_page_table;
+  p.int2_pt = int2_page_table;
+  p.bf16_pool = (const uint8_t*)bf16_pool;
+  p.int2_pool = (const uint8_t*)int2_pool;
+  p.r_k = r_k;
+  p.out = (uint16_t*)out;
+  p.counters = (uint32_t*)((char*)workspace + pl.off_counters);
+  p.part_lse = (float*)((char*)workspace + pl.off_lse);
+  p.part_o = (float*)((char*)workspace + pl.off_o);
+  p.bf16_pt_stride = bf16_pt_stride;
+  p.bf16_num_pages = bf16_num_pages;
+  p.int2_pt_stride = int2_pt_stride;
+  p.int2_num_pages = int2_num_pages;
+  p.batch = batch;
+  p.num_kv_heads = c.num_kv_heads;
+  p.sink = c.sink_tokens;
+  p.recent = c.recent_tokens;
+  p.n_bf16_units = pl.n_bf16_units;
+  p.bf16_pages_per_unit = pl.bf16_pages_per_unit;
+  p.max_chunks = pl.max_chunks;
+  p.pages_per_chunk = pl.pages_per_chunk;
+  p.units_per_head = pl.units;
+  p.sm_log2 = pool->sm_scale * 1.4426950408889634f;
+  if (!oscar::launch_decode(p, c.head_dim, pool->n_groups, pool->gqa, false, pl.grid, (hipStream_t)stream))
+    return fail(OSCAR_ERR_UNSUPPORTED, "no decode kernel for this shape");
+  return check_hip("decode launch");
+}
+
+oscar_status oscar_bf16_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
+                                         const void* q, const int32_t* seq_lens,
+                                         const int32_t* bf16_page_table, int32_t bf16_pt_stride,
+                                         int32_t bf16_num_pages, const void* bf16_pool, void* out,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!pool) return fail(OSCAR_ERR_INVALID, "pool must be non-null");
+  if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID, "negative batch or max_seq_len");
+  if (batch == 0) return ok();
+  if (!q || !seq_lens || !bf16_pool || !out)
+    return fail(OSCAR_ERR_INVALID, "q, seq_lens, bf16_pool and out must be non-null");
+  if (!aligned16(q) || !aligned16(bf16_pool)) return fail(OSCAR_ERR_INVALID, "q and pool must be 16-byte aligned");
+  oscar_status st = check_tables(bf16_page_table, bf16_pt_stride, bf16_num_pages, nullptr, 0, 0, false);
+  if (st != OSCAR_OK) return st;
+  const Plan pl = make_plan(pool, batch, max_seq_len, true);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes)
+    return fail(OSCAR_ERR_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes", pl.bytes);
+  const oscar_config& c = pool->cfg;
+  oscar::DecodeParams p{};
+  p.q = (const uint16_t*)q;
+  p.seq_lens = seq_lens;
+  p.bf16_pt = bf16_page_table;
+  p.bf16_pool = (const uint8_t*)bf16_pool;
+  p.out = (uint16_t*)out;
+  p.counters = (uint32_t*)((char*)workspace + pl.off_counters);
+  p.part_lse = (float*)((char*)workspace + pl.off_lse);
+  p.part_o = (float*)((char*)workspace + pl.off_o);
+  p.bf16_pt_stride = bf16_pt_stride;
+  p.bf16_num_pages = bf16_num_pages;
+  p.int2_pt_stride = 1;
+  p.batch = batch;
+  p.num_kv_heads = c.num_kv_heads;
+  p.sink = c.sink_tokens;
+  p.recent = c.recent_tokens;
+  p.n_bf16_units = 0;
+  p.max_chunks = pl.max_chunks;
+  p.pages_per_chunk = pl.pages_per_chunk;
+  p.units_per_head = pl.units;
+  p.sm_log2 = pool->sm_scale * 1.4426950408889634f;
+  if (!oscar::launch_decode(p, c.head_dim, pool->n_groups, pool->gqa, true, pl.grid, (hipStream_t)stream))
+    return fail(OSCAR_ERR_UNSUPPORTED, "no decode kernel for this shape");
+  return check_hip("bf16 decode launch");
+}
+
+oscar_status oscar_merge(int32_t rows, int32_t head_dim, const int32_t* row_offsets, const float* o_partials,
+                         const float* lse_partials, void* out, void* stream) {
+  if (rows < 0) return fail(OSCAR_ERR_INVALID, "negative rows");
+  if (head_dim != 64 && head_dim != 128) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (rows == 0) return ok();
+  if (!row_offsets || !o_partials || !lse_partials || !out)
+    return fail(OSCAR_ERR_INVALID, "row_offsets, partials and out must be non-null");
+  oscar::MergeParams p{rows, head_dim, row_offsets, o_partials, lse_partials, (uint16_t*)out};
+  if (!oscar::launch_merge(p, (hipStream_t)stream)) return fail(OSCAR_ERR_UNSUPPORTED, "no merge kernel");
+  return check_hip("merge launch");
+}
+
+oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const void* k_new, const void* v_new,
+                                 const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                 int32_t bf16_pt_stride, int32_t bf16_num_pages,
+                                 const int32_t* int2_page_table, int32_t int2_pt_stride,
+                                 int32_t int2_num_pages, void* bf16_pool, void* int2_pool, const float* r_k,
+                                 const float* r_v, const float* tau_k, const float* tau_v, void* stream) {
+  if (!pool) return fail(OSCAR_ERR_INVALID, "pool must be non-null");
+  if (batch < 0) return fail(OSCAR_ERR_INVALID, "negative batch");
+  if (batch == 0) return ok();
+  if (!k_new || !v_new || !seq_lens || !bf16_pool || !int2_pool || !r_k || !tau_k || !tau_v)
+    return fail(OSCAR_ERR_INVALID, "k_new, v_new, seq_lens, pools, r_k, tau_k and tau_v must be non-null");
+  if (r_v) return fail(OSCAR_ERR_UNSUPPORTED, "r_v must be NULL: values are stored in the absorbed V basis");
+  if (!aligned16(r_k) || !aligned16(bf16_pool) || !aligned16(int2_pool))
+    return fail(OSCAR_ERR_INVALID, "pools and r_k must be 16-byte aligned");
+  oscar_status st = check_tables(bf16_page_table, bf16_pt_stride, bf16_num_pages, int2_page_table, int2_pt_stride,
+                                 int2_num_pages, true);
+  if (st != OSCAR_OK) return st;
+  const oscar_config& c = pool->cfg;
+  oscar::WriteParams p{};
+  p.k_new = (const uint16_t*)k_new;
+  p.v_new = (const uint16_t*)v_new;
+  p.seq_lens = seq_lens;
+  p.bf16_pt = bf16_page_table;
+  p.int2_pt = int2_page_table;
+  p.bf16_pool = (uint8_t*)bf16_pool;
+  p.int2_pool = (uint8_t*)int2_pool;
+  p.bf16_pt_stride = bf16_pt_stride;
+  p.bf16_num_pages = bf16_num_pages;
+  p.int2_pt_stride = int2_pt_stride;
+  p.int2_num_pages = int2_num_pages;
+  p.r_k = r_k;
+  p.tau_k = tau_k;
+  p.tau_v = tau_v;
+  p.batch = batch;
+  p.num_kv_heads = c.num_kv_heads;
+  p.sink = c.sink_tokens;
+  p.recent = c.recent_tokens;
+  if (!oscar::launch_append_demote(p, c.head_dim, pool->n_groups, (hipStream_t)stream))
+    return fail(OSCAR_ERR_UNSUPPORTED, "no append/demote kernel for this shape");
+  return check_hip("append/demote launch");
+}
+
+oscar_status oscar_quantize_pack(const oscar_pool* pool, int32_t num_tokens, const void* k, const void* v,
+                                 const int32_t* page_ids, int32_t int2_num_pages, void* int2_pool,
+                                 const float* r_k, const float* r_v, const float* tau_k, const float* tau_v,
+                                 void* stream) {
+  if (!pool) return fail(OSCAR_ERR_INVALID, "pool must be non-null");
+  if (num_tokens < 0) return fail(OSCAR_ERR_INVALID, "negative num_tokens");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !page_ids || !int2_pool || !r_k || !tau_k || !tau_v || int2_num_pages <= 0)
+    return fail(OSCAR_ERR_INVALID, "k, v, page_ids, int2_pool, r_k, tau_k, tau_v and int2_num_pages must be given");
+  if (r_v) return fail(OSCAR_ERR_UNSUPPORTED, "r_v must be NULL: values are stored in the absorbed V basis");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(int2_pool) || !aligned16(r_k))
+    return fail(OSCAR_ERR_INVALID, "k, v, int2_pool and r_k must be 16-byte aligned");
+  const oscar_config& c = pool->cfg;
+  oscar::WriteParams p{};
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.page_ids = page_ids;
+  p.num_tokens = num_tokens;
+  p.int2_pool = (uint8_t*)int2_pool;
+  p.int2_num_pages = int2_num_pages;
+  p.pages_per_block = env_int("OSCAR_QP_PAGES_PER_BLOCK", 32);
+  if (p.pages_per_block < 4) p.pages_per_block = 4;
+  p.r_k = r_k;
+  p.tau_k = tau_k;
+  p.tau_v = tau_v;
+  p.num_kv_heads = c.num_kv_heads;
+  p.sink = c.sink_tokens;
+  p.recent = c.recent_tokens;
+  if (!oscar::launch_quantize_pack(p, c.head_dim, pool->n_groups, (hipStream_t)stream))
+    return fail(OSCAR_ERR_UNSUPPORTED, "no quantize/pack kernel for this shape");
+  return check_hip("quantize/pack launch");
+}
+
+oscar_status oscar_write_bf16(const oscar_pool* pool, int32_t num_tokens, int32_t first_position, const void* k,
+                              const void* v, const int32_t* bf16_page_table, int32_t bf16_pt_stride,
+                              int32_t bf16_num_pages, void* bf16_pool, void* stream) {
+  if (!pool) return fail(OSCAR_ERR_INVALID, "pool must be non-null");
+  if (num_tokens < 0 || first_position < 0) return fail(OSCAR_ERR_INVALID, "negative num_tokens or first_position");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !bf16_pool) return fail(OSCAR_ERR_INVALID, "k, v and bf16_pool must be non-null");
+  oscar_status st = check_tables(bf16_page_table, bf16_pt_stride, bf16_num_pages, nullptr, 0, 0, false);
+  if (st != OSCAR_OK) return st;
+  oscar::WriteParams p{};
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.num_tokens = num_tokens;
+  p.bf16_pt = bf16_page_table;
+  p.bf16_pt_stride = bf16_pt_stride;
+  p.bf16_num_pages = bf16_num_pages;
+  p.bf16_pool = (uint8_t*)bf16_pool;
+  p.num_kv_heads = pool->cfg.num_kv_heads;
+  if (!oscar::launch_write_bf16(p, pool->cfg.head_dim, first_position, (hipStream_t)stream))
+    return fail(OSCAR_ERR_UNSUPPORTED, "no BF16 writer for this shape");
+  return check_hip("bf16 write launch");
+}
+
+}  // extern "C"

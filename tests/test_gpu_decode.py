@@ -1,0 +1,135 @@
+"""GPU parity: oscar_decode_attention, oscar_bf16_decode_attention and
+oscar_merge against the fp64 oracle, on oracle-built pools uploaded through
+the documented layout (so decode is tested independently of the write path).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pool_io
+from harness import DECODE_TOL, check_decode, log, make_seqs, pool_config, to_dev, upload
+from synthetic import CONFIGS, draw_inputs, make_workload
+
+pytestmark = pytest.mark.gpu
+
+TINY = CONFIGS["tiny-d64-l512"]
+QWEN = CONFIGS["qwen3-8b-l100k"]
+
+CASES = {
+    "tiny-d64-gqa2-l512": make_workload(TINY),
+    "d64-gqa2-boundary-lengths": make_workload(TINY, batch=10, seq_lens=(1, 63, 64, 65, 319, 320, 321, 336, 337, 1000),
+                                               seed=5),
+    "d64-gqa8-ragged": make_workload(TINY, num_q_heads=16, batch=2, seq_lens=(3000, 50), seed=6),
+    "d128-gqa4-ragged": make_workload(QWEN, num_q_heads=8, num_kv_heads=2, batch=3, seq_lens=(1000, 5000, 333), seed=7),
+    "d128-g64-gqa8": make_workload(QWEN, num_q_heads=16, num_kv_heads=2, group_size=64, batch=2, seq_lens=(4100, 700),
+                                   seed=8),
+    "d128-gqa2": make_workload(QWEN, num_q_heads=4, num_kv_heads=2, batch=1, seq_lens=(2500,), seed=9),
+    "d128-gqa4-long": make_workload(QWEN, num_q_heads=16, num_kv_heads=4, batch=1, seq_lens=(20000,), seed=10),
+}
+
+
+def _decode(oscar, wl, seqs, q, pools, r_k, max_len=None):
+    pool = oscar.OscarPool(pool_config(wl))
+    dev = upload(pools)
+    lens = torch.tensor([s.L for s in seqs], dtype=torch.int32, device="cuda")
+    max_len = max_len or max(s.L for s in seqs)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = pool.alloc_workspace(len(seqs), max_len)
+    log(f"decode launch: batch={len(seqs)} max_len={max_len}")
+    oscar.oscar_decode_attention(pool, q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"], dev["bf16_pool"],
+                                 dev["int2_pool"], to_dev(r_k), out, ws)
+    torch.cuda.synchronize()
+    return out, (pool, dev, lens, ws, max_len)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_matches_oracle(gpu_lib, name):
+    wl = CASES[name]
+    log(f"case {name}: {wl}")
+    inp = draw_inputs(wl)
+    seqs = make_seqs(wl, inp)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
+    check_decode(out, ref, what=name)
+
+
+def test_decode_deterministic_and_workspace_reusable(gpu_lib):
+    wl = CASES["d128-gqa4-ragged"]
+    inp = draw_inputs(wl)
+    seqs = make_seqs(wl, inp)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=1)
+    out1, (pool, dev, lens, ws, max_len) = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
+    rk = to_dev(inp.calib.r_k)
+    outs = []
+    for _ in range(3):
+        o = torch.zeros_like(out1)
+        gpu_lib.oscar_decode_attention(pool, inp.q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"],
+                                       dev["bf16_pool"], dev["int2_pool"], rk, o, ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), out1.view(torch.int16))
+    # the per-head tickets are left at zero after every call
+    assert int(ws[: 4 * wl.batch * wl.num_kv_heads].view(torch.int32).abs().sum()) == 0
+
+
+def test_decode_full_size_headline_sampled(gpu_lib):
+    """Qwen3-8B-shaped layer at 100,000 tokens, in the launch configuration
+    bench.py times; the oracle computes a sample of query heads."""
+    wl = QWEN
+    inp = draw_inputs(wl)
+    log("oracle quantization of 99,680 x 8 history tokens")
+    seqs = make_seqs(wl, inp)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
+    pairs = [(0, 0), (0, 5), (0, 13), (0, 22), (0, 31)]
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k, pairs=pairs)
+    check_decode(out, ref, pairs=pairs, what="qwen3-8b-l100k sampled")
+
+
+@pytest.mark.parametrize("name", ["tiny-d64-gqa2-l512", "d128-gqa4-ragged", "d128-g64-gqa8"])
+def test_bf16_only_decode_matches_oracle(gpu_lib, name):
+    wl = CASES[name]
+    inp = draw_inputs(wl)
+    seqs = make_seqs(wl, inp)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=3,
+                                bf16_for_all=True)
+    pool = gpu_lib.OscarPool(pool_config(wl))
+    dev = upload(pools)
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
+    out = torch.full(inp.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = pool.alloc_workspace(wl.batch, max(wl.seq_lens), bf16_only=True)
+    gpu_lib.oscar_bf16_decode_attention(pool, inp.q.cuda(), lens, max(wl.seq_lens), dev["bf16_pt"], dev["bf16_pool"],
+                                        out, ws)
+    torch.cuda.synchronize()
+    ks = [s.k for s in seqs]
+    vs = [s.v for s in seqs]
+    ref, _ = oracle.bf16_decode_attention(ks, vs, inp.q.float().numpy(), list(wl.seq_lens))
+    check_decode(out, ref, what=f"bf16-only {name}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_matches_oracle(gpu_lib, d):
+    rng = np.random.default_rng(d)
+    rows = 37
+    counts = rng.integers(0, 9, rows)
+    counts[3] = 0
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    nnz = int(offs[-1])
+    o = rng.standard_normal((nnz, d)).astype(np.float32)
+    lse = (rng.standard_normal(nnz) * 20).astype(np.float32)
+    lse[rng.random(nnz) < 0.15] = -np.inf
+    a, bnd = int(offs[5]), int(offs[6])
+    lse[a:bnd] = -np.inf  # a row whose partials are all empty
+    out = torch.full((rows, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.oscar_merge(to_dev(offs), to_dev(o), to_dev(lse), out)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle.merge_partials(o[offs[i]:offs[i + 1]], lse[offs[i]:offs[i + 1]])[0] for i in range(rows)])
+    got = out.float().cpu().numpy()
+    for i in range(rows):
+        nrm = np.linalg.norm(ref[i])
+        assert np.max(np.abs(got[i] - ref[i])) <= DECODE_TOL * max(nrm, 1e-30) + (0 if nrm > 0 else 0), i
+    assert np.all(got[3] == 0) and np.all(got[5] == 0)
