@@ -31,7 +31,18 @@
 namespace oscar {
 namespace {
 
-constexpr int kWaves = 8;
+// build-time tuning knobs (defaults are the measured best on MI355X)
+#ifndef OSCAR_DECODE_WAVES
+#define OSCAR_DECODE_WAVES 8
+#endif
+#ifndef OSCAR_DECODE_RING
+#define OSCAR_DECODE_RING 2
+#endif
+#ifndef OSCAR_BF16_SLOTS
+#define OSCAR_BF16_SLOTS 2
+#endif
+constexpr int kWaves = OSCAR_DECODE_WAVES;  // waves per workgroup
+constexpr int kRing = OSCAR_DECODE_RING;    // INT2 tiles held per wave (1 computing + kRing-1 in flight)
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1.0e30f;  // finite "no token yet" running max
 constexpr float kLazy = 8.0f;        // log2 slack before the running max is raised
@@ -42,7 +53,7 @@ struct DC {
   static constexpr int G = D / NG;
   static constexpr int SLOTS = (16 / GQA) < 4 ? (16 / GQA) : 4;  // INT2 pages per tile
   static constexpr int COLS = SLOTS * GQA;
-  static constexpr int SLOTS_B = SLOTS < 2 ? SLOTS : 2;  // BF16 pages per tile
+  static constexpr int SLOTS_B = SLOTS < OSCAR_BF16_SLOTS ? SLOTS : OSCAR_BF16_SLOTS;  // BF16 pages per tile
   static constexpr int COLS_B = SLOTS_B * GQA;
   static constexpr int KW = D / 64;  // 32-bit K (and V) code words per record
   static constexpr int CB = D / 16;  // 16-channel blocks (P.V MFMAs per page)
@@ -54,12 +65,12 @@ struct DC {
 
 template <int D, int GQA>
 struct Smem {
+  static constexpr int SLOTS = (16 / GQA) < 4 ? (16 / GQA) : 4;
   union {
-    float r[D * D];                   // R_K of this KV head (INT2 prologue)
     float part[kWaves][GQA][D + 1];   // per-wave partials, [D] = lse (log2)
-    float wts[D * D];                 // final-merge weights [unit][head]
+    float wts[kWaves * GQA * (D + 1)];  // final-merge weights [unit][head]
   } u;
-  float qf[GQA * D];                  // q (fp32)
+  v4i bq[SLOTS][2][D / 64][64];       // int8 q' B operands per lane (shared by the waves)
   float qr[GQA * D];                  // q' = q R_K (fp32)
   alignas(16) int8_t ta[GQA * D];     // int8 terms of q'
   alignas(16) int8_t tb[GQA * D];
@@ -173,10 +184,10 @@ struct I2Tile {
 };
 
 template <int D, int NG, int GQA>
-__device__ __forceinline__ void i2_load(I2Tile<D, NG, GQA>& t, const DecodeParams& p, int b, int kvh,
+__device__ __forceinline__ void i2_load(I2Tile<D, NG, GQA>& t, const DecodeParams& p,
+                                        const int32_t* __restrict__ pt, const uint8_t* __restrict__ pool, int kvh,
                                         int tile_first, int page_end, int hist_len, int lane, int my_slot) {
   using C = DC<D, NG, GQA>;
-  const int32_t* pt = p.int2_pt + (size_t)b * p.int2_pt_stride;
   const int j = lane >> 4;
   int mine_id = -1;
 #pragma unroll
@@ -186,48 +197,57 @@ __device__ __forceinline__ void i2_load(I2Tile<D, NG, GQA>& t, const DecodeParam
     if (lp < page_end) id = pt[lp];
     const bool ok = id >= 0 && id < p.int2_num_pages;
     if (s == my_slot) mine_id = ok ? id : -1;
+    // load into locals, assign the tile unconditionally (keeps it in VGPRs)
+    uint4 x = uint4{0u, 0u, 0u, 0u};
     if (ok) {
-      const uint8_t* rec = p.int2_pool + ((size_t)id * p.num_kv_heads + kvh) * C::BLK2 + lane * C::REC;
+      const uint8_t* rec = pool + ((size_t)id * p.num_kv_heads + kvh) * C::BLK2 + lane * C::REC;
       if constexpr (D == 128) {
-        const uint4 x = *(const uint4*)rec;
-        t.kw[s][0] = x.x;
-        t.kw[s][1] = x.y;
-        t.vw[s][0] = x.z;
-        t.vw[s][1] = x.w;
+        x = *(const uint4*)rec;
       } else {
-        const uint2 x = *(const uint2*)rec;
-        t.kw[s][0] = x.x;
-        t.vw[s][0] = x.y;
+        const uint2 y = *(const uint2*)rec;
+        x.x = y.x;
+        x.y = y.y;
       }
+    }
+    if constexpr (D == 128) {
+      t.kw[s][0] = x.x;
+      t.kw[s][1] = x.y;
+      t.vw[s][0] = x.z;
+      t.vw[s][1] = x.w;
     } else {
-#pragma unroll
-      for (int w = 0; w < C::KW; ++w) t.kw[s][w] = t.vw[s][w] = 0u;
+      t.kw[s][0] = x.x;
+      t.vw[s][0] = x.y;
     }
   }
-  t.nvalid = 0;
+  int nv = 0;
+  uint4 sx[2 * NG];
 #pragma unroll
-  for (int i = 0; i < 8 * NG; ++i) t.sc[i] = 0u;
+  for (int i = 0; i < 2 * NG; ++i) sx[i] = uint4{0u, 0u, 0u, 0u};
   if (mine_id >= 0) {
     const int base = (tile_first + my_slot) * kPage + 4 * j;
-    t.nvalid = min(max(hist_len - base, 0), 4);
-    const uint4* sp = (const uint4*)(p.int2_pool + ((size_t)mine_id * p.num_kv_heads + kvh) * C::BLK2 + 8 * D +
-                                     j * 32 * NG);
+    nv = min(max(hist_len - base, 0), 4);
+    const uint4* sp = (const uint4*)(pool + ((size_t)mine_id * p.num_kv_heads + kvh) * C::BLK2 + 8 * D + j * 32 * NG);
 #pragma unroll
-    for (int i = 0; i < 2 * NG; ++i) {
-      const uint4 x = sp[i];
-      t.sc[4 * i + 0] = x.x;
-      t.sc[4 * i + 1] = x.y;
-      t.sc[4 * i + 2] = x.z;
-      t.sc[4 * i + 3] = x.w;
-    }
+    for (int i = 0; i < 2 * NG; ++i) sx[i] = sp[i];
+  }
+  t.nvalid = nv;
+#pragma unroll
+  for (int i = 0; i < 2 * NG; ++i) {
+    t.sc[4 * i + 0] = sx[i].x;
+    t.sc[4 * i + 1] = sx[i].y;
+    t.sc[4 * i + 2] = sx[i].z;
+    t.sc[4 * i + 3] = sx[i].w;
   }
 }
 
 template <int D, int NG, int GQA>
 __device__ __forceinline__ void i2_compute(const I2Tile<D, NG, GQA>& t, Acc<D, NG>& st,
-                                           const v4i (&bq)[DC<D, NG, GQA>::SLOTS][2][D / 64], float kappa,
-                                           const float (&sig)[NG], int my_slot) {
+                                           const v4i (&bq)[DC<D, NG, GQA>::SLOTS][2][D / 64][64], float kappa,
+                                           const float (&sig)[NG], int my_slot, int lane) {
   using C = DC<D, NG, GQA>;
+  // the q' operands are read from LDS on every tile: an opaque lane index
+  // keeps the compiler from hoisting them into 64 loop-invariant VGPRs
+  asm volatile("" : "+v"(lane));
   // ---- scores on the int8 matrix cores
   v4i ca[NG], cb[NG];
 #pragma unroll
@@ -242,8 +262,9 @@ __device__ __forceinline__ void i2_compute(const I2Tile<D, NG, GQA>& t, Acc<D, N
       constexpr int dummy = 0;
       (void)dummy;
       const int g = (NG == 1) ? 0 : w;
-      ca[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq[s][0][w], ca[g], 0, 0, 0);
-      cb[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq[s][1][w], cb[g], 0, 0, 0);
+      const v4i b0 = bq[s][0][w][lane], b1 = bq[s][1][w][lane];
+      ca[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b0, ca[g], 0, 0, 0);
+      cb[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b1, cb[g], 0, 0, 0);
     }
   }
   // ---- logits (log2 domain)
@@ -321,11 +342,10 @@ struct B16Valid {
 };
 
 template <int D, int GQA>
-__device__ __forceinline__ void b16_load(B16Tile<D, GQA>& t, const DecodeParams& p, int b, int kvh, int tile_first,
-                                         int list_end, int n_sp, int first_rp, bool bf16_only, const B16Valid& valid,
-                                         int lane) {
+__device__ __forceinline__ void b16_load(B16Tile<D, GQA>& t, const DecodeParams& p, const int32_t* __restrict__ pt,
+                                         const uint8_t* __restrict__ pool, int kvh, int tile_first, int list_end,
+                                         int n_sp, int first_rp, bool bf16_only, const B16Valid& valid, int lane) {
   using T = B16Tile<D, GQA>;
-  const int32_t* pt = p.bf16_pt + (size_t)b * p.bf16_pt_stride;
   const int j = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int s = 0; s < T::S; ++s) {
@@ -337,35 +357,31 @@ __device__ __forceinline__ void b16_load(B16Tile<D, GQA>& t, const DecodeParams&
     }
     const bool ok = id >= 0 && id < p.bf16_num_pages;
     t.lp[s] = ok ? lp : -1;
+    uint4 kx[T::KB], vx[T::KB];
+#pragma unroll
+    for (int q = 0; q < T::KB; ++q) kx[q] = vx[q] = uint4{0u, 0u, 0u, 0u};
     if (ok) {
-      const uint8_t* blk = p.bf16_pool + ((size_t)id * p.num_kv_heads + kvh) * (64 * D);
+      const uint8_t* blk = pool + ((size_t)id * p.num_kv_heads + kvh) * (64 * D);
       const uint4* kp = (const uint4*)(blk + r * 2 * D + j * (D / 2));
       const uint4* vp = (const uint4*)(blk + 32 * D + j * 8 * D + r * (D / 2));
 #pragma unroll
       for (int q = 0; q < T::KB; ++q) {
-        t.k[s][q] = kp[q];
-        t.v[s][q] = vp[q];
+        kx[q] = kp[q];
+        vx[q] = vp[q];
       }
-      // zero tokens outside the sink / recent segments (stale or unwritten)
-      const int p0 = lp * kPage;
-      if (!(valid(p0) && valid(p0 + kPage - 1))) {
-        if (!valid(p0 + r)) {
+    }
+    // zero tokens outside the sink / recent segments (stale or unwritten)
+    const int p0 = lp * kPage;
+    const bool partial = ok && !(valid(p0) && valid(p0 + kPage - 1));
+    const bool kv_ok = !partial || valid(p0 + r);
+    const uint32_t m01 = (!partial || valid(p0 + 4 * j) ? 0xFFFFu : 0u) |
+                         (!partial || valid(p0 + 4 * j + 1) ? 0xFFFF0000u : 0u);
+    const uint32_t m23 = (!partial || valid(p0 + 4 * j + 2) ? 0xFFFFu : 0u) |
+                         (!partial || valid(p0 + 4 * j + 3) ? 0xFFFF0000u : 0u);
 #pragma unroll
-          for (int q = 0; q < T::KB; ++q) t.k[s][q] = uint4{0u, 0u, 0u, 0u};
-        }
-        const uint32_t m01 = (valid(p0 + 4 * j) ? 0xFFFFu : 0u) | (valid(p0 + 4 * j + 1) ? 0xFFFF0000u : 0u);
-        const uint32_t m23 = (valid(p0 + 4 * j + 2) ? 0xFFFFu : 0u) | (valid(p0 + 4 * j + 3) ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int q = 0; q < T::KB; ++q) {
-          t.v[s][q].x &= m01;
-          t.v[s][q].y &= m23;
-          t.v[s][q].z &= m01;
-          t.v[s][q].w &= m23;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < T::KB; ++q) t.k[s][q] = t.v[s][q] = uint4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < T::KB; ++q) {
+      t.k[s][q] = kv_ok ? kx[q] : uint4{0u, 0u, 0u, 0u};
+      t.v[s][q] = uint4{vx[q].x & m01, vx[q].y & m23, vx[q].z & m01, vx[q].w & m23};
     }
   }
 }
@@ -461,10 +477,16 @@ __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, in
 
 // ------------------------------------------------------------- kernel ----
 template <int D, int NG, int GQA, bool BF16_ONLY>
-__global__ void __launch_bounds__(kThreads) k_decode(const DecodeParams p) {
+__global__ void __launch_bounds__(kThreads)
+    k_decode(const DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ bf16_pt_all,
+             const int32_t* __restrict__ int2_pt_all, const uint8_t* __restrict__ bf16_pool,
+             const uint8_t* __restrict__ int2_pool, const uint16_t* __restrict__ qin, const float* __restrict__ r_k) {
   using C = DC<D, NG, GQA>;
   __shared__ Smem<D, GQA> sm;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: page-table lookups then stay scalar loads and the
+  // tile prefetch is never serialized behind a vector-memory wait
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, j = lane >> 4;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int U = p.units_per_head;
@@ -473,7 +495,7 @@ __global__ void __launch_bounds__(kThreads) k_decode(const DecodeParams p) {
   const int b = lin / (U * p.num_kv_heads);
   const int hq = p.num_kv_heads * GQA;
 
-  int L = max(p.seq_lens[b], 0);
+  int L = max(seq_lens[b], 0);
   L = min(L, kPage * p.bf16_pt_stride);
   if (!BF16_ONLY) L = min(L, p.sink + p.recent + kPage * p.int2_pt_stride);
   const int r0 = max(p.sink, L - p.recent);
@@ -513,28 +535,58 @@ __global__ void __launch_bounds__(kThreads) k_decode(const DecodeParams p) {
     // ---------------------------------------------------- INT2 chunk unit
     const int my_slot = (n < C::COLS) ? n / GQA : C::SLOTS;
     const int ntiles = (end - first + C::SLOTS - 1) / C::SLOTS;
-    int tile = wave;
-    I2Tile<D, NG, GQA> cur;
-    if (tile < ntiles) i2_load<D, NG, GQA>(cur, p, b, kvh, first + tile * C::SLOTS, end, hist_len, lane, my_slot);
-
-    // prologue: q' = q R_K for this KV head's query heads, then int8 terms
-    {
-      const uint16_t* qsrc = p.q + ((size_t)b * hq + kvh * GQA) * D;
-      for (int i = tid; i < GQA * D; i += kThreads) sm.qf[i] = bf16_to_f32(qsrc[i]);
-      const uint4* rsrc = (const uint4*)(p.r_k + (size_t)kvh * D * D);
-      for (int i = tid; i < D * D / 4; i += kThreads) ((uint4*)sm.u.r)[i] = rsrc[i];
+    const int32_t* __restrict__ ipt = int2_pt_all + (size_t)b * p.int2_pt_stride;
+    // prologue: q' = q R_K on the bf16 matrix cores (R_K = R_hi + R_lo, both
+    // bf16, so q' keeps ~2^-17 relative accuracy); wave w computes output
+    // channels [16w, 16w + 16) for the query heads (MFMA rows) of this KV
+    // head.  Its loads are issued before the first tiles' so that the
+    // prologue runs while those are in flight.
+    constexpr int KB = D / 32;
+    uint4 qa[KB];
+    float rv[KB][8];
+    const bool qwave = wave < D / 16;
+    if (qwave) {
+      const uint16_t* qrow = qin + ((size_t)b * hq + kvh * GQA + (n < GQA ? n : 0)) * D;
+      const float* rcol = r_k + (size_t)kvh * D * D + wave * 16 + n;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        qa[kb] = uint4{0u, 0u, 0u, 0u};
+        if (n < GQA) qa[kb] = *(const uint4*)(qrow + kb * 32 + j * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rv[kb][e] = rcol[(size_t)(kb * 32 + j * 8 + e) * D];
+      }
+    }
+    // prefetch ring: tile wave + r*kWaves in slot r; tiles past the last one
+    // load nothing but are fully initialized, so the buffers stay in VGPRs
+    I2Tile<D, NG, GQA> ring[kRing];
+    auto ld = [&](I2Tile<D, NG, GQA>& t, int tl) {
+      i2_load<D, NG, GQA>(t, p, ipt, int2_pool, kvh, first + tl * C::SLOTS, tl < ntiles ? end : 0, hist_len, lane,
+                          my_slot);
+    };
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r) ld(ring[r], wave + r * kWaves);
+    if (qwave) {
+      v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = rv[kb][2 * e], x1 = rv[kb][2 * e + 1];
+          hi[e] = pack_bf16x2(x0, x1);
+          lo[e] = pack_bf16x2(x0 - bf16_lo(hi[e]), x1 - bf16_hi(hi[e]));
+        }
+        const v8bf av = as_v8bf(qa[kb]);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_v8bf(uint4{hi[0], hi[1], hi[2], hi[3]}), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_v8bf(uint4{lo[0], lo[1], lo[2], lo[3]}), c, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * j + i < GQA) sm.qr[(4 * j + i) * D + wave * 16 + n] = c[i];
     }
     __syncthreads();
     float amax = 0.f;
-    for (int idx = tid; idx < GQA * D; idx += kThreads) {
-      const int h = idx / D, c = idx % D;
-      const float* qh = sm.qf + h * D;
-      float acc = 0.f;
-#pragma unroll 16
-      for (int i = 0; i < D; ++i) acc = fmaf(qh[i], sm.u.r[i * D + c], acc);
-      sm.qr[idx] = acc;
-      amax = fmaxf(amax, fabsf(acc));
-    }
+    for (int idx = tid; idx < GQA * D; idx += kThreads) amax = fmaxf(amax, fabsf(sm.qr[idx]));
     amax = wave_max(amax);
     if (lane == 0) sm.wred[wave] = amax;
     __syncthreads();
@@ -553,48 +605,52 @@ __global__ void __launch_bounds__(kThreads) k_decode(const DecodeParams p) {
     __syncthreads();
     for (int pair = wave; pair < GQA * NG; pair += kWaves) {
       const int h = pair / NG, g = pair % NG;
-      int s = 0;
+      int sacc = 0;
       for (int c = lane; c < C::G; c += 64) {
         const int idx = h * D + g * C::G + c;
-        s += 256 * (int)sm.ta[idx] + (int)sm.tb[idx];
+        sacc += 256 * (int)sm.ta[idx] + (int)sm.tb[idx];
       }
-      s = wave_sum_i(s);
-      if (lane == 0) sm.sig[pair] = s;
+      sacc = wave_sum_i(sacc);
+      if (lane == 0) sm.sig[pair] = sacc;
+    }
+    // B operands: column n = (page slot, head), block-diagonal over slots;
+    // every wave needs the same per-lane values, wave 0 builds them
+    const int chd = n % GQA;
+    if (wave == 0) {
+#pragma unroll
+      for (int s = 0; s < C::SLOTS; ++s)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int w = 0; w < C::KW; ++w) {
+            uint32_t o4[4] = {0u, 0u, 0u, 0u};
+            if (my_slot == s) {
+              const int8_t* src = (tt == 0 ? sm.ta : sm.tb) + chd * D + w * 64 + j * 16;
+              const uint4 x = *(const uint4*)src;
+              const uint32_t in4[4] = {x.x, x.y, x.z, x.w};
+              transpose4x4(in4, o4);
+            }
+            sm.bq[s][tt][w][lane] = v4i{(int)o4[0], (int)o4[1], (int)o4[2], (int)o4[3]};
+          }
     }
     __syncthreads();
-    // B operands: column n = (page slot, head); slot-block-diagonal
-    v4i bq[C::SLOTS][2][C::KW];
-    const int chd = n % GQA;
-#pragma unroll
-    for (int s = 0; s < C::SLOTS; ++s)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int w = 0; w < C::KW; ++w) {
-          uint32_t o4[4] = {0u, 0u, 0u, 0u};
-          if (my_slot == s) {
-            const int8_t* src = (tt == 0 ? sm.ta : sm.tb) + chd * D + w * 64 + j * 16;
-            const uint4 x = *(const uint4*)src;
-            const uint32_t in4[4] = {x.x, x.y, x.z, x.w};
-            transpose4x4(in4, o4);
-          }
-          bq[s][tt][w] = v4i{(int)o4[0], (int)o4[1], (int)o4[2], (int)o4[3]};
-        }
     float sig[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) sig[g] = (float)sm.sig[chd * NG + g];
     const float kappa = p.sm_log2 * sq * (1.f / 256.f);
-    __syncthreads();  // sm.u.r is reused for partials below
 
     Acc<D, NG> st;
     st.init();
-    while (tile < ntiles) {
-      const int nxt = tile + kWaves;
-      I2Tile<D, NG, GQA> nt;
-      if (nxt < ntiles) i2_load<D, NG, GQA>(nt, p, b, kvh, first + nxt * C::SLOTS, end, hist_len, lane, my_slot);
-      i2_compute<D, NG, GQA>(cur, st, bq, kappa, sig, my_slot);
-      cur = nt;
-      tile = nxt;
+    int tile = wave;
+    while (true) {
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        if (tile >= ntiles) break;
+        ld(ring[(r + kRing - 1) % kRing], tile + (kRing - 1) * kWaves);
+        i2_compute<D, NG, GQA>(ring[r], st, sm.bq, kappa, sig, my_slot, lane);
+        tile += kWaves;
+      }
+      if (tile >= ntiles) break;
     }
     wave_finish<D, NG, GQA, true>(st, sm, wave, lane);
   } else {
@@ -605,7 +661,7 @@ __global__ void __launch_bounds__(kThreads) k_decode(const DecodeParams p) {
     // q (unrotated, bf16) as B operands
     v8bf bq[SB][D / 32];
     {
-      const uint16_t* qh = p.q + ((size_t)b * hq + kvh * GQA + (n % GQA)) * D + j * (D / 4);
+      const uint16_t* qh = qin + ((size_t)b * hq + kvh * GQA + (n % GQA)) * D + j * (D / 4);
 #pragma unroll
       for (int s = 0; s < SB; ++s)
 #pragma unroll
@@ -618,15 +674,16 @@ __global__ void __launch_bounds__(kThreads) k_decode(const DecodeParams p) {
     const int ntiles = (end - first + SB - 1) / SB;
     Acc<D, 1> st;
     st.init();
+    const int32_t* __restrict__ bpt = bf16_pt_all + (size_t)b * p.bf16_pt_stride;
     int tile = wave;
     B16Tile<D, GQA> cur;
-    if (tile < ntiles)
-      b16_load<D, GQA>(cur, p, b, kvh, first + tile * SB, end, n_sp, first_rp, BF16_ONLY, valid, lane);
+    b16_load<D, GQA>(cur, p, bpt, bf16_pool, kvh, first + tile * SB, tile < ntiles ? end : 0, n_sp, first_rp,
+                     BF16_ONLY, valid, lane);
     while (tile < ntiles) {
       const int nxt = tile + kWaves;
       B16Tile<D, GQA> nt;
-      if (nxt < ntiles)
-        b16_load<D, GQA>(nt, p, b, kvh, first + nxt * SB, end, n_sp, first_rp, BF16_ONLY, valid, lane);
+      b16_load<D, GQA>(nt, p, bpt, bf16_pool, kvh, first + nxt * SB, nxt < ntiles ? end : 0, n_sp, first_rp,
+                       BF16_ONLY, valid, lane);
       b16_compute<D, GQA>(cur, st, bq, p.sm_log2, valid, my_slot, lane);
       cur = nt;
       tile = nxt;
@@ -669,30 +726,30 @@ __global__ void __launch_bounds__(kThreads) k_decode(const DecodeParams p) {
     p.part_o[(pidx + h) * D + c] = o;
     if (c == 0) p.part_lse[pidx + h] = lse;
   }
-  // ---- last workgroup of this (sequence, KV head) merges every partial
-  __threadfence();
+  // ---- last workgroup of this (sequence, KV head) merges every partial.
+  // Every wave drains its partial stores to L2 (s_waitcnt vmcnt(0)); then one
+  // thread releases at device scope (L2 write-back) and takes a ticket; the
+  // workgroup that takes the last ticket acquires and reads all partials.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.counters + head_base, 1u, __ATOMIC_ACQ_REL,
+    const uint32_t prev = __hip_atomic_fetch_add(p.counters + head_base, 1u, __ATOMIC_RELEASE,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = (prev == (uint32_t)(total - 1));
+    const int last = prev == (uint32_t)(total - 1);
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    sm.last = last;
   }
   __syncthreads();
   if (!sm.last) return;
-  __threadfence();
   const size_t p0 = head_base * U * GQA;
   // weights exp(lse_u - M_h) / sum_u exp(lse_u - M_h), in sm.u.wts[u * GQA + h]
   for (int h = wave; h < GQA; h += kWaves) {
     float mx = -INFINITY;
-    for (int uu = lane; uu < total; uu += 64)
-      mx = fmaxf(mx, __hip_atomic_load(p.part_lse + p0 + (size_t)uu * GQA + h, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT));
+    for (int uu = lane; uu < total; uu += 64) mx = fmaxf(mx, p.part_lse[p0 + (size_t)uu * GQA + h]);
     mx = wave_max(mx);
     float sw = 0.f;
     for (int uu = lane; uu < total; uu += 64) {
-      const float l = __hip_atomic_load(p.part_lse + p0 + (size_t)uu * GQA + h, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-      const float e = (mx > -INFINITY) ? expf(l - mx) : 0.f;
+      const float e = (mx > -INFINITY) ? expf(p.part_lse[p0 + (size_t)uu * GQA + h] - mx) : 0.f;
       sm.u.wts[uu * GQA + h] = e;
       sw += e;
     }
@@ -704,13 +761,17 @@ __global__ void __launch_bounds__(kThreads) k_decode(const DecodeParams p) {
   __syncthreads();
   for (int idx = tid; idx < GQA * D; idx += kThreads) {
     const int h = idx / D, c = idx % D;
+    const float* src = p.part_o + (p0 + h) * D + c;  // partial u at src[u * GQA * D]
     float acc = 0.f;
-    for (int uu = 0; uu < total; ++uu) {
-      const float w = sm.u.wts[uu * GQA + h];
-      if (w != 0.f)
-        acc += w * __hip_atomic_load(p.part_o + (p0 + (size_t)uu * GQA + h) * D + c, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+    int uu = 0;
+    for (; uu + 16 <= total; uu += 16) {  // 16 independent loads in flight
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = src[(size_t)(uu + k) * GQA * D];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc += sm.u.wts[(uu + k) * GQA + h] * v[k];
     }
+    for (; uu < total; ++uu) acc += sm.u.wts[uu * GQA + h] * src[(size_t)uu * GQA * D];
     p.out[((size_t)b * hq + kvh * GQA + h) * D + c] = (uint16_t)f32_to_bf16(acc);
   }
   if (tid == 0) __hip_atomic_store(p.counters + head_base, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -745,9 +806,11 @@ __global__ void __launch_bounds__(256) k_merge(const MergeParams p) {
 template <int D, int NG, int GQA>
 bool launch_decode_t(const DecodeParams& p, bool bf16_only, int grid, hipStream_t stream) {
   if (bf16_only)
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, true>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens, p.bf16_pt,
+                       p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
   else
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, false>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens, p.bf16_pt,
+                       p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
   return true;
 }
 

@@ -113,9 +113,10 @@ Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
     pl.pages_per_chunk = ppc;
     pl.max_chunks = (hist_pages + ppc - 1) / ppc;
   }
-  // the last workgroup keeps one merge weight per (unit, query head) in a
-  // D*D-float LDS table; the last chunk absorbs any remainder
-  int cap = c.head_dim * c.head_dim / pool->gqa - pl.n_bf16_units;
+  // the last workgroup keeps one merge weight per (unit, query head) in an
+  // LDS table of 8 * (D + 1) entries per head; the last chunk absorbs any
+  // remainder
+  int cap = 8 * (c.head_dim + 1) - pl.n_bf16_units;
   if (cap > kMaxChunks) cap = kMaxChunks;
   if (pl.max_chunks > cap) pl.max_chunks = cap;
   pl.units = pl.n_bf16_units + pl.max_chunks;

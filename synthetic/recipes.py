@@ -299,7 +299,7 @@ def draw_inputs(wl: Workload, calib: Optional[Calibration] = None, device="cpu",
         u = torch.as_tensor(calib.q_basis, dtype=torch.float32, device=device)
         z = torch.randn(wl.batch, wl.num_q_heads, d, generator=gen, device=device) * lam
         kv_of_head = torch.arange(wl.num_q_heads, device=device) // wl.gqa
-        q = torch.einsum("bhd,hed->bhe", z, u[kv_of_head]).to(torch.bfloat16)
+        q = torch.einsum("bhd,hed->bhe", z, u[kv_of_head]).to(torch.bfloat16).contiguous()
     return Inputs(workload=wl, calib=calib, k=ks, v=vs, q=q)
 
 
