@@ -48,7 +48,9 @@ def parse():
     ap.add_argument("--no-bf16", action="store_true", help="skip the BF16-only comparator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
-                    help="only run N eager decode steps on one copy (for rocprofv3), print nothing else")
+                    help="only run N eager decode steps over the cold pool copies, then one plain copy of "
+                         "--probe-bytes (for rocprofv3 counters); prints no JSON")
+    ap.add_argument("--probe-bytes", type=int, default=256 * 2**20)
     return ap.parse_args()
 
 
@@ -215,36 +217,51 @@ def traffic_for(workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, inp):
-    """The oracle's decode (R1-R3) timed on this host on a bounded sample:
-    two of the KV heads (their query heads) over the full context."""
+def cpu_baseline(wl, inp, repeats=3):
+    """The oracle's decode (R1-R3) of the whole step, timed on this host's
+    cores: every KV head of every sequence over its full context.  The
+    oracle's own write path builds its pool first (not timed)."""
     import numpy as np
     import oracle
-    n_kv = 2
-    g = wl.gqa
-    seqs = []
-    L = wl.seq_lens[0]
     c = inp.calib
-    k = inp.k[0][:, :n_kv].float().cpu().numpy()
-    v = inp.v[0][:, :n_kv].float().cpu().numpy()
-    s = oracle.SeqPool(n_kv, wl.head_dim, wl.group_size, wl.sink, wl.recent)
-    s.prefill(k, v, c.r_k[:n_kv], c.tau_k[:n_kv], c.tau_v[:n_kv])
-    seqs.append(s)
-    q = inp.q[:1, : n_kv * g].float().cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.decode_attention(seqs, q, c.r_k[:n_kv])
-    dt = time.perf_counter() - t0
+    seqs = []
+    for b, L in enumerate(wl.seq_lens):
+        k = inp.k[b][:L].float().cpu().numpy()
+        v = inp.v[b][:L].float().cpu().numpy()
+        s = oracle.SeqPool(wl.num_kv_heads, wl.head_dim, wl.group_size, wl.sink, wl.recent)
+        s.prefill(k, v, c.r_k, c.tau_k, c.tau_v)
+        seqs.append(s)
+    q = inp.q.float().cpu().numpy()
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.decode_attention(seqs, q, c.r_k)
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
     kv = wl.kv_bytes()
-    sample_bytes = kv["total"] * n_kv / wl.num_kv_heads
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count()
-    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 numpy oracle decode (dequantize, inverse-rotate, one softmax) of {n_kv} of "
-                      f"{wl.num_kv_heads} KV heads ({n_kv * g} query heads) at {L} tokens; KV bytes of that "
-                      f"share / wall time {dt:.2f} s"}
+    return {"value": round(kv["total"] / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole step: fp64 numpy oracle decode (dequantize, inverse-rotate, one softmax) of all "
+                      f"{wl.num_kv_heads} KV heads / {wl.num_q_heads} query heads of {wl.batch} sequence(s) at "
+                      f"{list(wl.seq_lens)[:4]} tokens; step KV bytes / median wall time of {repeats} runs "
+                      f"({dt:.2f} s); host has {os.cpu_count()} logical CPUs"}
+
+
+def copy_probe(nbytes):
+    """One plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    x = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    # an elementwise kernel (a device memcpy may run on a DMA engine, which
+    # carries no per-dispatch counters): reads nbytes, writes nbytes
+    torch.bitwise_not(x, out=y)
+    torch.cuda.synchronize()
+    log(f"copy probe: bitwise_not kernel, {nbytes} bytes read, {nbytes} bytes written")
 
 
 def main():
@@ -265,8 +282,6 @@ def main():
     pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
                                             wl.sink, wl.recent, 1, 0.0))
     n_copies = max(1, math.ceil(args.cold_bytes / kv["total"]))
-    if args.profile_steps:
-        n_copies = 1
     copies, int2_pool, bf16_pool, r_k = build_pools(oscar, pool, wl, inp, n_copies, seed=wl.seed)
     log(f"built {n_copies} pool copies ({n_copies * kv['total'] / 2**30:.2f} GiB of KV)")
     q = inp.q.contiguous()
@@ -279,6 +294,7 @@ def main():
             dec(i)
         torch.cuda.synchronize()
         log(f"profile run: {args.profile_steps} decode steps done")
+        copy_probe(args.probe_bytes)
         return
 
     ms, ms_min = time_steps(dec, args.steps, args.warmup, args.repeats, use_graph=True)
