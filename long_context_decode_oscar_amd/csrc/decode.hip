@@ -25,6 +25,8 @@
 // covers SLOTS pages and all softmax arithmetic is shared across them.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -143,24 +145,21 @@ template <int D, int NG>
 struct Acc {
   v4f o[D / 16];
   float m, l;
-  float W[NG], Z[NG];  // INT2 only: sum of bf16 weights, sum of weight * zero
+  float Z[NG];  // INT2 only: sum over tokens of weight * (operand bias + zero)
   __device__ void init() {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
     m = kNegBig;
     l = 0.f;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) W[g] = Z[g] = 0.f;
+    for (int g = 0; g < NG; ++g) Z[g] = 0.f;
   }
   __device__ void scale(float f) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) o[i] *= f;
     l *= f;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      W[g] *= f;
-      Z[g] *= f;
-    }
+    for (int g = 0; g < NG; ++g) Z[g] *= f;
   }
   // lazy running max: raise m only when some logit exceeds it by kLazy
   __device__ __forceinline__ void update_max(const float lg[4]) {
@@ -183,54 +182,47 @@ struct I2Tile {
   int nvalid;           // valid rows (a prefix) among this lane's 4 tokens
 };
 
+// Loads one tile: SLOTS consecutive logical pages of one KV head.  Code
+// records of absent pages are read from physical page 0 (never used: their
+// scales are zero and their logits -inf); scale words of tokens that are not
+// history tokens are zeroed, so stale bits can never reach the arithmetic.
 template <int D, int NG, int GQA>
 __device__ __forceinline__ void i2_load(I2Tile<D, NG, GQA>& t, const DecodeParams& p,
                                         const int32_t* __restrict__ pt, const uint8_t* __restrict__ pool, int kvh,
                                         int tile_first, int page_end, int hist_len, int lane, int my_slot) {
   using C = DC<D, NG, GQA>;
   const int j = lane >> 4;
+  const uint32_t rec_off = (uint32_t)lane * C::REC;
   int mine_id = -1;
+  bool full = (tile_first + C::SLOTS) * kPage <= hist_len && tile_first + C::SLOTS <= page_end;
 #pragma unroll
   for (int s = 0; s < C::SLOTS; ++s) {
     const int lp = tile_first + s;
     int id = -1;
     if (lp < page_end) id = pt[lp];
     const bool ok = id >= 0 && id < p.int2_num_pages;
+    full = full && ok;
     if (s == my_slot) mine_id = ok ? id : -1;
-    // load into locals, assign the tile unconditionally (keeps it in VGPRs)
-    uint4 x = uint4{0u, 0u, 0u, 0u};
-    if (ok) {
-      const uint8_t* rec = pool + ((size_t)id * p.num_kv_heads + kvh) * C::BLK2 + lane * C::REC;
-      if constexpr (D == 128) {
-        x = *(const uint4*)rec;
-      } else {
-        const uint2 y = *(const uint2*)rec;
-        x.x = y.x;
-        x.y = y.y;
-      }
-    }
+    const uint8_t* blk = pool + ((size_t)(ok ? id : 0) * p.num_kv_heads + kvh) * C::BLK2;
     if constexpr (D == 128) {
+      const uint4 x = *(const uint4*)(blk + rec_off);
       t.kw[s][0] = x.x;
       t.kw[s][1] = x.y;
       t.vw[s][0] = x.z;
       t.vw[s][1] = x.w;
     } else {
-      t.kw[s][0] = x.x;
-      t.vw[s][0] = x.y;
+      const uint2 y = *(const uint2*)(blk + rec_off);
+      t.kw[s][0] = y.x;
+      t.vw[s][0] = y.y;
     }
   }
-  int nv = 0;
+  const int base = (tile_first + my_slot) * kPage + 4 * j;
+  const int nv = mine_id >= 0 ? min(max(hist_len - base, 0), 4) : 0;
+  const uint4* sp =
+      (const uint4*)(pool + ((size_t)max(mine_id, 0) * p.num_kv_heads + kvh) * C::BLK2 + 8 * D + j * 32 * NG);
   uint4 sx[2 * NG];
 #pragma unroll
-  for (int i = 0; i < 2 * NG; ++i) sx[i] = uint4{0u, 0u, 0u, 0u};
-  if (mine_id >= 0) {
-    const int base = (tile_first + my_slot) * kPage + 4 * j;
-    nv = min(max(hist_len - base, 0), 4);
-    const uint4* sp = (const uint4*)(pool + ((size_t)mine_id * p.num_kv_heads + kvh) * C::BLK2 + 8 * D + j * 32 * NG);
-#pragma unroll
-    for (int i = 0; i < 2 * NG; ++i) sx[i] = sp[i];
-  }
-  t.nvalid = nv;
+  for (int i = 0; i < 2 * NG; ++i) sx[i] = sp[i];
 #pragma unroll
   for (int i = 0; i < 2 * NG; ++i) {
     t.sc[4 * i + 0] = sx[i].x;
@@ -238,12 +230,65 @@ __device__ __forceinline__ void i2_load(I2Tile<D, NG, GQA>& t, const DecodeParam
     t.sc[4 * i + 2] = sx[i].z;
     t.sc[4 * i + 3] = sx[i].w;
   }
+  // lanes without a (slot, head) column exist only when SLOTS * GQA < 16
+  const bool clean = C::COLS < 16 ? (!full || mine_id < 0) : !full;
+  if (clean) {
+    // word 4*i + e of the K (i < NG) and V (i >= NG) quads belongs to token
+    // e / NG of this lane's quad
+#pragma unroll
+    for (int w = 0; w < 8 * NG; ++w)
+      if ((w % (4 * NG)) / NG >= nv) t.sc[w] = 0u;
+  }
+  t.nvalid = nv;
 }
 
+// P.V operands from packed value codes, without per-code shifts.  A value
+// word holds, for the lane's 4 tokens 4j+i and 4 channel blocks bb, the code
+// at bits 16*(i&1) + 2*(2*bb + (i>>1)).  One shift by 4*bb - 6 bits puts the
+// codes of tokens i = 0,1 at bits 6-7 of each 16-bit half and those of
+// i = 2,3 at bits 8-9; OR-ing in an fp16 exponent then gives exact fp16
+// values 16 + code (exponent 19) and 4 + code (exponent 17).  The biases 16
+// and 4 are removed through the per-token correction sum Z.
+template <int BB>
+__device__ __forceinline__ uint32_t v_shift(uint32_t x) {
+  if constexpr (BB == 0) return x << 6;
+  if constexpr (BB == 1) return x << 2;
+  if constexpr (BB == 2) return x >> 2;
+  return x >> 6;
+}
+constexpr uint32_t kMaskLo = 0x00C000C0u, kExpLo = 0x4C004C00u;  // tokens i = 0,1: 16 + code
+constexpr uint32_t kMaskHi = 0x03000300u, kExpHi = 0x44004400u;  // tokens i = 2,3: 4 + code
+constexpr float kBiasLo = 16.f, kBiasHi = 4.f;
+
+template <int D, int NG, int W0>
+__device__ __forceinline__ void pv_block_pair(Acc<D, NG>& st, uint32_t x0, uint32_t x1, const v4i (&bw)[NG],
+                                              uint32_t exp_lo, uint32_t exp_hi) {
+  constexpr int G = D / NG;
+  // the four channel blocks of this word pair, two pages per MFMA (k = 32)
+  auto one = [&](auto bbc) {
+    constexpr int BB = decltype(bbc)::value;
+    constexpr int cblk = 4 * W0 + BB;
+    constexpr int g = (cblk * 16) / G;
+    const uint32_t y0 = v_shift<BB>(x0), y1 = v_shift<BB>(x1);
+    const v4i a = {(int)((y0 & kMaskLo) | exp_lo), (int)((y0 & kMaskHi) | exp_hi), (int)((y1 & kMaskLo) | exp_lo),
+                   (int)((y1 & kMaskHi) | exp_hi)};
+    st.o[cblk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, bw[g]),
+                                                        st.o[cblk], 0, 0, 0);
+  };
+  one(std::integral_constant<int, 0>{});
+  one(std::integral_constant<int, 1>{});
+  one(std::integral_constant<int, 2>{});
+  one(std::integral_constant<int, 3>{});
+}
+
+// One INT2 tile.  Tokens outside the history (and every token of a lane
+// whose column holds no (slot, head) pair) get logit -inf; their scale words
+// are zero, so their weights are exactly zero.
 template <int D, int NG, int GQA>
 __device__ __forceinline__ void i2_compute(const I2Tile<D, NG, GQA>& t, Acc<D, NG>& st,
                                            const v4i (&bq)[DC<D, NG, GQA>::SLOTS][2][D / 64][64], float kappa,
-                                           const float (&sig)[NG], int my_slot, int lane) {
+                                           const float (&sig)[NG], int my_slot, int lane, uint32_t exp_lo,
+                                           uint32_t exp_hi) {
   using C = DC<D, NG, GQA>;
   // the q' operands are read from LDS on every tile: an opaque lane index
   // keeps the compiler from hoisting them into 64 loop-invariant VGPRs
@@ -259,8 +304,6 @@ __device__ __forceinline__ void i2_compute(const I2Tile<D, NG, GQA>& t, Acc<D, N
       const uint32_t x = t.kw[s][w];
       const v4i a = {(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
                      (int)((x >> 6) & 0x03030303u)};
-      constexpr int dummy = 0;
-      (void)dummy;
       const int g = (NG == 1) ? 0 : w;
       const v4i b0 = bq[s][0][w][lane], b1 = bq[s][1][w][lane];
       ca[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b0, ca[g], 0, 0, 0);
@@ -278,49 +321,40 @@ __device__ __forceinline__ void i2_compute(const I2Tile<D, NG, GQA>& t, Acc<D, N
       const uint32_t sz = t.sc[i * NG + g];
       acc += bf16_lo(sz) * (sint - bf16_hi(sz) * sig[g]);
     }
-    lg[i] = (i < t.nvalid) ? acc * kappa : -INFINITY;
+    lg[i] = fmaf(acc, kappa, i < t.nvalid ? 0.f : -INFINITY);
   }
   st.update_max(lg);
   float pr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(lg[i] - st.m);
   st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  // ---- bf16 weights w = p * s_V per group
-  uint32_t wb[NG][2];
+  // ---- fp16 weights w = p * s_V per group, and the correction
+  //      Z += sum w * (bias + z) with the rounded weights
+  v4i bw[C::SLOTS / 2][NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    float w[4], z[4];
+    float w[4], zb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t sz = t.sc[4 * NG + i * NG + g];
-      w[i] = (i < t.nvalid) ? pr[i] * bf16_lo(sz) : 0.f;
-      z[i] = (i < t.nvalid) ? bf16_hi(sz) : 0.f;
+      w[i] = pr[i] * bf16_lo(sz);
+      zb[i] = bf16_hi(sz) + (i < 2 ? kBiasLo : kBiasHi);
     }
-    wb[g][0] = pack_bf16x2(w[0], w[1]);
-    wb[g][1] = pack_bf16x2(w[2], w[3]);
-    const float r0 = bf16_lo(wb[g][0]), r1 = bf16_hi(wb[g][0]), r2 = bf16_lo(wb[g][1]), r3 = bf16_hi(wb[g][1]);
-    st.W[g] += (r0 + r1) + (r2 + r3);
-    st.Z[g] += (r0 * z[0] + r1 * z[1]) + (r2 * z[2] + r3 * z[3]);
+    const h2 w01 = __builtin_convertvector(f2{w[0], w[1]}, h2);
+    const h2 w23 = __builtin_convertvector(f2{w[2], w[3]}, h2);
+    st.Z[g] += ((float)w01[0] * zb[0] + (float)w01[1] * zb[1]) + ((float)w23[0] * zb[2] + (float)w23[1] * zb[3]);
+    const uint32_t u01 = __builtin_bit_cast(uint32_t, w01), u23 = __builtin_bit_cast(uint32_t, w23);
+#pragma unroll
+    for (int pp = 0; pp < C::SLOTS / 2; ++pp) {
+      const bool m0 = my_slot == 2 * pp, m1 = my_slot == 2 * pp + 1;
+      bw[pp][g] = v4i{(int)(m0 ? u01 : 0u), (int)(m0 ? u23 : 0u), (int)(m1 ? u01 : 0u), (int)(m1 ? u23 : 0u)};
+    }
   }
-  // ---- P.V on the bf16 matrix cores, value codes as 1 + code/8
+  // ---- P.V on the fp16 matrix cores, two pages per MFMA
 #pragma unroll
-  for (int s = 0; s < C::SLOTS; ++s) {
-    const bool mine = (my_slot == s);
-    v4s bw[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) bw[g] = as_v4s(mine ? wb[g][0] : 0u, mine ? wb[g][1] : 0u);
-#pragma unroll
-    for (int w = 0; w < C::KW; ++w) {
-      const uint32_t x = t.vw[s][w];
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int cblk = 4 * w + bb;
-        const int g = (cblk * 16) / C::G;
-        const uint32_t a0 = ((bb == 0 ? (x << 4) : (x >> (4 * bb - 4))) & 0x00300030u) | 0x3F803F80u;
-        const uint32_t a1 = ((bb == 0 ? (x << 2) : (x >> (4 * bb - 2))) & 0x00300030u) | 0x3F803F80u;
-        st.o[cblk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_v4s(a0, a1), bw[g], st.o[cblk], 0, 0, 0);
-      }
-    }
+  for (int pp = 0; pp < C::SLOTS / 2; ++pp) {
+    pv_block_pair<D, NG, 0>(st, t.vw[2 * pp][0], t.vw[2 * pp + 1][0], bw[pp], exp_lo, exp_hi);
+    if constexpr (C::KW > 1) pv_block_pair<D, NG, 1>(st, t.vw[2 * pp][1], t.vw[2 * pp + 1][1], bw[pp], exp_lo, exp_hi);
   }
 }
 
@@ -429,25 +463,19 @@ __device__ __forceinline__ void b16_compute(const B16Tile<D, GQA>& t, Acc<D, 1>&
 // -------------------------------------------------------- wave epilogue --
 // Reduce a wave's column states to one (o, lse) per query head and store it
 // in sm.part[wave].  INT2: channel of o[cb][i] is cb*16 + 4j + i and the
-// numerator is 8 (acc - W) - Z.  BF16: channel (4j + i) * D/16 + cb.
+// numerator is acc - Z.  BF16: channel (4j + i) * D/16 + cb.
 template <int D, int NG, int GQA, bool INT2>
 __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, int wave, int lane) {
   constexpr int G = D / NG;
   const int n = lane & 15, j = lane >> 4;
   st.l = col_sum(st.l);
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    st.W[g] = col_sum(st.W[g]);
-    st.Z[g] = col_sum(st.Z[g]);
-  }
+  for (int g = 0; g < NG; ++g) st.Z[g] = col_sum(st.Z[g]);
   const float mh = slot_max<GQA>(st.m);
   st.scale(__builtin_amdgcn_exp2f(st.m - mh));
   st.l = slot_sum<GQA>(st.l);
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    st.W[g] = slot_sum<GQA>(st.W[g]);
-    st.Z[g] = slot_sum<GQA>(st.Z[g]);
-  }
+  for (int g = 0; g < NG; ++g) st.Z[g] = slot_sum<GQA>(st.Z[g]);
 #pragma unroll
   for (int cbk = 0; cbk < D / 16; ++cbk)
 #pragma unroll
@@ -462,7 +490,7 @@ __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, in
         int c;
         if constexpr (INT2) {
           const int g = (cbk * 16) / G;
-          o = (8.f * (st.o[cbk][i] - st.W[g]) - st.Z[g]) * inv;
+          o = (st.o[cbk][i] - st.Z[g]) * inv;
           c = cbk * 16 + 4 * j + i;
         } else {
           o = st.o[cbk][i] * inv;
@@ -638,6 +666,10 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int g = 0; g < NG; ++g) sig[g] = (float)sm.sig[chd * NG + g];
     const float kappa = p.sm_log2 * sq * (1.f / 256.f);
+    // fp16 exponent patterns of the P.V operands, held in VGPRs so that each
+    // operand is one and-or (bitop3) of a shifted code word
+    uint32_t exp_lo = kExpLo, exp_hi = kExpHi;
+    asm volatile("" : "+v"(exp_lo), "+v"(exp_hi));
 
     Acc<D, NG> st;
     st.init();
@@ -647,7 +679,7 @@ __global__ void __launch_bounds__(kThreads)
       for (int r = 0; r < kRing; ++r) {
         if (tile >= ntiles) break;
         ld(ring[(r + kRing - 1) % kRing], tile + (kRing - 1) * kWaves);
-        i2_compute<D, NG, GQA>(ring[r], st, sm.bq, kappa, sig, my_slot, lane);
+        i2_compute<D, NG, GQA>(ring[r], st, sm.bq, kappa, sig, my_slot, lane, exp_lo, exp_hi);
         tile += kWaves;
       }
       if (tile >= ntiles) break;
@@ -697,7 +729,7 @@ __global__ void __launch_bounds__(kThreads)
       st2.m = st.m;
       st2.l = st.l;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) st2.W[g] = st2.Z[g] = 0.f;
+      for (int g = 0; g < NG; ++g) st2.Z[g] = 0.f;
     }
     wave_finish<D, NG, GQA, false>(st2, sm, wave, lane);
   }
