@@ -9,8 +9,10 @@ oscar_write_bf16) from seeded synthetic tensors.
 
 Timing protocol: the pool working set of one step (58.7 MB at 100K tokens)
 fits the 256 MB Infinity Cache, so steps rotate through independent pool
-copies totalling >= 2 GiB (cold-cache); the K timed steps are replayed from
-a HIP graph and bracketed by HIP events on the launch stream.  The median of
+copies totalling >= 2 GiB (cold-cache), one pool tensor per copy like the
+per-layer KV caches of a model, all sharing the sequences' page tables as a
+model's layers do; the K timed steps are replayed from a HIP graph and
+bracketed by HIP events on the launch stream.  The median of
 several repeats is reported; warm (single copy) and eager-launch numbers are
 reported beside it.
 
@@ -57,7 +59,7 @@ def parse():
 class Decoder:
     """Pre-marshalled oscar_decode_attention calls, one per pool copy."""
 
-    def __init__(self, oscar, pool, wl, q, lens, copies, int2_pool, bf16_pool, r_k, out, ws, bf16_only=False):
+    def __init__(self, oscar, pool, wl, q, lens, copies, r_k, out, ws, bf16_only=False):
         import torch
         lib = oscar.load()
         self.lib = lib
@@ -65,15 +67,16 @@ class Decoder:
         self.torch = torch
         self.args = []
         for c in copies:
+            b16, i2 = c["bf16_pool"], c["int2_pool"]
             if bf16_only:
                 self.args.append((pool.handle, wl.batch, max(wl.seq_lens), q.data_ptr(), lens.data_ptr(),
-                                  c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], bf16_pool.shape[0],
-                                  bf16_pool.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()))
+                                  c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], b16.shape[0],
+                                  b16.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()))
             else:
                 self.args.append((pool.handle, wl.batch, max(wl.seq_lens), q.data_ptr(), lens.data_ptr(),
-                                  c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], bf16_pool.shape[0],
-                                  c["int2_pt"].data_ptr(), c["int2_pt"].shape[1], int2_pool.shape[0],
-                                  bf16_pool.data_ptr(), int2_pool.data_ptr(), r_k.data_ptr(), None,
+                                  c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], b16.shape[0],
+                                  c["int2_pt"].data_ptr(), c["int2_pt"].shape[1], i2.shape[0],
+                                  b16.data_ptr(), i2.data_ptr(), r_k.data_ptr(), None,
                                   out.data_ptr(), ws.data_ptr(), ws.numel()))
         self.fn = lib.oscar_bf16_decode_attention if bf16_only else lib.oscar_decode_attention
 
@@ -84,11 +87,16 @@ class Decoder:
             raise RuntimeError(self.lib.oscar_last_error().decode())
 
 
-def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0):
-    """n_copies independent pools of one workload, written by the library."""
+def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0, shared_tables=True):
+    """n_copies independent pools of one workload, written by the library.
+
+    shared_tables=True models one layer's KV cache per copy: every copy has
+    its own pool tensor (a slice of one allocation) and all copies share the
+    sequences' page tables, as the layers of a model share a sequence's page
+    table.  shared_tables=False gives every copy its own page tables over one
+    big pool (the page-table reads are then cold as well)."""
     import numpy as np
     import torch
-    hkv, d = wl.num_kv_heads, wl.head_dim
     rng = np.random.Generator(np.random.PCG64(seed + 300))
     c = inp.calib
     r_k = torch.as_tensor(c.r_k).cuda()
@@ -105,17 +113,16 @@ def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0):
             b16_lists.append([p for p in range((L + 15) // 16)
                               if p * 16 < min(L, wl.sink) or ((p + 1) * 16 > r0 and p * 16 < L)])
             i2_counts.append((wl.hist_len(L) + 15) // 16)
-    n16 = sum(len(x) for x in b16_lists) * n_copies
-    n2 = sum(i2_counts) * n_copies
-    bf16_pool = torch.empty((max(n16, 1), pool.bf16_page_bytes), dtype=torch.uint8, device="cuda")
-    int2_pool = torch.empty((max(n2, 1), pool.int2_page_bytes), dtype=torch.uint8, device="cuda")
-    perm16 = rng.permutation(max(n16, 1))
-    perm2 = rng.permutation(max(n2, 1))
-    p16 = p2 = 0
-    copies = []
-    for _ in range(n_copies):
+    n16c = max(sum(len(x) for x in b16_lists), 1)  # pages per copy
+    n2c = max(sum(i2_counts), 1)
+    bf16_all = torch.empty((n16c * n_copies, pool.bf16_page_bytes), dtype=torch.uint8, device="cuda")
+    int2_all = torch.empty((n2c * n_copies, pool.int2_page_bytes), dtype=torch.uint8, device="cuda")
+
+    def tables(n16, n2):
+        perm16, perm2 = rng.permutation(n16), rng.permutation(n2)
         bpt = np.full((wl.batch, max_pages + 1), -1, np.int32)
         ipt = np.full((wl.batch, max(max(i2_counts), 1)), -1, np.int32)
+        p16 = p2 = 0
         for b in range(wl.batch):
             for lp in b16_lists[b]:
                 bpt[b, lp] = perm16[p16]
@@ -123,25 +130,45 @@ def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0):
             for lp in range(i2_counts[b]):
                 ipt[b, lp] = perm2[p2]
                 p2 += 1
-        cp = {"bf16_pt": torch.from_numpy(bpt).cuda(), "int2_pt": torch.from_numpy(ipt).cuda()}
+        return torch.from_numpy(bpt).cuda(), torch.from_numpy(ipt).cuda()
+
+    shared = tables(n16c, n2c) if shared_tables else None
+    if not shared_tables:
+        glob16, glob2 = rng.permutation(n16c * n_copies), rng.permutation(n2c * n_copies)
+    copies = []
+    for ci in range(n_copies):
+        if shared_tables:
+            bpt, ipt = shared
+            b16, i2 = bf16_all[ci * n16c:(ci + 1) * n16c], int2_all[ci * n2c:(ci + 1) * n2c]
+        else:
+            # distinct tables over the whole allocation; copy ci owns the
+            # pages its permutation slice names
+            perm16 = glob16[ci * n16c:(ci + 1) * n16c]
+            perm2 = glob2[ci * n2c:(ci + 1) * n2c]
+            bpt_h, ipt_h = tables(n16c, n2c)
+            bpt = torch.from_numpy(np.where(bpt_h.cpu().numpy() >= 0, perm16[np.maximum(bpt_h.cpu().numpy(), 0)], -1)
+                                   .astype(np.int32)).cuda()
+            ipt = torch.from_numpy(np.where(ipt_h.cpu().numpy() >= 0, perm2[np.maximum(ipt_h.cpu().numpy(), 0)], -1)
+                                   .astype(np.int32)).cuda()
+            b16, i2 = bf16_all, int2_all
+        cp = {"bf16_pt": bpt, "int2_pt": ipt, "bf16_pool": b16, "int2_pool": i2}
         for b, L in enumerate(wl.seq_lens):
             k, v = inp.k[b], inp.v[b]
             if bf16_only:
-                oscar.oscar_write_bf16(pool, k[:L].contiguous(), v[:L].contiguous(), 0, cp["bf16_pt"][b], bf16_pool)
+                oscar.oscar_write_bf16(pool, k[:L].contiguous(), v[:L].contiguous(), 0, bpt[b], b16)
                 continue
             sink = min(L, wl.sink)
-            oscar.oscar_write_bf16(pool, k[:sink].contiguous(), v[:sink].contiguous(), 0, cp["bf16_pt"][b], bf16_pool)
+            oscar.oscar_write_bf16(pool, k[:sink].contiguous(), v[:sink].contiguous(), 0, bpt[b], b16)
             r0 = wl.recent_start(L)
             if r0 < L:
-                oscar.oscar_write_bf16(pool, k[r0:L].contiguous(), v[r0:L].contiguous(), r0, cp["bf16_pt"][b],
-                                       bf16_pool)
+                oscar.oscar_write_bf16(pool, k[r0:L].contiguous(), v[r0:L].contiguous(), r0, bpt[b], b16)
             h = wl.hist_len(L)
             if h:
                 oscar.oscar_quantize_pack(pool, k[wl.sink:wl.sink + h].contiguous(), v[wl.sink:wl.sink + h].contiguous(),
-                                          cp["int2_pt"][b, :i2_counts[b]].contiguous(), int2_pool, r_k, tau_k, tau_v)
+                                          ipt[b, :i2_counts[b]].contiguous(), i2, r_k, tau_k, tau_v)
         copies.append(cp)
     torch.cuda.synchronize()
-    return copies, int2_pool, bf16_pool, r_k
+    return copies, r_k
 
 
 def time_steps(step, n_steps, warmup, repeats, use_graph=True):
@@ -282,13 +309,13 @@ def main():
     pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
                                             wl.sink, wl.recent, 1, 0.0))
     n_copies = max(1, math.ceil(args.cold_bytes / kv["total"]))
-    copies, int2_pool, bf16_pool, r_k = build_pools(oscar, pool, wl, inp, n_copies, seed=wl.seed)
+    copies, r_k = build_pools(oscar, pool, wl, inp, n_copies, seed=wl.seed)
     log(f"built {n_copies} pool copies ({n_copies * kv['total'] / 2**30:.2f} GiB of KV)")
     q = inp.q.contiguous()
     lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     ws = pool.alloc_workspace(wl.batch, max(wl.seq_lens))
-    dec = Decoder(oscar, pool, wl, q, lens, copies, int2_pool, bf16_pool, r_k, out, ws)
+    dec = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws)
     if args.profile_steps:
         for i in range(args.profile_steps):
             dec(i)
@@ -301,9 +328,18 @@ def main():
     log(f"INT2 decode (graph, cold): {ms * 1e3:.2f} us/step (min {ms_min * 1e3:.2f})")
     ms_eager, _ = time_steps(dec, args.steps, args.warmup, 3, use_graph=False)
     log(f"INT2 decode (eager, cold): {ms_eager * 1e3:.2f} us/step")
-    warm = Decoder(oscar, pool, wl, q, lens, copies[:1], int2_pool, bf16_pool, r_k, out, ws)
+    warm = Decoder(oscar, pool, wl, q, lens, copies[:1], r_k, out, ws)
     ms_warm, _ = time_steps(warm, args.steps, args.warmup, 3, use_graph=True)
     log(f"INT2 decode (graph, warm single copy): {ms_warm * 1e3:.2f} us/step")
+    del warm, dec, copies
+    torch.cuda.empty_cache()
+    # the same protocol with a private page table per copy (page-table reads cold too)
+    pcopies, _ = build_pools(oscar, pool, wl, inp, n_copies, seed=wl.seed + 2, shared_tables=False)
+    pdec = Decoder(oscar, pool, wl, q, lens, pcopies, r_k, out, ws)
+    ms_priv, _ = time_steps(pdec, args.steps, args.warmup, 3, use_graph=True)
+    log(f"INT2 decode (graph, cold, private page table per copy): {ms_priv * 1e3:.2f} us/step")
+    del pdec, pcopies
+    torch.cuda.empty_cache()
 
     gbps = kv["total"] / (ms * 1e-3) / 1e9
     result = {
@@ -313,31 +349,31 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "group_size": wl.group_size, "context": list(wl.seq_lens)[:4],
                    "sink": wl.sink, "recent": wl.recent, "page_size": 16, "pool_copies": n_copies,
-                   "timing": "HIP-graph replay of the timed steps, cold cache (rotating pool copies)"},
+                   "timing": "HIP-graph replay of the timed steps, cold cache: rotating over per-layer pool "
+                             "copies that share the sequence's page tables"},
         "tokens_per_s": round(wl.batch / (ms * 1e-3), 1),
         "kv_tokens_scanned_per_s": round(sum(wl.seq_lens) / (ms * 1e-3), 1),
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_step": kv["total"],
         "eager_ms_per_step": round(ms_eager, 6),
         "warm_ms_per_step": round(ms_warm, 6),
+        "private_tables_ms_per_step": round(ms_priv, 6),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_for(wl.name),
                      "kernel": "k_decode (INT2 split-K + BF16 sink/recent + LSE merge, one launch per step)"},
     }
     if not args.no_bf16:
-        del copies
-        torch.cuda.empty_cache()
         n16 = max(1, math.ceil(args.cold_bytes / kv["bf16_only_total"]))
-        bcopies, _, bpool, _ = build_pools(oscar, pool, wl, inp, n16, bf16_only=True, seed=wl.seed + 1)
+        bcopies, _ = build_pools(oscar, pool, wl, inp, n16, bf16_only=True, seed=wl.seed + 1)
         bws = pool.alloc_workspace(wl.batch, max(wl.seq_lens), bf16_only=True)
-        bdec = Decoder(oscar, pool, wl, q, lens, bcopies, int2_pool, bpool, r_k, out, bws, bf16_only=True)
+        bdec = Decoder(oscar, pool, wl, q, lens, bcopies, r_k, out, bws, bf16_only=True)
         ms16, _ = time_steps(bdec, max(20, args.steps // 4), args.warmup, args.repeats, use_graph=True)
         log(f"BF16-only decode (graph, cold): {ms16 * 1e3:.2f} us/step")
         result["bf16_comparator"] = {"ms_per_step": round(ms16, 6),
                                      "kv_GBps": round(kv["bf16_only_total"] / (ms16 * 1e-3) / 1e9, 2),
                                      "kv_bytes_per_step": kv["bf16_only_total"], "pool_copies": n16,
                                      "int2_speedup": round(ms16 / ms, 3)}
-        del bcopies, bpool
+        del bcopies
         torch.cuda.empty_cache()
     result["copy_ceiling_GBps"] = round(copy_ceiling_gbps(), 1)
     if not args.no_cpu_baseline:

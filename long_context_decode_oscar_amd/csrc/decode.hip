@@ -11,8 +11,9 @@
 // INT2 history (per wave, tiles of SLOTS pages):
 //   scores  S = codes . q'  on the int8 matrix cores.  q' = q R_K (the online
 //           rotation, MarkTechPost article, "Outcome") is computed once per
-//           workgroup and split into two int8 terms, q' ~ sq (a + b/256), so
-//           the integer dot is exact and q' carries ~16 significant bits.
+//           workgroup in fp32 and split, per query head, into two int8 terms,
+//           q' ~ sq (a + b/256), so the integer dot is exact and q' carries
+//           ~16 significant bits.
 //           With the key dequantization k' = s (code - z) the logit is
 //           sm * s * sq/256 * (S_ab - z * sum(256 a + b)).
 //   P.V     on the bf16 matrix cores with the value codes as exact bf16
@@ -23,6 +24,9 @@
 // The GQA query heads of a KV head share every loaded page; the 16 columns
 // of each MFMA tile hold (page slot, query head) pairs, so one score tile
 // covers SLOTS pages and all softmax arithmetic is shared across them.
+// Each wave keeps a ring of tiles in flight and is software-pipelined: the
+// score MFMAs of tile i+1 are issued next to the softmax and P.V work of
+// tile i, so matrix-core and vector work of one wave overlap.
 #include <math.h>
 
 #include <type_traits>
@@ -38,17 +42,19 @@ namespace {
 #define OSCAR_DECODE_WAVES 8
 #endif
 #ifndef OSCAR_DECODE_RING
-#define OSCAR_DECODE_RING 2
+#define OSCAR_DECODE_RING 3
 #endif
 #ifndef OSCAR_BF16_SLOTS
 #define OSCAR_BF16_SLOTS 2
 #endif
 constexpr int kWaves = OSCAR_DECODE_WAVES;  // waves per workgroup
-constexpr int kRing = OSCAR_DECODE_RING;    // INT2 tiles held per wave (1 computing + kRing-1 in flight)
+constexpr int kRing = OSCAR_DECODE_RING;    // INT2 tiles held per wave (ring of loads in flight)
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1.0e30f;  // finite "no token yet" running max
 constexpr float kLazy = 8.0f;        // log2 slack before the running max is raised
-constexpr float kLn2 = 0.69314718055994530942f;
+// dword 3 of a gfx9 buffer descriptor for raw (untyped) loads: 32-bit data
+// format, no swizzle; out-of-range offsets read as zero
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D, int NG, int GQA>
 struct DC {
@@ -69,29 +75,66 @@ template <int D, int GQA>
 struct Smem {
   static constexpr int SLOTS = (16 / GQA) < 4 ? (16 / GQA) : 4;
   union {
-    float part[kWaves][GQA][D + 1];   // per-wave partials, [D] = lse (log2)
-    float wts[kWaves * GQA * (D + 1)];  // final-merge weights [unit][head]
+    float part[kWaves][GQA][D + 1];  // per-wave partials, [D] = lse (log2)
+    float qpart[kWaves][GQA][D];     // prologue: per-wave partial sums of q R_K
   } u;
-  v4i bq[SLOTS][2][D / 64][64];       // int8 q' B operands per lane (shared by the waves)
-  float qr[GQA * D];                  // q' = q R_K (fp32)
-  alignas(16) int8_t ta[GQA * D];     // int8 terms of q'
-  alignas(16) int8_t tb[GQA * D];
-  int sig[GQA * 2];                   // sum(256 a + b) per head and group
-  float wred[kWaves];
+  v4i bq[SLOTS][2][D / 64][64];      // int8 q' B operands per lane (shared by the waves)
+  float kap[GQA];                    // logit factor sm * log2(e) * sq / 256 per query head
+  int sig[GQA * 2];                  // sum(256 a + b) per head and group
   int last;
 };
 
 // ---------------------------------------------------------------- helpers --
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+// Cross-lane reductions without LDS: DPP row rotations inside each 16-lane
+// row, then the gfx950 permlane swaps, which exchange rows 0<->1, 2<->3
+// (lane l meets l^16) and the two 32-lane halves (lane l meets l^32).
+__device__ __forceinline__ uint32_t as_u(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ float xor16_add(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(as_u(x), as_u(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+__device__ __forceinline__ float xor32_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(as_u(x), as_u(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int xor16_add(int x) {
+  const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (int)r[0] + (int)r[1];
+}
+__device__ __forceinline__ int xor32_add(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (int)r[0] + (int)r[1];
+}
+template <int N>
+__device__ __forceinline__ int dpp_row_ror_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, 0x120 + N, 0xF, 0xF, false);
+}
+// every lane receives the reduction over its 16-lane row
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp_row_ror<8>(x));
+  x = fmaxf(x, dpp_row_ror<4>(x));
+  x = fmaxf(x, dpp_row_ror<2>(x));
+  return fmaxf(x, dpp_row_ror<1>(x));
+}
+__device__ __forceinline__ int row_sum_i(int x) {
+  x += dpp_row_ror_i<8>(x);
+  x += dpp_row_ror_i<4>(x);
+  x += dpp_row_ror_i<2>(x);
+  return x + dpp_row_ror_i<1>(x);
+}
+// every lane receives the reduction over the wave
+__device__ __forceinline__ float wave_max(float x) { return xor32_max(xor16_max(row_max(x))); }
+__device__ __forceinline__ int wave_sum_i(int x) { return xor32_add(xor16_add(row_sum_i(x))); }
+// over one 32-lane half
+__device__ __forceinline__ int half_sum_i(int x) { return xor16_add(row_sum_i(x)); }
 // max / sum over the columns of one 16-lane row that hold the same query head
 template <int GQA>
 __device__ __forceinline__ float slot_max(float x) {
@@ -107,16 +150,9 @@ __device__ __forceinline__ float slot_sum(float x) {
   if constexpr (4 * GQA < 16) x += dpp_row_ror<4 * GQA>(x);
   return x;
 }
-__device__ __forceinline__ float col_sum(float x) {  // over the 4 lane groups
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-__device__ __forceinline__ float col_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
+// over the 4 lane groups j (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float col_sum(float x) { return xor32_add(xor16_add(x)); }
+__device__ __forceinline__ float col_max(float x) { return xor32_max(xor16_max(x)); }
 __device__ __forceinline__ v4s as_v4s(uint32_t lo, uint32_t hi) {
   v4s r;
   r[0] = (short)(lo & 0xFFFF);
@@ -128,18 +164,6 @@ __device__ __forceinline__ v4s as_v4s(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ v8bf as_v8bf(uint4 x) {
   return __builtin_bit_cast(v8bf, x);
 }
-// byte transpose: out[m].byte[b] = in[b].byte[m]
-__device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
-  const uint32_t t01l = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
-  const uint32_t t23l = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
-  const uint32_t t01h = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
-  const uint32_t t23h = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
-}
-
 // online-softmax state of one wave: accumulators O^T[channel][column]
 template <int D, int NG>
 struct Acc {
@@ -180,46 +204,76 @@ struct I2Tile {
   uint32_t vw[C::SLOTS][C::KW];
   uint32_t sc[8 * NG];  // own page's quad: K (s,z) x 4 tokens x NG, then V
   int nvalid;           // valid rows (a prefix) among this lane's 4 tokens
+  // keeps every register of the tile live (and in place) up to this point:
+  // the registers of a ring slot are then never reused as temporaries while
+  // the slot waits for its next load
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int s = 0; s < C::SLOTS; ++s)
+#pragma unroll
+      for (int w = 0; w < C::KW; ++w) asm volatile("" : "+v"(kw[s][w]), "+v"(vw[s][w]));
+#pragma unroll
+    for (int w = 0; w < 8 * NG; ++w) asm volatile("" : "+v"(sc[w]));
+    asm volatile("" : "+v"(nvalid));
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int s = 0; s < C::SLOTS; ++s)
+#pragma unroll
+      for (int w = 0; w < C::KW; ++w) kw[s][w] = vw[s][w] = 0u;
+#pragma unroll
+    for (int w = 0; w < 8 * NG; ++w) sc[w] = 0u;
+    nvalid = 0;
+  }
 };
 
-// Loads one tile: SLOTS consecutive logical pages of one KV head.  Code
-// records of absent pages are read from physical page 0 (never used: their
-// scales are zero and their logits -inf); scale words of tokens that are not
-// history tokens are zeroed, so stale bits can never reach the arithmetic.
+// Loads one tile: SLOTS consecutive logical history pages of one KV head,
+// starting at logical page lp0.  The physical ids come from lanes idx0 ..
+// idx0+SLOTS-1 of `pids` (-1 = absent; idx0 < 0: no page at all), so every
+// code address is a uniform base plus the lane's record offset.  Records of absent pages are read from
+// physical page 0 (never used: their scales are zero and their logits
+// -inf); scale words of tokens that are not history tokens are zeroed, so
+// stale bits can never reach the arithmetic.
 template <int D, int NG, int GQA>
-__device__ __forceinline__ void i2_load(I2Tile<D, NG, GQA>& t, const DecodeParams& p,
-                                        const int32_t* __restrict__ pt, const uint8_t* __restrict__ pool, int kvh,
-                                        int tile_first, int page_end, int hist_len, int lane, int my_slot) {
+__device__ __forceinline__ void i2_fetch(I2Tile<D, NG, GQA>& t, const uint8_t* __restrict__ hpool,
+                                         size_t page_bytes, int pids, int idx0, int lp0, int hist_len, int my_slot,
+                                         int lane) {
   using C = DC<D, NG, GQA>;
   const int j = lane >> 4;
-  const uint32_t rec_off = (uint32_t)lane * C::REC;
-  int mine_id = -1;
-  bool full = (tile_first + C::SLOTS) * kPage <= hist_len && tile_first + C::SLOTS <= page_end;
+  int ids[C::SLOTS];
+  bool full = (lp0 + C::SLOTS) * kPage <= hist_len;
+  const int i0 = idx0 >= 0 ? idx0 : 0;
 #pragma unroll
   for (int s = 0; s < C::SLOTS; ++s) {
-    const int lp = tile_first + s;
-    int id = -1;
-    if (lp < page_end) id = pt[lp];
-    const bool ok = id >= 0 && id < p.int2_num_pages;
-    full = full && ok;
-    if (s == my_slot) mine_id = ok ? id : -1;
-    const uint8_t* blk = pool + ((size_t)(ok ? id : 0) * p.num_kv_heads + kvh) * C::BLK2;
+    const int v = __builtin_amdgcn_readlane(pids, i0 + s);
+    ids[s] = idx0 >= 0 ? v : -1;
+    full = full && ids[s] >= 0;
+  }
+  int mine = -1;
+#pragma unroll
+  for (int s = 0; s < C::SLOTS; ++s)
+    if (s == my_slot) mine = ids[s];
+  // code records: one buffer descriptor per page (scalar registers), the
+  // lane's record offset as the only per-lane address term
+#pragma unroll
+  for (int s = 0; s < C::SLOTS; ++s) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(hpool + (size_t)max(ids[s], 0) * page_bytes), (short)0, C::BLK2, kBufferFlags);
     if constexpr (D == 128) {
-      const uint4 x = *(const uint4*)(blk + rec_off);
-      t.kw[s][0] = x.x;
-      t.kw[s][1] = x.y;
-      t.vw[s][0] = x.z;
-      t.vw[s][1] = x.w;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * C::REC, 0, 0);
+      t.kw[s][0] = x[0];
+      t.kw[s][1] = x[1];
+      t.vw[s][0] = x[2];
+      t.vw[s][1] = x[3];
     } else {
-      const uint2 y = *(const uint2*)(blk + rec_off);
-      t.kw[s][0] = y.x;
-      t.vw[s][0] = y.y;
+      const auto y = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * C::REC, 0, 0);
+      t.kw[s][0] = y[0];
+      t.vw[s][0] = y[1];
     }
   }
-  const int base = (tile_first + my_slot) * kPage + 4 * j;
-  const int nv = mine_id >= 0 ? min(max(hist_len - base, 0), 4) : 0;
-  const uint4* sp =
-      (const uint4*)(pool + ((size_t)max(mine_id, 0) * p.num_kv_heads + kvh) * C::BLK2 + 8 * D + j * 32 * NG);
+  const int base = (lp0 + my_slot) * kPage + 4 * j;
+  const int nv = mine >= 0 ? min(max(hist_len - base, 0), 4) : 0;
+  const uint4* sp = (const uint4*)(hpool + (size_t)max(mine, 0) * page_bytes + 8 * D + j * 32 * NG);
   uint4 sx[2 * NG];
 #pragma unroll
   for (int i = 0; i < 2 * NG; ++i) sx[i] = sp[i];
@@ -231,7 +285,7 @@ __device__ __forceinline__ void i2_load(I2Tile<D, NG, GQA>& t, const DecodeParam
     t.sc[4 * i + 3] = sx[i].w;
   }
   // lanes without a (slot, head) column exist only when SLOTS * GQA < 16
-  const bool clean = C::COLS < 16 ? (!full || mine_id < 0) : !full;
+  const bool clean = C::COLS < 16 ? (!full || mine < 0) : !full;
   if (clean) {
     // word 4*i + e of the K (i < NG) and V (i >= NG) quads belongs to token
     // e / NG of this lane's quad
@@ -240,6 +294,36 @@ __device__ __forceinline__ void i2_load(I2Tile<D, NG, GQA>& t, const DecodeParam
       if ((w % (4 * NG)) / NG >= nv) t.sc[w] = 0u;
   }
   t.nvalid = nv;
+}
+
+template <int NG>
+struct I2Scores {
+  v4i a[NG], b[NG];  // integer dots with the two int8 terms of q', per group
+};
+
+// Scores of one tile on the int8 matrix cores (block-diagonal B operands:
+// slot s's page meets only the columns of slot s).  The operands are
+// loop-invariant and held in VGPRs.
+template <int D, int NG, int GQA>
+__device__ __forceinline__ I2Scores<NG> i2_scores(const I2Tile<D, NG, GQA>& t,
+                                                  const v4i (&bq)[DC<D, NG, GQA>::SLOTS][2][D / 64]) {
+  using C = DC<D, NG, GQA>;
+  I2Scores<NG> r;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) r.a[g] = r.b[g] = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int s = 0; s < C::SLOTS; ++s) {
+#pragma unroll
+    for (int w = 0; w < C::KW; ++w) {
+      const uint32_t x = t.kw[s][w];
+      const v4i a = {(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
+                     (int)((x >> 6) & 0x03030303u)};
+      const int g = (NG == 1) ? 0 : w;
+      r.a[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq[s][0][w], r.a[g], 0, 0, 0);
+      r.b[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq[s][1][w], r.b[g], 0, 0, 0);
+    }
+  }
+  return r;
 }
 
 // P.V operands from packed value codes, without per-code shifts.  A value
@@ -281,35 +365,19 @@ __device__ __forceinline__ void pv_block_pair(Acc<D, NG>& st, uint32_t x0, uint3
   one(std::integral_constant<int, 3>{});
 }
 
-// One INT2 tile.  Tokens outside the history (and every token of a lane
-// whose column holds no (slot, head) pair) get logit -inf; their scale words
-// are zero, so their weights are exactly zero.
+// Softmax of one INT2 tile from its scores: logits, online max and sum, and
+// the fp16 P.V weights.  Tokens outside the history (and every token of a
+// lane whose column holds no (slot, head) pair) get logit -inf; their scale
+// words are zero, so their weights are exactly zero.
 template <int D, int NG, int GQA>
-__device__ __forceinline__ void i2_compute(const I2Tile<D, NG, GQA>& t, Acc<D, NG>& st,
-                                           const v4i (&bq)[DC<D, NG, GQA>::SLOTS][2][D / 64][64], float kappa,
-                                           const float (&sig)[NG], int my_slot, int lane, uint32_t exp_lo,
-                                           uint32_t exp_hi) {
+struct I2Weights {
+  v4i bw[DC<D, NG, GQA>::SLOTS / 2][NG];  // block-diagonal B operands of the P.V MFMAs
+};
+template <int D, int NG, int GQA>
+__device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, GQA>& t, const I2Scores<NG>& S,
+                                                           Acc<D, NG>& st, float kappa, const float (&sig)[NG],
+                                                           int my_slot) {
   using C = DC<D, NG, GQA>;
-  // the q' operands are read from LDS on every tile: an opaque lane index
-  // keeps the compiler from hoisting them into 64 loop-invariant VGPRs
-  asm volatile("" : "+v"(lane));
-  // ---- scores on the int8 matrix cores
-  v4i ca[NG], cb[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) ca[g] = cb[g] = v4i{0, 0, 0, 0};
-#pragma unroll
-  for (int s = 0; s < C::SLOTS; ++s) {
-#pragma unroll
-    for (int w = 0; w < C::KW; ++w) {
-      const uint32_t x = t.kw[s][w];
-      const v4i a = {(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
-                     (int)((x >> 6) & 0x03030303u)};
-      const int g = (NG == 1) ? 0 : w;
-      const v4i b0 = bq[s][0][w][lane], b1 = bq[s][1][w][lane];
-      ca[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b0, ca[g], 0, 0, 0);
-      cb[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b1, cb[g], 0, 0, 0);
-    }
-  }
   // ---- logits (log2 domain)
   float lg[4];
 #pragma unroll
@@ -317,7 +385,7 @@ __device__ __forceinline__ void i2_compute(const I2Tile<D, NG, GQA>& t, Acc<D, N
     float acc = 0.f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const float sint = (float)(ca[g][i] * 256 + cb[g][i]);
+      const float sint = (float)(S.a[g][i] * 256 + S.b[g][i]);
       const uint32_t sz = t.sc[i * NG + g];
       acc += bf16_lo(sz) * (sint - bf16_hi(sz) * sig[g]);
     }
@@ -330,7 +398,7 @@ __device__ __forceinline__ void i2_compute(const I2Tile<D, NG, GQA>& t, Acc<D, N
   st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   // ---- fp16 weights w = p * s_V per group, and the correction
   //      Z += sum w * (bias + z) with the rounded weights
-  v4i bw[C::SLOTS / 2][NG];
+  I2Weights<D, NG, GQA> W;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     float w[4], zb[4];
@@ -347,14 +415,22 @@ __device__ __forceinline__ void i2_compute(const I2Tile<D, NG, GQA>& t, Acc<D, N
 #pragma unroll
     for (int pp = 0; pp < C::SLOTS / 2; ++pp) {
       const bool m0 = my_slot == 2 * pp, m1 = my_slot == 2 * pp + 1;
-      bw[pp][g] = v4i{(int)(m0 ? u01 : 0u), (int)(m0 ? u23 : 0u), (int)(m1 ? u01 : 0u), (int)(m1 ? u23 : 0u)};
+      W.bw[pp][g] = v4i{(int)(m0 ? u01 : 0u), (int)(m0 ? u23 : 0u), (int)(m1 ? u01 : 0u), (int)(m1 ? u23 : 0u)};
     }
   }
-  // ---- P.V on the fp16 matrix cores, two pages per MFMA
+  return W;
+}
+
+// P.V of one INT2 tile on the fp16 matrix cores, two pages per MFMA.
+template <int D, int NG, int GQA>
+__device__ __forceinline__ void i2_pv(const I2Tile<D, NG, GQA>& t, const I2Weights<D, NG, GQA>& W, Acc<D, NG>& st,
+                                      uint32_t exp_lo, uint32_t exp_hi) {
+  using C = DC<D, NG, GQA>;
 #pragma unroll
   for (int pp = 0; pp < C::SLOTS / 2; ++pp) {
-    pv_block_pair<D, NG, 0>(st, t.vw[2 * pp][0], t.vw[2 * pp + 1][0], bw[pp], exp_lo, exp_hi);
-    if constexpr (C::KW > 1) pv_block_pair<D, NG, 1>(st, t.vw[2 * pp][1], t.vw[2 * pp + 1][1], bw[pp], exp_lo, exp_hi);
+    pv_block_pair<D, NG, 0>(st, t.vw[2 * pp][0], t.vw[2 * pp + 1][0], W.bw[pp], exp_lo, exp_hi);
+    if constexpr (C::KW > 1)
+      pv_block_pair<D, NG, 1>(st, t.vw[2 * pp][1], t.vw[2 * pp + 1][1], W.bw[pp], exp_lo, exp_hi);
   }
 }
 
@@ -523,7 +599,46 @@ __global__ void __launch_bounds__(kThreads)
   const int b = lin / (U * p.num_kv_heads);
   const int hq = p.num_kv_heads * GQA;
 
-  int L = max(seq_lens[b], 0);
+  // Loads that do not depend on the sequence length are issued before its
+  // value arrives: for an INT2 chunk the page ids of its planned page range
+  // (clamped to the page table) and R_K and q for the rotation prologue.
+  const int L_in = seq_lens[b];
+  constexpr int TPB = 64 / C::SLOTS;  // tiles whose page ids one VGPR holds
+  constexpr int CG = D / 4, RS = kThreads / CG, RPS = D / RS;
+  const int cg = tid % CG, rs = tid / CG;
+  const bool int2_planned = !BF16_ONLY && u >= p.n_bf16_units;
+  const int c_int2 = u - p.n_bf16_units;
+  int pid_raw = -1;
+  float4 rr[RPS];
+  uint32_t qq[GQA][RPS / 2];
+  if (int2_planned) {
+    // lane i*SLOTS + s: slot s of this wave's i-th tile, wave + i*kWaves
+    const int i = lane / C::SLOTS, s = lane % C::SLOTS;
+    const int lp = c_int2 * p.pages_per_chunk + (wave + i * kWaves) * C::SLOTS + s;
+    const int pend = min((c_int2 + 1) * p.pages_per_chunk, p.int2_pt_stride);
+    if (lp < pend) pid_raw = int2_pt_all[(size_t)b * p.int2_pt_stride + lp];
+    // thread (rs, cg) owns rows [rs*RPS, rs*RPS + RPS) of R_K and output
+    // channels 4cg .. 4cg+3 of q' = q R_K
+    const float* rbase = r_k + (size_t)kvh * D * D + (size_t)(rs * RPS) * D + 4 * cg;
+#pragma unroll
+    for (int r = 0; r < RPS; ++r) rr[r] = *(const float4*)(rbase + (size_t)r * D);
+    const uint16_t* qb = qin + ((size_t)b * hq + kvh * GQA) * D + rs * RPS;
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) {
+      if constexpr (RPS == 8) {
+        const uint4 x = *(const uint4*)(qb + h * D);
+        qq[h][0] = x.x;
+        qq[h][1] = x.y;
+        qq[h][2] = x.z;
+        qq[h][3] = x.w;
+      } else {
+        static_assert(RPS == 2, "row split");
+        qq[h][0] = *(const uint32_t*)(qb + h * D);
+      }
+    }
+  }
+
+  int L = min(max(L_in, 0), p.max_len);
   L = min(L, kPage * p.bf16_pt_stride);
   if (!BF16_ONLY) L = min(L, p.sink + p.recent + kPage * p.int2_pt_stride);
   const int r0 = max(p.sink, L - p.recent);
@@ -561,128 +676,160 @@ __global__ void __launch_bounds__(kThreads)
 
   if (!BF16_ONLY && int2_unit) {
     // ---------------------------------------------------- INT2 chunk unit
+    constexpr int R = kRing;
     const int my_slot = (n < C::COLS) ? n / GQA : C::SLOTS;
+    const int chd = n % GQA;
     const int ntiles = (end - first + C::SLOTS - 1) / C::SLOTS;
-    const int32_t* __restrict__ ipt = int2_pt_all + (size_t)b * p.int2_pt_stride;
-    // prologue: q' = q R_K on the bf16 matrix cores (R_K = R_hi + R_lo, both
-    // bf16, so q' keeps ~2^-17 relative accuracy); wave w computes output
-    // channels [16w, 16w + 16) for the query heads (MFMA rows) of this KV
-    // head.  Its loads are issued before the first tiles' so that the
-    // prologue runs while those are in flight.
-    constexpr int KB = D / 32;
-    uint4 qa[KB];
-    float rv[KB][8];
-    const bool qwave = wave < D / 16;
-    if (qwave) {
-      const uint16_t* qrow = qin + ((size_t)b * hq + kvh * GQA + (n < GQA ? n : 0)) * D;
-      const float* rcol = r_k + (size_t)kvh * D * D + wave * 16 + n;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        qa[kb] = uint4{0u, 0u, 0u, 0u};
-        if (n < GQA) qa[kb] = *(const uint4*)(qrow + kb * 32 + j * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rv[kb][e] = rcol[(size_t)(kb * 32 + j * 8 + e) * D];
-      }
+    // tiles of this wave (at most TPB: the host bounds the chunk size)
+    const int nt_w = wave < ntiles ? min((ntiles - 1 - wave) / kWaves + 1, TPB) : 0;
+    const size_t page_bytes = (size_t)p.num_kv_heads * C::BLK2;
+    const uint8_t* __restrict__ hpool = int2_pool + (size_t)kvh * C::BLK2;
+    // physical page ids of this wave's tiles wave + i*kWaves: lane i*SLOTS + s
+    // holds slot s of tile i, -1 when absent or outside the history
+    int pids;
+    {
+      const int i = lane / C::SLOTS, s = lane % C::SLOTS;
+      const int lp = first + (wave + i * kWaves) * C::SLOTS + s;
+      const bool ok = i < nt_w && lp < end && pid_raw >= 0 && pid_raw < p.int2_num_pages;
+      pids = ok ? pid_raw : -1;
     }
-    // prefetch ring: tile wave + r*kWaves in slot r; tiles past the last one
-    // load nothing but are fully initialized, so the buffers stay in VGPRs
-    I2Tile<D, NG, GQA> ring[kRing];
-    auto ld = [&](I2Tile<D, NG, GQA>& t, int tl) {
-      i2_load<D, NG, GQA>(t, p, ipt, int2_pool, kvh, first + tl * C::SLOTS, tl < ntiles ? end : 0, hist_len, lane,
-                          my_slot);
+
+    // ring of tiles in flight: the first R-1 tiles are requested before the
+    // prologue computes q', so HBM is busy from the start
+    I2Tile<D, NG, GQA> ring[R];
+    auto fetch = [&](I2Tile<D, NG, GQA>& t, int i) {
+      // tiles past this wave's last one read no page (all ids -1)
+      i2_fetch<D, NG, GQA>(t, hpool, page_bytes, pids, i < nt_w ? i * C::SLOTS : -1,
+                           first + (wave + i * kWaves) * C::SLOTS, hist_len, my_slot, lane);
     };
 #pragma unroll
-    for (int r = 0; r < kRing - 1; ++r) ld(ring[r], wave + r * kWaves);
-    if (qwave) {
-      v4f c = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < R - 1; ++r) fetch(ring[r], r);
+
+    // ---- prologue: q' = q R_K (fp32), per-head int8 split, B operands
+    {
+      v4i* bqz = &sm.bq[0][0][0][0];
+      for (int x = tid; x < C::SLOTS * 2 * C::KW * 64; x += kThreads) bqz[x] = v4i{0, 0, 0, 0};
+    }
+    float qacc[GQA][4];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        uint32_t hi[4], lo[4];
+    for (int h = 0; h < GQA; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = rv[kb][2 * e], x1 = rv[kb][2 * e + 1];
-          hi[e] = pack_bf16x2(x0, x1);
-          lo[e] = pack_bf16x2(x0 - bf16_lo(hi[e]), x1 - bf16_hi(hi[e]));
+      for (int e = 0; e < 4; ++e) qacc[h][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) {
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) {
+        const float qv = (i & 1) ? bf16_hi(qq[h][i >> 1]) : bf16_lo(qq[h][i >> 1]);
+        qacc[h][0] = fmaf(qv, rr[i].x, qacc[h][0]);
+        qacc[h][1] = fmaf(qv, rr[i].y, qacc[h][1]);
+        qacc[h][2] = fmaf(qv, rr[i].z, qacc[h][2]);
+        qacc[h][3] = fmaf(qv, rr[i].w, qacc[h][3]);
+      }
+    }
+    // sum the row segments held by this wave (lanes with equal cg)
+    static_assert(CG == 16 || CG == 32, "one or two row segments per 32 lanes");
+#pragma unroll
+    for (int h = 0; h < GQA; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (CG == 16) qacc[h][e] = xor16_add(qacc[h][e]);
+        qacc[h][e] = xor32_add(qacc[h][e]);
+      }
+    if (lane < CG) {
+#pragma unroll
+      for (int h = 0; h < GQA; ++h)
+        *(float4*)&sm.u.qpart[wave][h][4 * cg] = float4{qacc[h][0], qacc[h][1], qacc[h][2], qacc[h][3]};
+    }
+    __syncthreads();
+    if (wave < GQA) {
+      // wave h finishes query head h: lane owns channels CPL*lane + e
+      const int h = wave;
+      constexpr int CPL = D / 64;
+      float x[CPL];
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v += sm.u.qpart[w][h][CPL * lane + e];
+        x[e] = v;
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+      amax = wave_max(amax);
+      const float sq = amax > 0.f ? amax / 127.f : 1.f;
+      const float inv_sq = 1.f / sq;
+      int sg = 0;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const int c = CPL * lane + e;
+        const float y = x[e] * inv_sq;
+        const float a = fminf(fmaxf(rintf(y), -127.f), 127.f);
+        const float bt = fminf(fmaxf(rintf((y - a) * 256.f), -127.f), 127.f);
+        sg += 256 * (int)a + (int)bt;
+        // byte of channel c inside the transposed 16-byte operand of lane
+        // group c%64/16 (the unpacked K codes hold channel 4*b + k at byte
+        // 4*k + b)
+        const int w = c / 64, jj = (c % 64) / 16, m = c % 16;
+        const int byte = 4 * (m % 4) + m / 4;
+#pragma unroll
+        for (int s = 0; s < C::SLOTS; ++s) {
+          const int l = 16 * jj + s * GQA + h;
+          ((int8_t*)&sm.bq[s][0][w][l])[byte] = (int8_t)a;
+          ((int8_t*)&sm.bq[s][1][w][l])[byte] = (int8_t)bt;
         }
-        const v8bf av = as_v8bf(qa[kb]);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_v8bf(uint4{hi[0], hi[1], hi[2], hi[3]}), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_v8bf(uint4{lo[0], lo[1], lo[2], lo[3]}), c, 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * j + i < GQA) sm.qr[(4 * j + i) * D + wave * 16 + n] = c[i];
-    }
-    __syncthreads();
-    float amax = 0.f;
-    for (int idx = tid; idx < GQA * D; idx += kThreads) amax = fmaxf(amax, fabsf(sm.qr[idx]));
-    amax = wave_max(amax);
-    if (lane == 0) sm.wred[wave] = amax;
-    __syncthreads();
-    amax = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, sm.wred[w]);
-    const float sq = amax > 0.f ? amax / 127.f : 1.f;
-    const float inv_sq = 1.f / sq;
-    for (int idx = tid; idx < GQA * D; idx += kThreads) {
-      const float x = sm.qr[idx] * inv_sq;
-      const float a = fminf(fmaxf(rintf(x), -127.f), 127.f);
-      const float bt = fminf(fmaxf(rintf((x - a) * 256.f), -127.f), 127.f);
-      sm.ta[idx] = (int8_t)a;
-      sm.tb[idx] = (int8_t)bt;
-    }
-    __syncthreads();
-    for (int pair = wave; pair < GQA * NG; pair += kWaves) {
-      const int h = pair / NG, g = pair % NG;
-      int sacc = 0;
-      for (int c = lane; c < C::G; c += 64) {
-        const int idx = h * D + g * C::G + c;
-        sacc += 256 * (int)sm.ta[idx] + (int)sm.tb[idx];
+      if constexpr (NG == 1) {
+        sg = wave_sum_i(sg);
+        if (lane == 0) sm.sig[h] = sg;
+      } else {
+        // D = 128, G = 64: lanes 0-31 hold group 0, lanes 32-63 group 1
+        sg = half_sum_i(sg);
+        if ((lane & 31) == 0) sm.sig[h * NG + (lane >> 5)] = sg;
       }
-      sacc = wave_sum_i(sacc);
-      if (lane == 0) sm.sig[pair] = sacc;
-    }
-    // B operands: column n = (page slot, head), block-diagonal over slots;
-    // every wave needs the same per-lane values, wave 0 builds them
-    const int chd = n % GQA;
-    if (wave == 0) {
-#pragma unroll
-      for (int s = 0; s < C::SLOTS; ++s)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int w = 0; w < C::KW; ++w) {
-            uint32_t o4[4] = {0u, 0u, 0u, 0u};
-            if (my_slot == s) {
-              const int8_t* src = (tt == 0 ? sm.ta : sm.tb) + chd * D + w * 64 + j * 16;
-              const uint4 x = *(const uint4*)src;
-              const uint32_t in4[4] = {x.x, x.y, x.z, x.w};
-              transpose4x4(in4, o4);
-            }
-            sm.bq[s][tt][w][lane] = v4i{(int)o4[0], (int)o4[1], (int)o4[2], (int)o4[3]};
-          }
+      if (lane == 0) sm.kap[h] = p.sm_log2 * sq * (1.f / 256.f);
     }
     __syncthreads();
+    const float kappa = sm.kap[chd];
     float sig[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) sig[g] = (float)sm.sig[chd * NG + g];
-    const float kappa = p.sm_log2 * sq * (1.f / 256.f);
     // fp16 exponent patterns of the P.V operands, held in VGPRs so that each
     // operand is one and-or (bitop3) of a shifted code word
     uint32_t exp_lo = kExpLo, exp_hi = kExpHi;
     asm volatile("" : "+v"(exp_lo), "+v"(exp_hi));
 
+    v4i bqr[C::SLOTS][2][C::KW];
+#pragma unroll
+    for (int s = 0; s < C::SLOTS; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int w = 0; w < C::KW; ++w) bqr[s][t][w] = sm.bq[s][t][w][lane];
+
     Acc<D, NG> st;
     st.init();
-    int tile = wave;
-    while (true) {
+    if (nt_w > 0) {
+      I2Scores<NG> S = i2_scores<D, NG, GQA>(ring[0], bqr);
+      int i = 0;
+      while (true) {
 #pragma unroll
-      for (int r = 0; r < kRing; ++r) {
-        if (tile >= ntiles) break;
-        ld(ring[(r + kRing - 1) % kRing], tile + (kRing - 1) * kWaves);
-        i2_compute<D, NG, GQA>(ring[r], st, sm.bq, kappa, sig, my_slot, lane, exp_lo, exp_hi);
-        tile += kWaves;
+        for (int r = 0; r < R; ++r) {
+          if (i >= nt_w) break;
+          fetch(ring[(r + R - 1) % R], i + R - 1);
+          // softmax of tile i first: the wait for tile i+1's data comes
+          // after it, next to the MFMAs that need that data
+          const I2Weights<D, NG, GQA> W = i2_softmax<D, NG, GQA>(ring[r], S, st, kappa, sig, my_slot);
+          S = i2_scores<D, NG, GQA>(ring[(r + 1) % R], bqr);
+          i2_pv<D, NG, GQA>(ring[r], W, st, exp_lo, exp_hi);
+          // slots r and r+1 hold arrived data (the loads of r+2 .. r+R-1 may
+          // still be in flight and are left alone)
+          ring[r].pin();
+          ring[(r + 1) % R].pin();
+          ++i;
+        }
+        if (i >= nt_w) break;
       }
-      if (tile >= ntiles) break;
     }
     wave_finish<D, NG, GQA, true>(st, sm, wave, lane);
   } else {
@@ -753,7 +900,7 @@ __global__ void __launch_bounds__(kThreads)
         so += e * sm.u.part[w][h][c];
       }
       o = so / sw;
-      lse = (mx + __log2f(sw)) * kLn2;
+      lse = mx + __log2f(sw);  // log2 units
     }
     p.part_o[(pidx + h) * D + c] = o;
     if (c == 0) p.part_lse[pidx + h] = lse;
@@ -774,37 +921,43 @@ __global__ void __launch_bounds__(kThreads)
   __syncthreads();
   if (!sm.last) return;
   const size_t p0 = head_base * U * GQA;
-  // weights exp(lse_u - M_h) / sum_u exp(lse_u - M_h), in sm.u.wts[u * GQA + h]
-  for (int h = wave; h < GQA; h += kWaves) {
-    float mx = -INFINITY;
-    for (int uu = lane; uu < total; uu += 64) mx = fmaxf(mx, p.part_lse[p0 + (size_t)uu * GQA + h]);
-    mx = wave_max(mx);
-    float sw = 0.f;
-    for (int uu = lane; uu < total; uu += 64) {
-      const float e = (mx > -INFINITY) ? expf(p.part_lse[p0 + (size_t)uu * GQA + h] - mx) : 0.f;
-      sm.u.wts[uu * GQA + h] = e;
-      sw += e;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sw += __shfl_xor(sw, o);
-    const float inv = sw > 0.f ? 1.f / sw : 0.f;
-    for (int uu = lane; uu < total; uu += 64) sm.u.wts[uu * GQA + h] *= inv;
-  }
-  __syncthreads();
+  // thread (h, c) folds the partials of head h in batches of 32, loading a
+  // batch's lse and o values together (one memory round trip per batch)
   for (int idx = tid; idx < GQA * D; idx += kThreads) {
     const int h = idx / D, c = idx % D;
-    const float* src = p.part_o + (p0 + h) * D + c;  // partial u at src[u * GQA * D]
-    float acc = 0.f;
-    int uu = 0;
-    for (; uu + 16 <= total; uu += 16) {  // 16 independent loads in flight
-      float v[16];
+    const float* lsrc = p.part_lse + p0 + h;        // partial u at lsrc[u * GQA]
+    const float* osrc = p.part_o + (p0 + h) * D + c;  // partial u at osrc[u * GQA * D]
+    float M = -INFINITY, S = 0.f, A = 0.f;
+    for (int u0 = 0; u0 < total; u0 += 32) {
+      float e[32], v[32];
+      // indices past the last partial re-read the last one (in bounds, no
+      // branches) and are then given weight zero
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = src[(size_t)(uu + k) * GQA * D];
+      for (int k = 0; k < 32; ++k) {
+        const int uu = min(u0 + k, total - 1);
+        e[k] = lsrc[(size_t)uu * GQA];
+        v[k] = osrc[(size_t)uu * GQA * D];
+      }
 #pragma unroll
-      for (int k = 0; k < 16; ++k) acc += sm.u.wts[(uu + k) * GQA + h] * v[k];
+      for (int k = 0; k < 32; ++k)
+        if (u0 + k >= total) e[k] = -INFINITY;
+      float mb = M;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) mb = fmaxf(mb, e[k]);
+      if (mb > -INFINITY) {
+        const float f = __builtin_amdgcn_exp2f(M - mb);  // 0 while M = -inf
+        S *= f;
+        A *= f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const float w = __builtin_amdgcn_exp2f(e[k] - mb);
+          S += w;
+          A = fmaf(w, v[k], A);
+        }
+        M = mb;
+      }
     }
-    for (; uu < total; ++uu) acc += sm.u.wts[uu * GQA + h] * src[(size_t)uu * GQA * D];
-    p.out[((size_t)b * hq + kvh * GQA + h) * D + c] = (uint16_t)f32_to_bf16(acc);
+    p.out[((size_t)b * hq + kvh * GQA + h) * D + c] = (uint16_t)f32_to_bf16(S > 0.f ? A / S : 0.f);
   }
   if (tid == 0) __hip_atomic_store(p.counters + head_base, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -16,11 +16,12 @@ struct DecodeParams {
   const float* r_k;          // [Hkv][D][D]
   uint16_t* out;             // [B][Hq][D] bf16
   uint32_t* counters;        // [B][Hkv]
-  float* part_lse;           // [B][Hkv][U][GQA] natural log
+  float* part_lse;           // [B][Hkv][U][GQA] log2 of the partial's softmax sum
   float* part_o;             // [B][Hkv][U][GQA][D]
   int32_t bf16_pt_stride, bf16_num_pages;
   int32_t int2_pt_stride, int2_num_pages;
   int32_t batch, num_kv_heads, sink, recent;
+  int32_t max_len;           // lengths above it are clamped to it
   int32_t n_bf16_units;      // BF16 (sink + recent) units per (sequence, KV head)
   int32_t bf16_pages_per_unit;
   int32_t max_chunks;        // INT2 (or, BF16-only, BF16) chunks per (sequence, KV head)

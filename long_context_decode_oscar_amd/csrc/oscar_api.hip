@@ -65,8 +65,10 @@ int env_int(const char* name, int dflt) {
 }
 
 constexpr int kMaxChunks = 1024;
+constexpr int kDecodeWaves = 8;  // waves per decode workgroup (decode.hip)
 
 struct Plan {
+  bool fits;  // false: the history needs more than kMaxChunks chunks
   int n_bf16_units, bf16_pages_per_unit, max_chunks, pages_per_chunk, units, grid;
   size_t off_counters, off_lse, off_o, bytes;
 };
@@ -81,6 +83,7 @@ int slots_for(int gqa) { return (16 / gqa) < 4 ? 16 / gqa : 4; }
 Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
   const oscar_config& c = pool->cfg;
   Plan pl{};
+  pl.fits = true;
   const int hkv = c.num_kv_heads;
   const int target = env_int("OSCAR_TARGET_WGS", num_cus());
   const int slots = slots_for(pool->gqa);
@@ -98,7 +101,7 @@ Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
     if (pl.max_chunks < 1) pl.max_chunks = 1;
   } else {
     const int list_max = c.sink_tokens / 16 + (c.recent_tokens + 15) / 16 + 1;
-    const int per_unit = env_int("OSCAR_BF16_PAGES_PER_UNIT", 16);
+    const int per_unit = env_int("OSCAR_BF16_PAGES_PER_UNIT", 32);
     pl.n_bf16_units = (list_max + per_unit - 1) / per_unit;
     pl.bf16_pages_per_unit = (list_max + pl.n_bf16_units - 1) / pl.n_bf16_units;
     const int r0 = max_len - c.recent_tokens > c.sink_tokens ? max_len - c.recent_tokens : c.sink_tokens;
@@ -110,15 +113,16 @@ Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
     int ppc = (hist_pages + want - 1) / want;
     ppc = ((ppc + slots - 1) / slots) * slots;
     if (ppc < slots) ppc = slots;
+    // a wave holds the page ids of its (at most 64 / slots) tiles in one
+    // VGPR: at most 64 * kDecodeWaves pages per chunk
+    if (ppc > 64 * kDecodeWaves) ppc = 64 * kDecodeWaves;
     pl.pages_per_chunk = ppc;
     pl.max_chunks = (hist_pages + ppc - 1) / ppc;
   }
-  // the last workgroup keeps one merge weight per (unit, query head) in an
-  // LDS table of 8 * (D + 1) entries per head; the last chunk absorbs any
-  // remainder
-  int cap = 8 * (c.head_dim + 1) - pl.n_bf16_units;
-  if (cap > kMaxChunks) cap = kMaxChunks;
-  if (pl.max_chunks > cap) pl.max_chunks = cap;
+  if (pl.max_chunks > kMaxChunks) {
+    pl.fits = false;
+    pl.max_chunks = kMaxChunks;
+  }
   pl.units = pl.n_bf16_units + pl.max_chunks;
   if (pl.units < 1) pl.units = 1;
   pl.grid = batch * hkv * pl.units;
@@ -190,7 +194,13 @@ oscar_status oscar_decode_workspace_bytes(const oscar_pool* pool, int32_t batch,
                                           int32_t bf16_only, size_t* bytes) {
   if (!pool || !bytes) return fail(OSCAR_ERR_INVALID, "pool and bytes must be non-null");
   if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID, "negative batch or max_seq_len");
-  *bytes = batch == 0 ? 0 : make_plan(pool, batch, max_seq_len, bf16_only != 0).bytes;
+  if (batch == 0) {
+    *bytes = 0;
+    return ok();
+  }
+  const Plan pl = make_plan(pool, batch, max_seq_len, bf16_only != 0);
+  if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
+  *bytes = pl.bytes;
   return ok();
 }
 
@@ -222,6 +232,7 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
                                  int2_num_pages, true);
   if (st != OSCAR_OK) return st;
   const Plan pl = make_plan(pool, batch, max_seq_len, false);
+  if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes)
     return fail(OSCAR_ERR_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes", pl.bytes);
   const oscar_config& c = pool->cfg;
@@ -245,6 +256,7 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
   p.num_kv_heads = c.num_kv_heads;
   p.sink = c.sink_tokens;
   p.recent = c.recent_tokens;
+  p.max_len = max_seq_len;
   p.n_bf16_units = pl.n_bf16_units;
   p.bf16_pages_per_unit = pl.bf16_pages_per_unit;
   p.max_chunks = pl.max_chunks;
@@ -270,6 +282,7 @@ oscar_status oscar_bf16_decode_attention(const oscar_pool* pool, int32_t batch, 
   oscar_status st = check_tables(bf16_page_table, bf16_pt_stride, bf16_num_pages, nullptr, 0, 0, false);
   if (st != OSCAR_OK) return st;
   const Plan pl = make_plan(pool, batch, max_seq_len, true);
+  if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes)
     return fail(OSCAR_ERR_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes", pl.bytes);
   const oscar_config& c = pool->cfg;
@@ -289,6 +302,7 @@ oscar_status oscar_bf16_decode_attention(const oscar_pool* pool, int32_t batch, 
   p.num_kv_heads = c.num_kv_heads;
   p.sink = c.sink_tokens;
   p.recent = c.recent_tokens;
+  p.max_len = max_seq_len;
   p.n_bf16_units = 0;
   p.max_chunks = pl.max_chunks;
   p.pages_per_chunk = pl.pages_per_chunk;
