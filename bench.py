@@ -53,6 +53,8 @@ def parse():
                     help="only run N eager decode steps over the cold pool copies, then one plain copy of "
                          "--probe-bytes (for rocprofv3 counters); prints no JSON")
     ap.add_argument("--probe-bytes", type=int, default=256 * 2**20)
+    ap.add_argument("--only", default="all", choices=["all", "headline", "bulk", "demote", "mixed"],
+                    help="run one section only (the JSON line then holds what was measured)")
     return ap.parse_args()
 
 
@@ -278,6 +280,42 @@ def cpu_baseline(wl, inp, repeats=3):
                       f"({dt:.2f} s); host has {os.cpu_count()} logical CPUs"}
 
 
+def bench_bulk_quant(oscar, steps=10, warmup=3, repeats=5):
+    """Write-path bulk quantization: K, V of 131,072 tokens x 8 KV heads x 128
+    (bf16) rotated (K), clipped, quantized and packed into 8,192 pages per
+    head, one oscar_quantize_pack launch per step.  Algorithmic bytes: the
+    bf16 K and V read once plus the packed pages written once."""
+    import numpy as np
+    import torch
+    from synthetic import CONFIGS, draw_inputs
+    wl = CONFIGS["bulk-quant-t131k"]
+    inp = draw_inputs(wl, with_q=False, device="cuda")
+    k, v = inp.k[0].contiguous(), inp.v[0].contiguous()
+    t = k.shape[0]
+    c = inp.calib
+    r_k, tau_k, tau_v = (torch.as_tensor(x).cuda() for x in (c.r_k, c.tau_k, c.tau_v))
+    pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
+                                            wl.sink, wl.recent, 1, 0.0))
+    npg = (t + 15) // 16
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 500))
+    ids = torch.from_numpy(rng.permutation(npg).astype(np.int32)).cuda()
+    int2 = torch.empty((npg, pool.int2_page_bytes), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        oscar.oscar_quantize_pack(pool, k, v, ids, int2, r_k, tau_k, tau_v)
+
+    ms, ms_min = time_steps(step, steps, warmup, repeats, use_graph=True)
+    nbytes = k.numel() * 2 + v.numel() * 2 + npg * pool.int2_page_bytes
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"bulk quantize ({t} tokens x {wl.num_kv_heads} heads): {ms * 1e3:.2f} us/launch, {gbps:.1f} GB/s")
+    del k, v, int2, inp
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "tokens": t, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+            "us_per_launch": round(ms * 1e3, 3), "us_min": round(ms_min * 1e3, 3), "bytes_per_launch": nbytes,
+            "GBps": round(gbps, 2), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            "kernel": "k_quantize_pack (bf16-MFMA key rotation + clip + quantize + pack)"}
+
+
 def copy_probe(nbytes):
     """One plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -302,6 +340,9 @@ def main():
     from synthetic import CONFIGS, draw_inputs
 
     oscar.load()
+    if args.only == "bulk":
+        print(json.dumps({"bulk_quantize": bench_bulk_quant(oscar)}), flush=True)
+        return
     wl = CONFIGS[args.workload]
     kv = wl.kv_bytes()
     log(f"workload {wl.name}: KV bytes/step {kv['total']:,} (INT2 {kv['int2']:,}, BF16 {kv['bf16']:,})")

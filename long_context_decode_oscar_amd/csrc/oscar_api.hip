@@ -387,8 +387,14 @@ oscar_status oscar_quantize_pack(const oscar_pool* pool, int32_t num_tokens, con
   p.num_tokens = num_tokens;
   p.int2_pool = (uint8_t*)int2_pool;
   p.int2_num_pages = int2_num_pages;
-  p.pages_per_block = env_int("OSCAR_QP_PAGES_PER_BLOCK", 32);
-  if (p.pages_per_block < 4) p.pages_per_block = 4;
+  {
+    // one 8-wave workgroup per compute unit (its LDS holds R_K twice), the
+    // pages of each KV head split evenly over the workgroups given to it
+    const int npages = (num_tokens + 15) / 16;
+    const int per_head = std::max(1, num_cus() / std::max(1, c.num_kv_heads));
+    p.pages_per_block = env_int("OSCAR_QP_PAGES_PER_BLOCK", (npages + per_head - 1) / per_head);
+    if (p.pages_per_block < 8) p.pages_per_block = 8;
+  }
   p.r_k = r_k;
   p.tau_k = tau_k;
   p.tau_v = tau_v;

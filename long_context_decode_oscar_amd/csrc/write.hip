@@ -176,17 +176,53 @@ __global__ void __launch_bounds__(256) k_append_demote(const WriteParams p) {
 }
 
 // ----------------------------------------------------------- bulk quantize --
+// One workgroup per (compute unit, KV head slice) converts R_K once and then
+// streams pages; each wave owns one page at a time and its own LDS area, so
+// the page loop needs no workgroup barrier.  The next page's K and V are
+// loaded while the current one is rotated and quantized.
+constexpr int kQpWaves = 8;
+constexpr int kQpThreads = 64 * kQpWaves;
+
 template <int D, int NG>
 struct BulkSmem {
   uint4 rb[2][D / 16][D / 32][64];  // R_hi / R_lo as MFMA B operands
-  float y[4][kPage][D + 4];         // per-wave rotated K tile
-  uint8_t code[4][2][kPage][D];     // per-wave K / V codes
+  // per wave: the rotated K tile, whose space then holds the K / V codes
+  union PerWave {
+    float y[kPage][D + 4];
+    uint8_t code[2][kPage][D];
+  } w[kQpWaves];
 };
 
-// quantize one token's channels held by 4 lanes (lane = 4 t + qq): this lane
-// holds channels w*64 + qq*16 + m (w < D/64, m < 16) in vals[w][m]
+// min / max over the 4 lanes of a quad (lanes 4t .. 4t+3)
+__device__ __forceinline__ float quad_min(float x) {
+  x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  return fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+}
+
+// c / s for a bf16 divisor s, given y = 1/s (correctly rounded): the
+// product c*y corrected once by its fma residual (Markstein).  For every fp32
+// significand of c and every bf16 significand of s this equals the IEEE
+// quotient; away from underflow and overflow the exponents only scale it.
+__device__ __forceinline__ float div_bf16(float c, float s, float y) {
+  const float q0 = c * y;
+  const float r = __builtin_fmaf(-s, q0, c);
+  return __builtin_fmaf(r, y, q0);
+}
+// the code of quotient q with zero point z into byte e of word
+__device__ __forceinline__ uint32_t code_into(uint32_t word, float q, float z, int e) {
+  const float t = rintf(__fadd_rn(q, z));
+  return __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(t, 0.f, 3.f), e, word);
+}
+
+// Quantizes one token's channels held by the 4 lanes of a quad (lane = 4t +
+// qq): this lane holds channels w*64 + qq*16 + m (w < D/64, m < 16) in
+// vals[w][m].  Codes come back one byte each, 16 per word group w.
 template <int D, int NG>
-__device__ __forceinline__ void quant_lane(float (&vals)[D / 64][16], float tau, uint8_t* code_row, int qq,
+__device__ __forceinline__ void quant_lane(float (&vals)[D / 64][16], float tau, uint32_t (&codes)[D / 64][4],
                                            uint32_t (&szw)[NG]) {
   constexpr int KW = D / 64;
   float mn[KW], mx[KW];
@@ -196,15 +232,13 @@ __device__ __forceinline__ void quant_lane(float (&vals)[D / 64][16], float tau,
     mx[w] = -INFINITY;
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
-      const float x = fminf(fmaxf(vals[w][m], -tau), tau);
+      const float x = __builtin_amdgcn_fmed3f(vals[w][m], -tau, tau);
       vals[w][m] = x;
       mn[w] = fminf(mn[w], x);
       mx[w] = fmaxf(mx[w], x);
     }
-    mn[w] = fminf(mn[w], __shfl_xor(mn[w], 1));
-    mn[w] = fminf(mn[w], __shfl_xor(mn[w], 2));
-    mx[w] = fmaxf(mx[w], __shfl_xor(mx[w], 1));
-    mx[w] = fmaxf(mx[w], __shfl_xor(mx[w], 2));
+    mn[w] = quad_min(mn[w]);
+    mx[w] = quad_max(mx[w]);
   }
   // words of one group: NG == 1 -> all words; NG == 2 (D = 128) -> word w
 #pragma unroll
@@ -220,146 +254,230 @@ __device__ __forceinline__ void quant_lane(float (&vals)[D / 64][16], float tau,
     float s, z;
     scale_zero(gmn, gmx, sb, zb, s, z);
     szw[g] = sb | (zb << 16);
+    // Away from the ends of the fp32 range the quotient comes from the
+    // reciprocal with one Markstein correction (exact: see div_bf16); the
+    // rest of the groups take the IEEE division.
+    const bool fast = s >= 0x1p-70f && fmaxf(fabsf(gmn), fabsf(gmx)) <= 0x1p56f;
+    const float y = 1.0f / s;
 #pragma unroll
     for (int w = 0; w < KW; ++w)
       if (NG == 1 || w == g) {
+        if (fast) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m) code_row[w * 64 + qq * 16 + m] = (uint8_t)quant_code(vals[w][m], s, z);
+          for (int q = 0; q < 4; ++q) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) word = code_into(word, div_bf16(vals[w][4 * q + e], s, y), z, e);
+            codes[w][q] = word;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) word = code_into(word, vals[w][4 * q + e] / s, z, e);
+            codes[w][q] = word;
+          }
+        }
       }
   }
 }
 
+// 16 one-byte codes (4 per word, values 0..3) -> one 32-bit word, code m at
+// bits 2m
+__device__ __forceinline__ uint32_t pack16(uint4 b) {
+  auto one = [](uint32_t u) {  // 4 codes -> 8 bits
+    const uint32_t t = u | (u >> 6);              // bits 0-3: codes 0,1; bits 16-19: codes 2,3
+    return (t & 0xFu) | ((t >> 12) & 0xF0u);
+  };
+  return one(b.x) | (one(b.y) << 8) | (one(b.z) << 16) | (one(b.w) << 24);
+}
+
 template <int D, int NG>
-__global__ void __launch_bounds__(256) k_quantize_pack(const WriteParams p) {
+struct BulkPage {  // one page's global inputs, as loaded
+  uint4 ka[D / 32];          // K tile as MFMA A operands: token r, channels j*D/4 + ks*8 + e
+  uint4 va[D / 64][2];       // V of token t, channels w*64 + qq*16 + 0..15
+  int id;                    // physical page (-1: none)
+};
+
+template <int D, int NG>
+__device__ __forceinline__ void bulk_load(BulkPage<D, NG>& pg, const WriteParams& p, int kvh, int page, int pg_end,
+                                          int lane) {
+  constexpr int KB = D / 32, KW = D / 64;
+  const int id = page < pg_end ? p.page_ids[page] : -1;
+  pg.id = (id >= 0 && id < p.int2_num_pages) ? id : -1;
+  const int j = lane >> 4, r = lane & 15, t = lane >> 2, qq = lane & 3;
+  const int tok0 = page * kPage;
+  {
+    const bool ok = pg.id >= 0 && tok0 + r < p.num_tokens;
+    const uint4* src = (const uint4*)(p.k + ((size_t)(ok ? tok0 + r : 0) * p.num_kv_heads + kvh) * D + j * (D / 4));
+#pragma unroll
+    for (int ks = 0; ks < KB; ++ks) pg.ka[ks] = ok ? src[ks] : uint4{0u, 0u, 0u, 0u};
+  }
+  {
+    const bool ok = pg.id >= 0 && tok0 + t < p.num_tokens;
+    const uint16_t* src = p.v + ((size_t)(ok ? tok0 + t : 0) * p.num_kv_heads + kvh) * D;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+      pg.va[w][0] = ok ? *(const uint4*)(src + w * 64 + qq * 16) : uint4{0u, 0u, 0u, 0u};
+      pg.va[w][1] = ok ? *(const uint4*)(src + w * 64 + qq * 16 + 8) : uint4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int D, int NG>
+__device__ __forceinline__ void bulk_page(const BulkPage<D, NG>& pg, const WriteParams& p, BulkSmem<D, NG>& sm,
+                                          int kvh, int page, int wave, int lane, float tau_k, float tau_v) {
   constexpr int KW = D / 64, KB = D / 32, OT = D / 16;
   constexpr int BLK2 = 8 * D + 128 * NG;
   constexpr int REC = D / 8;
+  const int j = lane >> 4, r = lane & 15, t = lane >> 2, qq = lane & 3;
+  const int tok0 = page * kPage;
+  auto& pw = sm.w[wave];
+  // ---- Y = K R_K on the bf16 matrix cores (R split hi + lo)
+#pragma unroll
+  for (int ot = 0; ot < OT; ++ot) {
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KB; ++ks) {
+      const v8bf a = __builtin_bit_cast(v8bf, pg.ka[ks]);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, sm.rb[0][ot][ks][lane]), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, sm.rb[1][ot][ks][lane]), c, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw.y[4 * j + i][ot * 16 + r] = c[i];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ---- quantize K (lane = 4t + qq) and V
+  const bool tok_ok = pg.id >= 0 && tok0 + t < p.num_tokens;
+  uint32_t kc[KW][4], vc[KW][4], szk[NG], szv[NG];
+  {
+    float vals[KW][16];
+#pragma unroll
+    for (int w = 0; w < KW; ++w)
+#pragma unroll
+      for (int m = 0; m < 16; m += 4) {
+        const float4 x = *(const float4*)&pw.y[t][w * 64 + qq * 16 + m];
+        vals[w][m] = x.x;
+        vals[w][m + 1] = x.y;
+        vals[w][m + 2] = x.z;
+        vals[w][m + 3] = x.w;
+      }
+    quant_lane<D, NG>(vals, tau_k, kc, szk);
+  }
+  {
+    float vals[KW][16];
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+      const uint32_t xs[8] = {pg.va[w][0].x, pg.va[w][0].y, pg.va[w][0].z, pg.va[w][0].w,
+                              pg.va[w][1].x, pg.va[w][1].y, pg.va[w][1].z, pg.va[w][1].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        vals[w][2 * q] = bf16_lo(xs[q]);
+        vals[w][2 * q + 1] = bf16_hi(xs[q]);
+      }
+    }
+    quant_lane<D, NG>(vals, tau_v, vc, szv);
+  }
+  // codes of tokens past the last one are zero
+#pragma unroll
+  for (int w = 0; w < KW; ++w)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      kc[w][q] = tok_ok ? kc[w][q] : 0u;
+      vc[w][q] = tok_ok ? vc[w][q] : 0u;
+    }
+  uint8_t* blk = p.int2_pool + ((size_t)max(pg.id, 0) * p.num_kv_heads + kvh) * BLK2;
+  // scales of token t (zeros for slots past the last token)
+  if (pg.id >= 0 && qq < NG) {
+    const int g = qq;
+    uint32_t* sc = (uint32_t*)(blk + 8 * D + (t / 4) * 32 * NG);
+    sc[(t % 4) * NG + g] = tok_ok ? szk[g] : 0u;
+    sc[4 * NG + (t % 4) * NG + g] = tok_ok ? szv[g] : 0u;
+  }
+  // the codes overwrite the rotated tile: every lane of the wave has read it
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int w = 0; w < KW; ++w) {
+    *(uint4*)&pw.code[0][t][w * 64 + qq * 16] = uint4{kc[w][0], kc[w][1], kc[w][2], kc[w][3]};
+    *(uint4*)&pw.code[1][t][w * 64 + qq * 16] = uint4{vc[w][0], vc[w][1], vc[w][2], vc[w][3]};
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ---- this lane's code record (j, r)
+  uint32_t kwd[KW], vwd[KW];
+#pragma unroll
+  for (int w = 0; w < KW; ++w) {
+    kwd[w] = pack16(*(const uint4*)&pw.code[0][r][w * 64 + j * 16]);
+    uint32_t vword = 0;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vword |= (uint32_t)pw.code[1][4 * j + i][(4 * w + bb) * 16 + r] << (16 * (i & 1) + 2 * (2 * bb + (i >> 1)));
+    vwd[w] = vword;
+  }
+  if (pg.id >= 0) {
+    if constexpr (D == 128) {
+      *(uint4*)(blk + lane * REC) = uint4{kwd[0], kwd[1], vwd[0], vwd[1]};
+    } else {
+      *(uint2*)(blk + lane * REC) = uint2{kwd[0], vwd[0]};
+    }
+  }
+  // the next page's tile reuses this wave's LDS
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int NG>
+__global__ void __launch_bounds__(kQpThreads) k_quantize_pack(const WriteParams p) {
+  constexpr int KB = D / 32, OT = D / 16;
   __shared__ BulkSmem<D, NG> sm;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int kvh = blockIdx.y;
   const int npages = (p.num_tokens + kPage - 1) / kPage;
   const int pg0 = blockIdx.x * p.pages_per_block;
   if (pg0 >= npages) return;
-
+  const int pg_end = min(pg0 + p.pages_per_block, npages);
+  BulkPage<D, NG> cur;
+  bulk_load<D, NG>(cur, p, kvh, pg0 + wave, pg_end, lane);  // first page's loads overlap the R_K split
   // R_K (fp32) -> R_hi + R_lo (bf16) in B-operand order:
   // rb[hl][ot][ks][lane (j, n)] element e = R[j*D/4 + ks*8 + e][ot*16 + n]
   {
-    const float* r = p.r_k + (size_t)kvh * D * D;
-    uint16_t* rb = (uint16_t*)sm.rb;
-    for (int idx = tid; idx < D * D; idx += 256) {
-      const int in = idx / D, out = idx % D;
-      const float x = r[idx];
-      const uint32_t hi = f32_to_bf16(x);
-      const uint32_t lo = f32_to_bf16(x - bf16_to_f32(hi));
-      const int j = in / (D / 4), ks = (in % (D / 4)) / 8, e = in % 8;
-      const int ot = out / 16, n = out % 16;
-      const int off = ((ot * KB + ks) * 64 + (j * 16 + n)) * 8 + e;
-      rb[off] = (uint16_t)hi;
-      rb[(OT * KB * 64 * 8) + off] = (uint16_t)lo;
+    const float* rk = p.r_k + (size_t)kvh * D * D;
+    for (int idx = tid; idx < D * D / 8; idx += kQpThreads) {
+      // eight consecutive input rows of one output column: one operand lane
+      const int lane_op = idx % 64, ks = (idx / 64) % KB, ot = idx / (64 * KB);
+      const int j = lane_op >> 4, n = lane_op & 15;
+      const int in0 = j * (D / 4) + ks * 8, out = ot * 16 + n;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = rk[(size_t)(in0 + 2 * e) * D + out], x1 = rk[(size_t)(in0 + 2 * e + 1) * D + out];
+        hi[e] = pack_bf16x2(x0, x1);
+        lo[e] = pack_bf16x2(x0 - bf16_lo(hi[e]), x1 - bf16_hi(hi[e]));
+      }
+      sm.rb[0][ot][ks][lane_op] = uint4{hi[0], hi[1], hi[2], hi[3]};
+      sm.rb[1][ot][ks][lane_op] = uint4{lo[0], lo[1], lo[2], lo[3]};
     }
   }
   __syncthreads();
   const float tau_k = p.tau_k[kvh], tau_v = p.tau_v[kvh];
-  const int j = lane >> 4, r = lane & 15;
-  const int t = lane >> 2, qq = lane & 3;  // quantization role
-  const int pg_end = min(pg0 + p.pages_per_block, npages);
-  // every wave runs the same number of iterations so that the workgroup
-  // barriers below are reached uniformly; a wave without a page idles
-  for (int pgb = pg0; pgb < pg_end; pgb += 4) {
-    const int pg = pgb + wave;
-    const int id = pg < pg_end ? p.page_ids[pg] : -1;
-    const bool active = id >= 0 && id < p.int2_num_pages;
-    const int tok0 = pg * kPage;
-    uint8_t* blk = p.int2_pool + ((size_t)(active ? id : 0) * p.num_kv_heads + kvh) * BLK2;
-    // ---- K tile as A operands: token r, channels j*D/4 + ks*8 + e
-    uint4 ka[KB];
-    {
-      const bool tv = active && tok0 + r < p.num_tokens;
-      const uint4* src = (const uint4*)(p.k + ((size_t)(tok0 + r) * p.num_kv_heads + kvh) * D + j * (D / 4));
-#pragma unroll
-      for (int ks = 0; ks < KB; ++ks) ka[ks] = tv ? src[ks] : uint4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int ot = 0; ot < OT; ++ot) {
-      v4f c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KB; ++ks) {
-        const v8bf a = __builtin_bit_cast(v8bf, ka[ks]);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, sm.rb[0][ot][ks][lane]), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, sm.rb[1][ot][ks][lane]), c, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.y[wave][4 * j + i][ot * 16 + r] = c[i];
-    }
-    __syncthreads();
-    // ---- quantize K (lane = 4 t + qq)
-    const bool tok_ok = active && tok0 + t < p.num_tokens;
-    uint32_t szk[NG], szv[NG];
-    {
-      float vals[KW][16];
-#pragma unroll
-      for (int w = 0; w < KW; ++w)
-#pragma unroll
-        for (int m = 0; m < 16; ++m) vals[w][m] = sm.y[wave][t][w * 64 + qq * 16 + m];
-      quant_lane<D, NG>(vals, tau_k, sm.code[wave][0][t], qq, szk);
-    }
-    // ---- quantize V (already rotated), loaded straight in the lane layout
-    {
-      float vals[KW][16];
-      const uint16_t* src = p.v + ((size_t)(tok0 + t) * p.num_kv_heads + kvh) * D;
-#pragma unroll
-      for (int w = 0; w < KW; ++w) {
-        uint4 x0 = uint4{0u, 0u, 0u, 0u}, x1 = x0;
-        if (tok_ok) {
-          x0 = *(const uint4*)(src + w * 64 + qq * 16);
-          x1 = *(const uint4*)(src + w * 64 + qq * 16 + 8);
-        }
-        const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          vals[w][2 * q] = bf16_lo(xs[q]);
-          vals[w][2 * q + 1] = bf16_hi(xs[q]);
-        }
-      }
-      quant_lane<D, NG>(vals, tau_v, sm.code[wave][1][t], qq, szv);
-    }
-    // scales of token t (zeros for slots past the last token)
-    if (active && qq < NG) {
-      const int g = qq;
-      const uint32_t k_sz = tok_ok ? szk[g] : 0u, v_sz = tok_ok ? szv[g] : 0u;
-      uint32_t* sc = (uint32_t*)(blk + 8 * D + (t / 4) * 32 * NG);
-      sc[(t % 4) * NG + g] = k_sz;
-      sc[4 * NG + (t % 4) * NG + g] = v_sz;
-    }
-    __syncthreads();
-    // ---- assemble this lane's code record (j, r)
-    uint32_t kwd[KW], vwd[KW];
-#pragma unroll
-    for (int w = 0; w < KW; ++w) {
-      const bool kval = tok0 + r < p.num_tokens;
-      uint32_t word = 0;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) word |= (uint32_t)sm.code[wave][0][r][w * 64 + j * 16 + m] << (2 * m);
-      kwd[w] = kval ? word : 0u;
-      uint32_t vword = 0;
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = tok0 + 4 * j + i < p.num_tokens;
-          const uint32_t cd = ok ? sm.code[wave][1][4 * j + i][(4 * w + bb) * 16 + r] : 0u;
-          vword |= cd << (16 * (i & 1) + 2 * (2 * bb + (i >> 1)));
-        }
-      vwd[w] = vword;
-    }
-    if (active) {
-      if constexpr (D == 128) {
-        *(uint4*)(blk + lane * REC) = uint4{kwd[0], kwd[1], vwd[0], vwd[1]};
-      } else {
-        *(uint2*)(blk + lane * REC) = uint2{kwd[0], vwd[0]};
-      }
-    }
-    __syncthreads();
+  // wave w handles pages pg0 + w, pg0 + w + kQpWaves, ...; two pages per trip
+  // so that the current and next page alternate between two register sets
+  BulkPage<D, NG> nxt;
+  for (int pg = pg0 + wave; pg < pg_end; pg += 2 * kQpWaves) {
+    bulk_load<D, NG>(nxt, p, kvh, pg + kQpWaves, pg_end, lane);
+    bulk_page<D, NG>(cur, p, sm, kvh, pg, wave, lane, tau_k, tau_v);
+    if (pg + kQpWaves >= pg_end) break;
+    bulk_load<D, NG>(cur, p, kvh, pg + 2 * kQpWaves, pg_end, lane);
+    bulk_page<D, NG>(nxt, p, sm, kvh, pg + kQpWaves, wave, lane, tau_k, tau_v);
   }
 }
 
@@ -392,7 +510,7 @@ void launch_qp(const WriteParams& p, hipStream_t s) {
   const int npages = (p.num_tokens + kPage - 1) / kPage;
   const int gx = (npages + p.pages_per_block - 1) / p.pages_per_block;
   if (gx == 0) return;
-  hipLaunchKernelGGL((k_quantize_pack<D, NG>), dim3(gx, p.num_kv_heads), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_quantize_pack<D, NG>), dim3(gx, p.num_kv_heads), dim3(kQpThreads), 0, s, p);
 }
 
 template <int D>

@@ -69,6 +69,24 @@ def test_quantize_pack_matches_oracle(gpu_lib, name, rotated):
                     f"{name} V head {h}")
 
 
+@pytest.mark.parametrize("ppb", [8, 20, 64])
+@pytest.mark.parametrize("name", ["d128-g64", "d64-g64"])
+def test_quantize_pack_page_split(gpu_lib, monkeypatch, name, ppb):
+    """Workgroups covering 8, 20 and 64 pages of a 63-page input: waves take
+    one to eight pages each and the last workgroup's range is ragged."""
+    monkeypatch.setenv("OSCAR_QP_PAGES_PER_BLOCK", str(ppb))
+    wl = WL[name]
+    inp = draw_inputs(wl, with_q=False)
+    k, v = inp.k[0][:1000].float().numpy(), inp.v[0][:1000].float().numpy()
+    c = inp.calib
+    kc, ks, kz, vc, vs, vz = _bulk(gpu_lib, wl, k, v, c.r_k, c.tau_k, c.tau_v, seed=ppb)
+    for h in range(wl.num_kv_heads):
+        check_write((kc[:, h], ks[:, h], kz[:, h]), k[:, h], c.r_k[h], c.tau_k[h], wl.group_size,
+                    f"{name} K head {h} pages/block={ppb}")
+        check_write((vc[:, h], vs[:, h], vz[:, h]), v[:, h], None, c.tau_v[h], wl.group_size,
+                    f"{name} V head {h} pages/block={ppb}")
+
+
 def test_quantize_pack_full_size_sampled(gpu_lib):
     """Bulk prefill of 131,072 tokens x 8 KV heads x 128 (the bulk workload);
     every page is read back and a sample of pages checked against the oracle."""
