@@ -280,7 +280,7 @@ def cpu_baseline(wl, inp, repeats=3):
                       f"({dt:.2f} s); host has {os.cpu_count()} logical CPUs"}
 
 
-def bench_bulk_quant(oscar, steps=10, warmup=3, repeats=5):
+def bench_bulk_quant(oscar, steps=10, warmup=3, repeats=5, profile_launches=0):
     """Write-path bulk quantization: K, V of 131,072 tokens x 8 KV heads x 128
     (bf16) rotated (K), clipped, quantized and packed into 8,192 pages per
     head, one oscar_quantize_pack launch per step.  Algorithmic bytes: the
@@ -304,6 +304,12 @@ def bench_bulk_quant(oscar, steps=10, warmup=3, repeats=5):
     def step(i):
         oscar.oscar_quantize_pack(pool, k, v, ids, int2, r_k, tau_k, tau_v)
 
+    if profile_launches:
+        for i in range(profile_launches):
+            step(i)
+        torch.cuda.synchronize()
+        log(f"profile run: {profile_launches} bulk quantize launches done")
+        return None
     ms, ms_min = time_steps(step, steps, warmup, repeats, use_graph=True)
     nbytes = k.numel() * 2 + v.numel() * 2 + npg * pool.int2_page_bytes
     gbps = nbytes / (ms * 1e-3) / 1e9
@@ -341,6 +347,10 @@ def main():
 
     oscar.load()
     if args.only == "bulk":
+        if args.profile_steps:
+            bench_bulk_quant(oscar, profile_launches=args.profile_steps)
+            copy_probe(args.probe_bytes)
+            return
         print(json.dumps({"bulk_quantize": bench_bulk_quant(oscar)}), flush=True)
         return
     wl = CONFIGS[args.workload]

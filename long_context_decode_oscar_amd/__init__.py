@@ -59,6 +59,9 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"liboscar.so not built at {path}; run python -m long_context_decode_oscar_amd.build")
+    # torch first: the library then binds to the HIP runtime torch already
+    # loaded, so torch's streams and device memory are valid in its calls
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I, S, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     lib.oscar_pool_create.argtypes = [ctypes.POINTER(CConfig), ctypes.POINTER(P), ctypes.POINTER(CLayout)]

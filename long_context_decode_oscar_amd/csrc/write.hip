@@ -176,21 +176,20 @@ __global__ void __launch_bounds__(256) k_append_demote(const WriteParams p) {
 }
 
 // ----------------------------------------------------------- bulk quantize --
-// One workgroup per (compute unit, KV head slice) converts R_K once and then
-// streams pages; each wave owns one page at a time and its own LDS area, so
-// the page loop needs no workgroup barrier.  The next page's K and V are
-// loaded while the current one is rotated and quantized.
-constexpr int kQpWaves = 8;
+// One workgroup per compute unit converts R_K once and then streams pages of
+// one KV head; each wave owns one page at a time and its own LDS area, so the
+// page loop needs no workgroup barrier.  The next page's K and V are loaded
+// while the current one is rotated and quantized.
+#ifndef OSCAR_QP_WAVES
+#define OSCAR_QP_WAVES 16
+#endif
+constexpr int kQpWaves = OSCAR_QP_WAVES;
 constexpr int kQpThreads = 64 * kQpWaves;
 
 template <int D, int NG>
 struct BulkSmem {
-  uint4 rb[2][D / 16][D / 32][64];  // R_hi / R_lo as MFMA B operands
-  // per wave: the rotated K tile, whose space then holds the K / V codes
-  union PerWave {
-    float y[kPage][D + 4];
-    uint8_t code[2][kPage][D];
-  } w[kQpWaves];
+  uint4 rb[2][D / 16][D / 32][64];  // R_hi / R_lo as MFMA A operands, output channels permuted
+  uint8_t vcode[kQpWaves][kPage][D];  // per wave: V codes, one byte each
 };
 
 // min / max over the 4 lanes of a quad (lanes 4t .. 4t+3)
@@ -201,6 +200,20 @@ __device__ __forceinline__ float quad_min(float x) {
 __device__ __forceinline__ float quad_max(float x) {
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
   return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+}
+// min / max over lanes n, n+16, n+32, n+48 (the gfx950 permlane swaps
+// exchange 16-lane rows 0<->1, 2<->3 and the two 32-lane halves)
+__device__ __forceinline__ float col4_min(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float col4_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // c / s for a bf16 divisor s, given y = 1/s (correctly rounded): the
@@ -218,110 +231,128 @@ __device__ __forceinline__ uint32_t code_into(uint32_t word, float q, float z, i
   return __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(t, 0.f, 3.f), e, word);
 }
 
-// Quantizes one token's channels held by the 4 lanes of a quad (lane = 4t +
-// qq): this lane holds channels w*64 + qq*16 + m (w < D/64, m < 16) in
-// vals[w][m].  Codes come back one byte each, 16 per word group w.
-template <int D, int NG>
-__device__ __forceinline__ void quant_lane(float (&vals)[D / 64][16], float tau, uint32_t (&codes)[D / 64][4],
-                                           uint32_t (&szw)[NG]) {
-  constexpr int KW = D / 64;
-  float mn[KW], mx[KW];
-#pragma unroll
-  for (int w = 0; w < KW; ++w) {
-    mn[w] = INFINITY;
-    mx[w] = -INFINITY;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float x = __builtin_amdgcn_fmed3f(vals[w][m], -tau, tau);
-      vals[w][m] = x;
-      mn[w] = fminf(mn[w], x);
-      mx[w] = fmaxf(mx[w], x);
-    }
-    mn[w] = quad_min(mn[w]);
-    mx[w] = quad_max(mx[w]);
+// scale_zero with fewer IEEE divisions, bit for bit the same result, plus
+// y = 1/s correctly rounded: d/3 and -mn/s by div_bf16 (3 is a bf16
+// significand times 2), and 1/s from v_rcp_f32 with one fma correction, which
+// for every bf16 significand of s turns any start within 2 ulp of 1/s into the
+// correctly rounded reciprocal.  Operands near the ends of the range, and a
+// zero minimum (whose quotient must keep its sign), take the IEEE division.
+__device__ __forceinline__ void scale_zero_recip(float mn, float mx, uint32_t& s_bits, uint32_t& z_bits, float& s,
+                                                 float& z, float& y) {
+  const float d = mx - mn;
+  float d3;
+  if (d >= 0x1p-100f && d <= 0x1p100f)
+    d3 = div_bf16(d, 3.0f, 0x1.555556p-2f);  // RN(1/3)
+  else
+    d3 = d / 3.0f;
+  s_bits = f32_to_bf16(d3);
+  s = bf16_to_f32(s_bits);
+  if (d == 0.f || s == 0.f) {
+    s_bits = 0x3F80u;
+    s = 1.f;
   }
-  // words of one group: NG == 1 -> all words; NG == 2 (D = 128) -> word w
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    float gmn = INFINITY, gmx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < KW; ++w)
-      if (NG == 1 || w == g) {
-        gmn = fminf(gmn, mn[w]);
-        gmx = fmaxf(gmx, mx[w]);
-      }
-    uint32_t sb, zb;
-    float s, z;
-    scale_zero(gmn, gmx, sb, zb, s, z);
-    szw[g] = sb | (zb << 16);
-    // Away from the ends of the fp32 range the quotient comes from the
-    // reciprocal with one Markstein correction (exact: see div_bf16); the
-    // rest of the groups take the IEEE division.
-    const bool fast = s >= 0x1p-70f && fmaxf(fabsf(gmn), fabsf(gmx)) <= 0x1p56f;
-    const float y = 1.0f / s;
-#pragma unroll
-    for (int w = 0; w < KW; ++w)
-      if (NG == 1 || w == g) {
-        if (fast) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) word = code_into(word, div_bf16(vals[w][4 * q + e], s, y), z, e);
-            codes[w][q] = word;
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) word = code_into(word, vals[w][4 * q + e] / s, z, e);
-            codes[w][q] = word;
-          }
-        }
-      }
+  const bool s_mid = s >= 0x1p-70f && s <= 0x1p70f;
+  if (s_mid) {
+    const float y0 = __builtin_amdgcn_rcpf(s);
+    y = __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0);
+  } else {
+    y = 1.0f / s;
   }
+  float zq;
+  if (s_mid && fabsf(mn) >= 0x1p-100f && fabsf(mn) <= 0x1p56f)
+    zq = div_bf16(-mn, s, y);
+  else
+    zq = -mn / s;
+  z_bits = f32_to_bf16(zq);
+  z = bf16_to_f32(z_bits);
 }
 
-// 16 one-byte codes (4 per word, values 0..3) -> one 32-bit word, code m at
-// bits 2m
-__device__ __forceinline__ uint32_t pack16(uint4 b) {
-  auto one = [](uint32_t u) {  // 4 codes -> 8 bits
-    const uint32_t t = u | (u >> 6);              // bits 0-3: codes 0,1; bits 16-19: codes 2,3
-    return (t & 0xFu) | ((t >> 12) & 0xF0u);
-  };
-  return one(b.x) | (one(b.y) << 8) | (one(b.z) << 16) | (one(b.w) << 24);
+// Scale, zero and codes of one group of clipped values x[N] (N % 4 == 0),
+// four codes per word, one byte each, x[4q + e] in byte e of words[q].
+//
+// Fast path, taken when s >= 2^-70, |min|, |max| <= 2^56 and |z| <= 128:
+// the quotient comes from the reciprocal (div_bf16, exact there) and the
+// code is v_cvt_pk_u8_f32 of t = q + z, which rounds to nearest even and
+// maps negatives to 0.  There t lies in [-0.26, 3.26]: (c - min)/s is at most
+// 3(1 + 2^-8) because s is within 2^-9 of (max - min)/3, and z is within
+// 2^-9 |z| <= 0.251 of -min/s; so the clamp to [0, 3] never acts.  Other
+// groups take the IEEE division, round and clamp.
+template <int N>
+__device__ __forceinline__ uint32_t group_codes(const float (&x)[N], float mn, float mx, uint32_t (&words)[N / 4]) {
+  uint32_t sb, zb;
+  float s, z, y;
+  scale_zero_recip(mn, mx, sb, zb, s, z, y);
+  const bool fast = s >= 0x1p-70f && fmaxf(fabsf(mn), fabsf(mx)) <= 0x1p56f && fabsf(z) <= 128.f;
+  if (fast) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        word = __builtin_amdgcn_cvt_pk_u8_f32(__fadd_rn(div_bf16(x[4 * q + e], s, y), z), e, word);
+      words[q] = word;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) word = code_into(word, x[4 * q + e] / s, z, e);
+      words[q] = word;
+    }
+  }
+  return sb | (zb << 16);
 }
 
 template <int D, int NG>
 struct BulkPage {  // one page's global inputs, as loaded
-  uint4 ka[D / 32];          // K tile as MFMA A operands: token r, channels j*D/4 + ks*8 + e
+  uint4 ka[D / 32];          // K as MFMA B operands: token r, channels j*D/4 + ks*8 + e
   uint4 va[D / 64][2];       // V of token t, channels w*64 + qq*16 + 0..15
   int id;                    // physical page (-1: none)
 };
 
+// buffer descriptor flags (gfx950 dword 3: raw buffer, 32-bit data format);
+// loads past num_records return zero
+constexpr int kBufferFlags = 0x00020000;
+
+// a wave-uniform pointer held in scalar registers
+__device__ __forceinline__ void* uniform_ptr(const void* q) {
+  const uint64_t u = (uint64_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Loads page `page` whose physical id (or -1) is `id`.  One buffer descriptor
+// per page, based at its first token, bounds the loads: slots past the last
+// token, and every slot of a page without a physical id, read as zero, with
+// no branch around the loads.
 template <int D, int NG>
-__device__ __forceinline__ void bulk_load(BulkPage<D, NG>& pg, const WriteParams& p, int kvh, int page, int pg_end,
+__device__ __forceinline__ void bulk_load(BulkPage<D, NG>& pg, const WriteParams& p, int kvh, int page, int id,
                                           int lane) {
   constexpr int KB = D / 32, KW = D / 64;
-  const int id = page < pg_end ? p.page_ids[page] : -1;
-  pg.id = (id >= 0 && id < p.int2_num_pages) ? id : -1;
+  pg.id = id;
   const int j = lane >> 4, r = lane & 15, t = lane >> 2, qq = lane & 3;
   const int tok0 = page * kPage;
-  {
-    const bool ok = pg.id >= 0 && tok0 + r < p.num_tokens;
-    const uint4* src = (const uint4*)(p.k + ((size_t)(ok ? tok0 + r : 0) * p.num_kv_heads + kvh) * D + j * (D / 4));
+  const int ntok = id >= 0 ? min(kPage, p.num_tokens - tok0) : 0;  // tokens present in this page
+  const int row = p.num_kv_heads * D * 2;                              // bytes per token
+  const size_t base = (size_t)tok0 * row + (size_t)kvh * D * 2;
+  const int nrec = __builtin_amdgcn_readfirstlane(max(ntok, 0) * row);  // wave-uniform
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t*)p.k + base), (short)0, nrec, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t*)p.v + base), (short)0, nrec, kBufferFlags);
+  // the last token's row ends at its head's D channels, inside num_records
 #pragma unroll
-    for (int ks = 0; ks < KB; ++ks) pg.ka[ks] = ok ? src[ks] : uint4{0u, 0u, 0u, 0u};
+  for (int ks = 0; ks < KB; ++ks) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, r * row + j * (D / 2) + ks * 16, 0, 0);
+    pg.ka[ks] = uint4{x[0], x[1], x[2], x[3]};
   }
-  {
-    const bool ok = pg.id >= 0 && tok0 + t < p.num_tokens;
-    const uint16_t* src = p.v + ((size_t)(ok ? tok0 + t : 0) * p.num_kv_heads + kvh) * D;
 #pragma unroll
-    for (int w = 0; w < KW; ++w) {
-      pg.va[w][0] = ok ? *(const uint4*)(src + w * 64 + qq * 16) : uint4{0u, 0u, 0u, 0u};
-      pg.va[w][1] = ok ? *(const uint4*)(src + w * 64 + qq * 16 + 8) : uint4{0u, 0u, 0u, 0u};
-    }
+  for (int w = 0; w < KW; ++w) {
+    const auto x0 = __builtin_amdgcn_raw_buffer_load_b128(rv, t * row + w * 128 + qq * 32, 0, 0);
+    const auto x1 = __builtin_amdgcn_raw_buffer_load_b128(rv, t * row + w * 128 + qq * 32 + 16, 0, 0);
+    pg.va[w][0] = uint4{x0[0], x0[1], x0[2], x0[3]};
+    pg.va[w][1] = uint4{x1[0], x1[1], x1[2], x1[3]};
   }
 }
 
@@ -333,103 +364,137 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG>& pg, const Write
   constexpr int REC = D / 8;
   const int j = lane >> 4, r = lane & 15, t = lane >> 2, qq = lane & 3;
   const int tok0 = page * kPage;
-  auto& pw = sm.w[wave];
-  // ---- Y = K R_K on the bf16 matrix cores (R split hi + lo)
-#pragma unroll
-  for (int ot = 0; ot < OT; ++ot) {
-    v4f c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KB; ++ks) {
-      const v8bf a = __builtin_bit_cast(v8bf, pg.ka[ks]);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, sm.rb[0][ot][ks][lane]), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, sm.rb[1][ot][ks][lane]), c, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pw.y[4 * j + i][ot * 16 + r] = c[i];
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // ---- quantize K (lane = 4t + qq) and V
-  const bool tok_ok = pg.id >= 0 && tok0 + t < p.num_tokens;
-  uint32_t kc[KW][4], vc[KW][4], szk[NG], szv[NG];
+  uint8_t(*vcode)[D] = sm.vcode[wave];
+  // the page's INT2 block through a buffer descriptor: stores without a
+  // physical page (num_records 0) or from lanes with nothing to store (offset
+  // past the block) are dropped, so no store sits behind a branch
+  const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(p.int2_pool + ((size_t)max(pg.id, 0) * p.num_kv_heads + kvh) * BLK2), (short)0,
+      pg.id >= 0 ? BLK2 : 0, kBufferFlags);
+  constexpr int kDrop = 1 << 20;  // an offset past every block
+  const int sc0 = 8 * D;          // scale words: 8*NG per token quad
+  // ---- keys: Y^T = R_K^T K^T on the bf16 matrix cores (R split hi + lo).
+  // The A operands hold R's columns in the order that gives lane (j, r)
+  // token r's channels w*64 + j*16 + 4q + i in y[4w + q][i]: the channels of
+  // the lane's own code record (j, r), word w.
+  uint32_t kwd[KW];
   {
-    float vals[KW][16];
+    float y[OT][4];
 #pragma unroll
-    for (int w = 0; w < KW; ++w)
+    for (int ot = 0; ot < OT; ++ot) {
+      v4f c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < 16; m += 4) {
-        const float4 x = *(const float4*)&pw.y[t][w * 64 + qq * 16 + m];
-        vals[w][m] = x.x;
-        vals[w][m + 1] = x.y;
-        vals[w][m + 2] = x.z;
-        vals[w][m + 3] = x.w;
+      for (int ks = 0; ks < KB; ++ks) {
+        const v8bf b = __builtin_bit_cast(v8bf, pg.ka[ks]);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sm.rb[0][ot][ks][lane]), b, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sm.rb[1][ot][ks][lane]), b, c, 0, 0, 0);
       }
-    quant_lane<D, NG>(vals, tau_k, kc, szk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[ot][i] = c[i];
+    }
+    const bool tok_ok = pg.id >= 0 && tok0 + r < p.num_tokens;
+    // x[(w' * 4 + i) * 4 + q] = y[4w + q][i], w' the word inside the group:
+    // the group's codes come back as words (w', i) holding bytes q
+    constexpr int WPG = KW / NG;  // record words per group
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float x[WPG * 16];
+      float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < WPG * 16; ++u) {
+        const int w = g * WPG + u / 16, i = (u / 4) % 4, q = u % 4;
+        x[u] = __builtin_amdgcn_fmed3f(y[4 * w + q][i], -tau_k, tau_k);
+        mn = fminf(mn, x[u]);
+        mx = fmaxf(mx, x[u]);
+      }
+      uint32_t words[WPG * 4];
+      const uint32_t sz = group_codes<WPG * 16>(x, col4_min(mn), col4_max(mx), words);
+#pragma unroll
+      for (int wp = 0; wp < WPG; ++wp) {
+        // byte q of word i holds code m = 4q + i at bits 8q; shifted by 2i
+        const uint32_t* d = &words[wp * 4];
+        const uint32_t word = d[0] | (d[1] << 2) | (d[2] << 4) | (d[3] << 6);
+        kwd[g * WPG + wp] = tok_ok ? word : 0u;
+      }
+      // scales of token r (zeros for slots past the last token)
+      __builtin_amdgcn_raw_buffer_store_b32(tok_ok ? sz : 0u, out,
+                                            j == g ? sc0 + 4 * ((r / 4) * 8 * NG + (r % 4) * NG + g) : kDrop, 0, 0);
+    }
   }
+  // ---- values (already rotated), lane = 4t + qq: channels w*64 + qq*16 + m
   {
-    float vals[KW][16];
+    const bool tok_ok = pg.id >= 0 && tok0 + t < p.num_tokens;
+    float x[KW][16];
+    float mn[KW], mx[KW];
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
       const uint32_t xs[8] = {pg.va[w][0].x, pg.va[w][0].y, pg.va[w][0].z, pg.va[w][0].w,
                               pg.va[w][1].x, pg.va[w][1].y, pg.va[w][1].z, pg.va[w][1].w};
+      mn[w] = INFINITY;
+      mx[w] = -INFINITY;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        vals[w][2 * q] = bf16_lo(xs[q]);
-        vals[w][2 * q + 1] = bf16_hi(xs[q]);
+        x[w][2 * q] = __builtin_amdgcn_fmed3f(bf16_lo(xs[q]), -tau_v, tau_v);
+        x[w][2 * q + 1] = __builtin_amdgcn_fmed3f(bf16_hi(xs[q]), -tau_v, tau_v);
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        mn[w] = fminf(mn[w], x[w][m]);
+        mx[w] = fmaxf(mx[w], x[w][m]);
+      }
+      mn[w] = quad_min(mn[w]);
+      mx[w] = quad_max(mx[w]);
+    }
+    uint32_t words[KW][4];
+    if constexpr (NG == 1 && KW == 2) {
+      float xx[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) xx[u] = x[u / 16][u % 16];
+      uint32_t ww[8];
+      const uint32_t sz = group_codes<32>(xx, fminf(mn[0], mn[1]), fmaxf(mx[0], mx[1]), ww);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) words[u / 4][u % 4] = ww[u];
+      __builtin_amdgcn_raw_buffer_store_b32(tok_ok ? sz : 0u, out,
+                                            qq == 0 ? sc0 + 4 * ((t / 4) * 8 * NG + 4 * NG + (t % 4) * NG) : kDrop,
+                                            0, 0);
+    } else {
+      // one group per 64-channel word group w
+      static_assert(NG == KW, "V groups are 64 channels wide here");
+#pragma unroll
+      for (int w = 0; w < KW; ++w) {
+        const uint32_t sz = group_codes<16>(x[w], mn[w], mx[w], words[w]);
+        __builtin_amdgcn_raw_buffer_store_b32(
+            tok_ok ? sz : 0u, out, qq == 0 ? sc0 + 4 * ((t / 4) * 8 * NG + 4 * NG + (t % 4) * NG + w) : kDrop, 0, 0);
       }
     }
-    quant_lane<D, NG>(vals, tau_v, vc, szv);
-  }
-  // codes of tokens past the last one are zero
 #pragma unroll
-  for (int w = 0; w < KW; ++w)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      kc[w][q] = tok_ok ? kc[w][q] : 0u;
-      vc[w][q] = tok_ok ? vc[w][q] : 0u;
-    }
-  uint8_t* blk = p.int2_pool + ((size_t)max(pg.id, 0) * p.num_kv_heads + kvh) * BLK2;
-  // scales of token t (zeros for slots past the last token)
-  if (pg.id >= 0 && qq < NG) {
-    const int g = qq;
-    uint32_t* sc = (uint32_t*)(blk + 8 * D + (t / 4) * 32 * NG);
-    sc[(t % 4) * NG + g] = tok_ok ? szk[g] : 0u;
-    sc[4 * NG + (t % 4) * NG + g] = tok_ok ? szv[g] : 0u;
+    for (int w = 0; w < KW; ++w)
+      *(uint4*)&vcode[t][w * 64 + qq * 16] =
+          tok_ok ? uint4{words[w][0], words[w][1], words[w][2], words[w][3]} : uint4{0u, 0u, 0u, 0u};
   }
-  // the codes overwrite the rotated tile: every lane of the wave has read it
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-  for (int w = 0; w < KW; ++w) {
-    *(uint4*)&pw.code[0][t][w * 64 + qq * 16] = uint4{kc[w][0], kc[w][1], kc[w][2], kc[w][3]};
-    *(uint4*)&pw.code[1][t][w * 64 + qq * 16] = uint4{vc[w][0], vc[w][1], vc[w][2], vc[w][3]};
-  }
+  // the codes of the whole page are in this wave's LDS (one wave's LDS
+  // accesses complete in order)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // ---- this lane's code record (j, r)
-  uint32_t kwd[KW], vwd[KW];
+  uint32_t vwd[KW];
 #pragma unroll
   for (int w = 0; w < KW; ++w) {
-    kwd[w] = pack16(*(const uint4*)&pw.code[0][r][w * 64 + j * 16]);
     uint32_t vword = 0;
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        vword |= (uint32_t)pw.code[1][4 * j + i][(4 * w + bb) * 16 + r] << (16 * (i & 1) + 2 * (2 * bb + (i >> 1)));
+        vword |= (uint32_t)vcode[4 * j + i][(4 * w + bb) * 16 + r] << (16 * (i & 1) + 2 * (2 * bb + (i >> 1)));
     vwd[w] = vword;
   }
-  if (pg.id >= 0) {
-    if constexpr (D == 128) {
-      *(uint4*)(blk + lane * REC) = uint4{kwd[0], kwd[1], vwd[0], vwd[1]};
-    } else {
-      *(uint2*)(blk + lane * REC) = uint2{kwd[0], vwd[0]};
-    }
+  if constexpr (D == 128) {
+    __builtin_amdgcn_raw_buffer_store_b128(v4u{kwd[0], kwd[1], vwd[0], vwd[1]}, out, lane * REC, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b64(v2u{kwd[0], vwd[0]}, out, lane * REC, 0, 0);
   }
-  // the next page's tile reuses this wave's LDS
+  // the next page's codes reuse this wave's LDS
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -437,7 +502,7 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG>& pg, const Write
 
 template <int D, int NG>
 __global__ void __launch_bounds__(kQpThreads) k_quantize_pack(const WriteParams p) {
-  constexpr int KB = D / 32, OT = D / 16;
+  constexpr int KB = D / 32;
   __shared__ BulkSmem<D, NG> sm;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int kvh = blockIdx.y;
@@ -445,17 +510,28 @@ __global__ void __launch_bounds__(kQpThreads) k_quantize_pack(const WriteParams 
   const int pg0 = blockIdx.x * p.pages_per_block;
   if (pg0 >= npages) return;
   const int pg_end = min(pg0 + p.pages_per_block, npages);
+  // wave w handles pages pg0 + w + k*kQpWaves, k < my_n (at most 64: the
+  // launch caps pages per workgroup); lane k holds the k-th one's physical id
+  const int first = pg0 + wave;
+  const int my_n = first < pg_end ? (pg_end - first + kQpWaves - 1) / kQpWaves : 0;
+  int my_ids = -1;
+  if (lane < my_n) {
+    const int id = p.page_ids[first + lane * kQpWaves];
+    my_ids = (id >= 0 && id < p.int2_num_pages) ? id : -1;
+  }
+  auto id_of = [&](int k) { return k < my_n ? __builtin_amdgcn_readlane(my_ids, k) : -1; };
   BulkPage<D, NG> cur;
-  bulk_load<D, NG>(cur, p, kvh, pg0 + wave, pg_end, lane);  // first page's loads overlap the R_K split
-  // R_K (fp32) -> R_hi + R_lo (bf16) in B-operand order:
-  // rb[hl][ot][ks][lane (j, n)] element e = R[j*D/4 + ks*8 + e][ot*16 + n]
+  bulk_load<D, NG>(cur, p, kvh, first, id_of(0), lane);  // first page's loads overlap the R_K split
+  // R_K (fp32) -> R_hi + R_lo (bf16) in A-operand order:
+  // rb[hl][ot][ks][lane (j, n)] element e = R[j*D/4 + ks*8 + e][pi(ot, n)],
+  // pi(ot, 4a + i) = (ot / 4)*64 + a*16 + (ot % 4)*4 + i, so that output row
+  // 4a + i of tile ot is that output channel
   {
     const float* rk = p.r_k + (size_t)kvh * D * D;
     for (int idx = tid; idx < D * D / 8; idx += kQpThreads) {
-      // eight consecutive input rows of one output column: one operand lane
       const int lane_op = idx % 64, ks = (idx / 64) % KB, ot = idx / (64 * KB);
       const int j = lane_op >> 4, n = lane_op & 15;
-      const int in0 = j * (D / 4) + ks * 8, out = ot * 16 + n;
+      const int in0 = j * (D / 4) + ks * 8, out = (ot / 4) * 64 + (n / 4) * 16 + (ot % 4) * 4 + n % 4;
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -469,15 +545,15 @@ __global__ void __launch_bounds__(kQpThreads) k_quantize_pack(const WriteParams 
   }
   __syncthreads();
   const float tau_k = p.tau_k[kvh], tau_v = p.tau_v[kvh];
-  // wave w handles pages pg0 + w, pg0 + w + kQpWaves, ...; two pages per trip
-  // so that the current and next page alternate between two register sets
+  // two pages per trip so that the current and next page alternate between
+  // two register sets
   BulkPage<D, NG> nxt;
-  for (int pg = pg0 + wave; pg < pg_end; pg += 2 * kQpWaves) {
-    bulk_load<D, NG>(nxt, p, kvh, pg + kQpWaves, pg_end, lane);
-    bulk_page<D, NG>(cur, p, sm, kvh, pg, wave, lane, tau_k, tau_v);
-    if (pg + kQpWaves >= pg_end) break;
-    bulk_load<D, NG>(cur, p, kvh, pg + 2 * kQpWaves, pg_end, lane);
-    bulk_page<D, NG>(nxt, p, sm, kvh, pg + kQpWaves, wave, lane, tau_k, tau_v);
+  for (int k = 0; k < my_n; k += 2) {
+    bulk_load<D, NG>(nxt, p, kvh, first + (k + 1) * kQpWaves, id_of(k + 1), lane);
+    bulk_page<D, NG>(cur, p, sm, kvh, first + k * kQpWaves, wave, lane, tau_k, tau_v);
+    if (k + 1 >= my_n) break;
+    bulk_load<D, NG>(cur, p, kvh, first + (k + 2) * kQpWaves, id_of(k + 2), lane);
+    bulk_page<D, NG>(nxt, p, sm, kvh, first + (k + 1) * kQpWaves, wave, lane, tau_k, tau_v);
   }
 }
 
@@ -508,9 +584,11 @@ void launch_ad(const WriteParams& p, hipStream_t s) {
 template <int D, int NG>
 void launch_qp(const WriteParams& p, hipStream_t s) {
   const int npages = (p.num_tokens + kPage - 1) / kPage;
-  const int gx = (npages + p.pages_per_block - 1) / p.pages_per_block;
+  WriteParams q = p;
+  q.pages_per_block = std::min(std::max(p.pages_per_block, 1), 64 * kQpWaves);  // <= 64 pages per wave
+  const int gx = (npages + q.pages_per_block - 1) / q.pages_per_block;
   if (gx == 0) return;
-  hipLaunchKernelGGL((k_quantize_pack<D, NG>), dim3(gx, p.num_kv_heads), dim3(kQpThreads), 0, s, p);
+  hipLaunchKernelGGL((k_quantize_pack<D, NG>), dim3(gx, p.num_kv_heads), dim3(kQpThreads), 0, s, q);
 }
 
 template <int D>
