@@ -89,14 +89,21 @@ class Decoder:
             raise RuntimeError(self.lib.oscar_last_error().decode())
 
 
-def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0, shared_tables=True):
+def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0, shared_tables=True, pre_append=False):
     """n_copies independent pools of one workload, written by the library.
 
     shared_tables=True models one layer's KV cache per copy: every copy has
     its own pool tensor (a slice of one allocation) and all copies share the
     sequences' page tables, as the layers of a model share a sequence's page
     table.  shared_tables=False gives every copy its own page tables over one
-    big pool (the page-table reads are then cold as well)."""
+    big pool (the page-table reads are then cold as well); the INT2 pool then
+    spans the workload's INT2 arena (wl.int2_arena_bytes) when that is larger,
+    pages scattered over it at random.
+
+    pre_append=True builds the state before the step's append: the BF16
+    window also holds the token that the step's oscar_append_demote moves to
+    the INT2 history.  Sequences 0..wl.shared_prefix_seqs-1 share the INT2
+    pages and BF16 sink pages of their common prefix (one physical copy)."""
     import numpy as np
     import torch
     rng = np.random.Generator(np.random.PCG64(seed + 300))
@@ -111,32 +118,51 @@ def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0, shared_
             b16_lists.append(list(range((L + 15) // 16)))
             i2_counts.append(0)
         else:
-            r0 = max(wl.sink, L - wl.recent)
+            r0 = max(wl.sink, L - wl.recent - (1 if pre_append else 0))
             b16_lists.append([p for p in range((L + 15) // 16)
                               if p * 16 < min(L, wl.sink) or ((p + 1) * 16 > r0 and p * 16 < L)])
             i2_counts.append((wl.hist_len(L) + 15) // 16)
-    n16c = max(sum(len(x) for x in b16_lists), 1)  # pages per copy
-    n2c = max(sum(i2_counts), 1)
+    # prefix sharing: logical pages below these counts map to sequence 0's pages
+    n_sh_seq = wl.shared_prefix_seqs if (wl.shared_prefix_seqs and not bf16_only) else 0
+    n_sh2 = max(0, wl.shared_prefix_tokens - wl.sink) // 16 if n_sh_seq else 0
+    n_sh16 = min(wl.sink, wl.shared_prefix_tokens) // 16 if n_sh_seq else 0
+    saved16 = max(0, n_sh_seq - 1) * n_sh16
+    saved2 = max(0, n_sh_seq - 1) * n_sh2
+    n16c = max(sum(len(x) for x in b16_lists) - saved16, 1)  # physical pages per copy
+    n2c = max(sum(i2_counts) - saved2, 1)
+    arena2 = n2c * n_copies
+    if not shared_tables and wl.int2_arena_bytes:
+        arena2 = max(arena2, wl.int2_arena_bytes // pool.int2_page_bytes)
     bf16_all = torch.empty((n16c * n_copies, pool.bf16_page_bytes), dtype=torch.uint8, device="cuda")
-    int2_all = torch.empty((n2c * n_copies, pool.int2_page_bytes), dtype=torch.uint8, device="cuda")
+    int2_all = torch.empty((arena2, pool.int2_page_bytes), dtype=torch.uint8, device="cuda")
 
-    def tables(n16, n2):
-        perm16, perm2 = rng.permutation(n16), rng.permutation(n2)
+    def tables(phys16, phys2):
+        """Page tables over the given physical page ids (consumed in order)."""
         bpt = np.full((wl.batch, max_pages + 1), -1, np.int32)
         ipt = np.full((wl.batch, max(max(i2_counts), 1)), -1, np.int32)
         p16 = p2 = 0
         for b in range(wl.batch):
             for lp in b16_lists[b]:
-                bpt[b, lp] = perm16[p16]
-                p16 += 1
+                if 0 < b < n_sh_seq and lp < n_sh16:
+                    bpt[b, lp] = bpt[0, lp]
+                else:
+                    bpt[b, lp] = phys16[p16]
+                    p16 += 1
             for lp in range(i2_counts[b]):
-                ipt[b, lp] = perm2[p2]
-                p2 += 1
+                if 0 < b < n_sh_seq and lp < n_sh2:
+                    ipt[b, lp] = ipt[0, lp]
+                else:
+                    ipt[b, lp] = phys2[p2]
+                    p2 += 1
+        assert p16 <= len(phys16) and p2 <= len(phys2)
         return torch.from_numpy(bpt).cuda(), torch.from_numpy(ipt).cuda()
 
-    shared = tables(n16c, n2c) if shared_tables else None
-    if not shared_tables:
-        glob16, glob2 = rng.permutation(n16c * n_copies), rng.permutation(n2c * n_copies)
+    if shared_tables:
+        shared = tables(rng.permutation(n16c), rng.permutation(n2c))
+    else:
+        glob16 = rng.permutation(n16c * n_copies)
+        glob2 = rng.choice(arena2, n2c * n_copies, replace=False) if arena2 > n2c * n_copies else \
+            rng.permutation(arena2)
     copies = []
     for ci in range(n_copies):
         if shared_tables:
@@ -144,14 +170,8 @@ def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0, shared_
             b16, i2 = bf16_all[ci * n16c:(ci + 1) * n16c], int2_all[ci * n2c:(ci + 1) * n2c]
         else:
             # distinct tables over the whole allocation; copy ci owns the
-            # pages its permutation slice names
-            perm16 = glob16[ci * n16c:(ci + 1) * n16c]
-            perm2 = glob2[ci * n2c:(ci + 1) * n2c]
-            bpt_h, ipt_h = tables(n16c, n2c)
-            bpt = torch.from_numpy(np.where(bpt_h.cpu().numpy() >= 0, perm16[np.maximum(bpt_h.cpu().numpy(), 0)], -1)
-                                   .astype(np.int32)).cuda()
-            ipt = torch.from_numpy(np.where(ipt_h.cpu().numpy() >= 0, perm2[np.maximum(ipt_h.cpu().numpy(), 0)], -1)
-                                   .astype(np.int32)).cuda()
+            # pages its slice of the global draw names
+            bpt, ipt = tables(glob16[ci * n16c:(ci + 1) * n16c], glob2[ci * n2c:(ci + 1) * n2c])
             b16, i2 = bf16_all, int2_all
         cp = {"bf16_pt": bpt, "int2_pt": ipt, "bf16_pool": b16, "int2_pool": i2}
         for b, L in enumerate(wl.seq_lens):
@@ -161,7 +181,7 @@ def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0, shared_
                 continue
             sink = min(L, wl.sink)
             oscar.oscar_write_bf16(pool, k[:sink].contiguous(), v[:sink].contiguous(), 0, bpt[b], b16)
-            r0 = wl.recent_start(L)
+            r0 = max(wl.sink, L - wl.recent - (1 if pre_append else 0))
             if r0 < L:
                 oscar.oscar_write_bf16(pool, k[r0:L].contiguous(), v[r0:L].contiguous(), r0, bpt[b], b16)
             h = wl.hist_len(L)
@@ -171,6 +191,101 @@ def build_pools(oscar, pool, wl, inp, n_copies, bf16_only=False, seed=0, shared_
         copies.append(cp)
     torch.cuda.synchronize()
     return copies, r_k
+
+
+class DemoteDecoder:
+    """One decode step with the append/demote folded in, per pool copy:
+    oscar_append_demote (token L-1 appended, token L-1-W demoted to INT2),
+    then oscar_decode_attention at length L, both on the current stream."""
+
+    def __init__(self, oscar, pool, wl, q, copies, r_k, tau_k, tau_v, k_new, v_new, lens_pre, lens, out, ws):
+        import torch
+        self.torch = torch
+        self.lib = oscar.load()
+        self.dec = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws)
+        self.args = []
+        for c in copies:
+            b16, i2 = c["bf16_pool"], c["int2_pool"]
+            self.args.append((pool.handle, wl.batch, k_new.data_ptr(), v_new.data_ptr(), lens_pre.data_ptr(),
+                              c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], b16.shape[0],
+                              c["int2_pt"].data_ptr(), c["int2_pt"].shape[1], i2.shape[0],
+                              b16.data_ptr(), i2.data_ptr(), r_k.data_ptr(), None, tau_k.data_ptr(),
+                              tau_v.data_ptr()))
+
+    def __call__(self, i):
+        st = self.lib.oscar_append_demote(*self.args[i % len(self.args)],
+                                          self.torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(self.lib.oscar_last_error().decode())
+        self.dec(i)
+
+
+def unique_kv_bytes(wl):
+    """HBM bytes of one decode step counting pages shared by a prefix once."""
+    kv = wl.kv_bytes()
+    if not wl.shared_prefix_seqs:
+        return kv["total"]
+    n_sh2 = max(0, wl.shared_prefix_tokens - wl.sink) // 16
+    n_sh16 = min(wl.sink, wl.shared_prefix_tokens)
+    dup = (wl.shared_prefix_seqs - 1) * wl.num_kv_heads * (
+        n_sh2 * 16 * wl.int2_bytes_per_token_head() + n_sh16 * wl.bf16_bytes_per_token_head())
+    return kv["total"] - dup
+
+
+def bench_decode_workload(oscar, name, steps, warmup, repeats, cold_bytes):
+    """Decode steps of a batched workload, timed like the headline: HIP-graph
+    replay over cold pool copies.  With wl.demote every step also appends one
+    token per sequence and demotes one to the INT2 history."""
+    import torch
+    from synthetic import CONFIGS, draw_inputs
+    wl = CONFIGS[name]
+    kv = wl.kv_bytes()
+    uniq = unique_kv_bytes(wl)
+    inp = draw_inputs(wl, device="cuda")
+    pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
+                                            wl.sink, wl.recent, 1, 0.0))
+    n_copies = max(2, math.ceil(cold_bytes / uniq))
+    copies, r_k = build_pools(oscar, pool, wl, inp, n_copies, seed=wl.seed, shared_tables=not wl.demote,
+                              pre_append=wl.demote)
+    q = inp.q.contiguous()
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = pool.alloc_workspace(wl.batch, max(wl.seq_lens))
+    if wl.demote:
+        c = inp.calib
+        tau_k = torch.as_tensor(c.tau_k).cuda()
+        tau_v = torch.as_tensor(c.tau_v).cuda()
+        k_new = torch.stack([inp.k[b][L - 1] for b, L in enumerate(wl.seq_lens)]).contiguous()
+        v_new = torch.stack([inp.v[b][L - 1] for b, L in enumerate(wl.seq_lens)]).contiguous()
+        lens_pre = lens - 1
+        step = DemoteDecoder(oscar, pool, wl, q, copies, r_k, tau_k, tau_v, k_new, v_new, lens_pre, lens, out, ws)
+    else:
+        step = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws)
+    ms, ms_min = time_steps(step, steps, warmup, repeats, use_graph=True)
+    # append/demote (and the write it does) counted on top of the KV read
+    # (per sequence and KV head: bf16 K, V written by the append and read by
+    # the demotion, the INT2 token written)
+    extra = wl.batch * wl.num_kv_heads * (2 * (2 * wl.head_dim * 2) + wl.int2_bytes_per_token_head()) \
+        if wl.demote else 0
+    log(f"{name}: {ms * 1e3:.2f} us/step ({'append/demote + ' if wl.demote else ''}decode), "
+        f"{uniq / (ms * 1e-3) / 1e9:.1f} GB/s unique KV")
+    res = {"workload": name, "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+           "context": list(wl.seq_lens) if wl.batch <= 8 else f"{wl.batch} x {wl.seq_lens[0]}",
+           "us_per_step": round(ms * 1e3, 3), "us_min": round(ms_min * 1e3, 3),
+           "tokens_per_s": round(wl.batch / (ms * 1e-3), 1),
+           "kv_bytes_per_step": kv["total"], "unique_kv_bytes_per_step": uniq,
+           "GBps": round((uniq + extra) / (ms * 1e-3) / 1e9, 2),
+           "pct_hbm_peak": round(100 * (uniq + extra) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+           "pool_copies": n_copies}
+    if wl.demote:
+        res["append_demote"] = "one token appended and one demoted per sequence inside every timed step"
+        res["int2_arena_GiB"] = round(wl.int2_arena_bytes / 2**30, 1)
+    if wl.shared_prefix_seqs:
+        res["shared_prefix"] = f"{wl.shared_prefix_seqs} sequences share {wl.shared_prefix_tokens} tokens"
+        res["logical_GBps"] = round(kv["total"] / (ms * 1e-3) / 1e9, 2)
+    del step, copies
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_steps(step, n_steps, warmup, repeats, use_graph=True):
@@ -346,6 +461,11 @@ def main():
     from synthetic import CONFIGS, draw_inputs
 
     oscar.load()
+    if args.only in ("demote", "mixed"):
+        name = "qwen3-8b-b32-l32k-demote" if args.only == "demote" else "qwen3-32b-b8-mixed-prefix"
+        print(json.dumps({args.only: bench_decode_workload(oscar, name, max(10, args.steps // 4), args.warmup,
+                                                           args.repeats, args.cold_bytes)}), flush=True)
+        return
     if args.only == "bulk":
         if args.profile_steps:
             bench_bulk_quant(oscar, profile_launches=args.profile_steps)
@@ -426,6 +546,15 @@ def main():
                                      "int2_speedup": round(ms16 / ms, 3)}
         del bcopies
         torch.cuda.empty_cache()
+    if args.only == "all":
+        # the other workloads, measured the same way (not the headline)
+        result["other_workloads"] = {
+            "batched_demote": bench_decode_workload(oscar, "qwen3-8b-b32-l32k-demote", max(10, args.steps // 4),
+                                                    args.warmup, args.repeats, args.cold_bytes),
+            "mixed_prefix_gqa8": bench_decode_workload(oscar, "qwen3-32b-b8-mixed-prefix", max(10, args.steps // 4),
+                                                       args.warmup, args.repeats, args.cold_bytes),
+            "bulk_quantize": bench_bulk_quant(oscar),
+        }
     result["copy_ceiling_GBps"] = round(copy_ceiling_gbps(), 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp)
