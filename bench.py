@@ -342,21 +342,25 @@ def copy_ceiling_gbps():
     return 2 * n / ms / 1e6
 
 
-def kernel_sha():
+DECODE_SOURCES = ("decode.hip", "common.h", "kernels.h")
+BULK_SOURCES = ("write.hip", "common.h", "kernels.h")
+
+
+def source_sha(files):
     h = hashlib.sha256()
-    for f in ("decode.hip", "common.h", "kernels.h"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "long_context_decode_oscar_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload):
+def traffic_for(workload, files=DECODE_SOURCES):
     """HBM bytes per launch from committed rocprofv3 PMC counters, if they
     were taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("kernel_source_sha") != kernel_sha():
+    if t.get("kernel_source_sha") != source_sha(files):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -434,6 +438,7 @@ def bench_bulk_quant(oscar, steps=10, warmup=3, repeats=5, profile_launches=0):
     return {"workload": wl.name, "tokens": t, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
             "us_per_launch": round(ms * 1e3, 3), "us_min": round(ms_min * 1e3, 3), "bytes_per_launch": nbytes,
             "GBps": round(gbps, 2), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            "hbm_traffic_bytes": traffic_for(wl.name, BULK_SOURCES),
             "kernel": "k_quantize_pack (bf16-MFMA key rotation + clip + quantize + pack)"}
 
 
