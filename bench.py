@@ -347,9 +347,15 @@ BULK_SOURCES = ("write.hip", "common.h", "kernels.h")
 
 
 def source_sha(files):
+    """Hash of the kernel sources with comments and blank space removed, so
+    that it changes with the code and not with its commentary."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        h.update(open(os.path.join(ROOT, "long_context_decode_oscar_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "long_context_decode_oscar_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

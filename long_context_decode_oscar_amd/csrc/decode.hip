@@ -16,9 +16,11 @@
 //           ~16 significant bits.
 //           With the key dequantization k' = s (code - z) the logit is
 //           sm * s * sq/256 * (S_ab - z * sum(256 a + b)).
-//   P.V     on the bf16 matrix cores with the value codes as exact bf16
-//           operands 1 + code/8 and the weights w = p * s_V as bf16:
-//           sum w (code - z) = 8 (sum w (1 + code/8) - sum w) - sum w z.
+//   P.V     on the fp16 matrix cores.  The value codes become exact fp16
+//           operands bias + code (bias 16 or 4, set by OR-ing an exponent
+//           into the shifted code bits) and the weights w = p * s_V are
+//           fp16:  sum w (code - z) = sum w (bias + code) - sum w (bias + z),
+//           the second sum tracked from the same rounded weights.
 //   softmax online, with a lazy running max (rescale only when a logit
 //           exceeds the running max by more than 2^8).
 // The GQA query heads of a KV head share every loaded page; the 16 columns
