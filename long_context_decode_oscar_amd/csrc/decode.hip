@@ -904,17 +904,24 @@ __global__ void __launch_bounds__(kThreads)
       o = so / sw;
       lse = mx + __log2f(sw);  // log2 units
     }
-    p.part_o[(pidx + h) * D + c] = o;
-    if (c == 0) p.part_lse[pidx + h] = lse;
+    // device-scope stores write through the XCD's L2, so no L2 write-back
+    // is needed before the ticket below
+    __hip_atomic_store(p.part_o + (pidx + h) * D + c, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c == 0) __hip_atomic_store(p.part_lse + pidx + h, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // ---- last workgroup of this (sequence, KV head) merges every partial.
-  // Every wave drains its partial stores to L2 (s_waitcnt vmcnt(0)); then one
-  // thread releases at device scope (L2 write-back) and takes a ticket; the
-  // workgroup that takes the last ticket acquires and reads all partials.
+  // Every wave waits until its device-scope partial stores have completed
+  // (s_waitcnt vmcnt(0)); then one thread takes a ticket with a device-scope
+  // atomic.  The workgroup that takes the last ticket invalidates its L2
+  // (acquire) and reads all partials from the device-coherent level.  A
+  // release on the ticket would also write back the whole L2 of the XCD,
+  // which measured 1-3 us per workgroup; the partials never sit dirty in L2,
+  // so it has nothing to publish.  Each head's counter has a 128-byte line
+  // of its own.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.counters + head_base, 1u, __ATOMIC_RELEASE,
+    const uint32_t prev = __hip_atomic_fetch_add(p.counters + head_base * kCounterStride, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == (uint32_t)(total - 1);
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -961,7 +968,8 @@ __global__ void __launch_bounds__(kThreads)
     }
     p.out[((size_t)b * hq + kvh * GQA + h) * D + c] = (uint16_t)f32_to_bf16(S > 0.f ? A / S : 0.f);
   }
-  if (tid == 0) __hip_atomic_store(p.counters + head_base, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0)
+    __hip_atomic_store(p.counters + head_base * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // --------------------------------------------------------- oscar_merge --

@@ -6,6 +6,9 @@
 
 namespace oscar {
 
+// decode ticket counters: one per (sequence, KV head), each on its own 128-byte line
+constexpr int kCounterStride = 32;
+
 struct DecodeParams {
   const uint16_t* q;         // [B][Hq][D] bf16
   const int32_t* seq_lens;   // [B]
@@ -15,7 +18,7 @@ struct DecodeParams {
   const uint8_t* int2_pool;
   const float* r_k;          // [Hkv][D][D]
   uint16_t* out;             // [B][Hq][D] bf16
-  uint32_t* counters;        // [B][Hkv]
+  uint32_t* counters;        // [B][Hkv], kCounterStride words apart
   float* part_lse;           // [B][Hkv][U][GQA] log2 of the partial's softmax sum
   float* part_o;             // [B][Hkv][U][GQA][D]
   int32_t bf16_pt_stride, bf16_num_pages;

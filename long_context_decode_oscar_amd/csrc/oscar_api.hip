@@ -130,7 +130,7 @@ Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
   const size_t parts = heads * pl.units * pool->gqa;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   pl.off_counters = 0;
-  pl.off_lse = up(heads * sizeof(uint32_t));
+  pl.off_lse = up(heads * oscar::kCounterStride * sizeof(uint32_t));
   pl.off_o = pl.off_lse + up(parts * sizeof(float));
   pl.bytes = pl.off_o + up(parts * c.head_dim * sizeof(float));
   return pl;
