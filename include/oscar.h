@@ -24,10 +24,13 @@
  *  - Positions of a sequence of length L (L counts every stored token):
  *      sink [0, min(L, S0)), history [S0, max(S0, L-W)),
  *      recent [max(S0, L-W), L).
- *    Keys in the BF16 segments are unrotated; values are stored in the pool's
- *    V basis in every segment (R_V absorbed into the projection weights,
- *    MarkTechPost article, "The Serving System"), and decode output is in that
- *    basis.
+ *    Keys in the BF16 segments are unrotated.  Values: with v_absorbed = 1
+ *    (R_V absorbed into the projection weights, MarkTechPost article, "The
+ *    Serving System") every segment stores V in the pool's V basis and the
+ *    decode output is in that basis; with v_absorbed = 0 the BF16 segments
+ *    store V itself, the INT2 history stores V R_V (rotated at demotion like
+ *    K), and decode rotates the history's contribution back by R_V^T, so the
+ *    output is in the model basis.
  *  - Errors: functions return an oscar_status; arguments are validated on the
  *    host before anything is launched, and nothing is launched on error.
  *    oscar_last_error() gives a human-readable reason (thread-local).
@@ -83,7 +86,8 @@ typedef enum {
  * Supported: head_dim 64 or 128; group_size 64 or 128 dividing head_dim;
  * num_q_heads / num_kv_heads in {2, 4, 8}; page_size 16; sink_tokens a
  * multiple of 16 (64 by default, MarkTechPost article, "The Serving System");
- * recent_tokens >= 1 (256 by default, same section); v_absorbed = 1. */
+ * recent_tokens >= 1 (256 by default, same section); v_absorbed 1 or 0
+ * (see the value basis above). */
 typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -129,12 +133,14 @@ oscar_status oscar_decode_workspace_bytes(const oscar_pool* pool, int32_t batch,
  *   - writes k_new[b], v_new[b] (bf16 [batch][Hkv][D]; v_new in the pool's V
  *     basis) at position L_b of the BF16 pool;
  *   - if d = L_b - W >= S0, reads token d's K and V from the BF16 pool and
- *     writes  k_d R_K[k]  (fp32 accumulation) and  v_d  (absorbed), each
+ *     writes  k_d R_K[k]  (fp32 accumulation) and  v_d  (absorbed V) or
+ *     v_d R_V[k]  (fp32 accumulation, v_absorbed = 0), each
  *     clipped to +-tau[k] and quantized with bf16 scale = bf16((max-min)/3)
  *     (1 if max = min) and zero = bf16(-min/scale), code =
  *     clamp(rne(c/scale + zero), 0, 3), into INT2 history slot d - S0.
  * seq_lens is not advanced; the caller owns lengths.  r_k: fp32 [Hkv][D][D];
- * r_v must be NULL (absorbed V); tau_k, tau_v: fp32 [Hkv] (+inf disables).
+ * r_v: fp32 [Hkv][D][D] when v_absorbed = 0, NULL otherwise (either
+ * mismatch is OSCAR_ERR_INVALID); tau_k, tau_v: fp32 [Hkv] (+inf disables).
  * Page tables must hold a valid entry for every page written.  Sequences that
  * share a page must not demote into it in the same call. */
 oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const void* k_new, const void* v_new,
@@ -151,7 +157,9 @@ oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const vo
  * query head h:
  *   out[b][h] = softmax_t(sm * q.k_t) . v_t  over all L_b tokens,
  * with history keys k^ = s(code - z) R_K^T (computed as q' = q R_K against
- * the codes) and history values s(code - z).
+ * the codes) and history values s(code - z), times R_V^T when v_absorbed = 0
+ * (applied once per head to the merged history partial; r_v as for
+ * oscar_append_demote).
  * q: bf16 [batch][Hq][D] (model basis); seq_lens: int32 [batch] device, L_b
  * counting the current token, at most max_seq_len (longer lengths are
  * clamped to max_seq_len and to what the page tables can address); out:
@@ -179,9 +187,11 @@ oscar_status oscar_merge(int32_t rows, int32_t head_dim, const int32_t* row_offs
                          const float* lse_partials, void* out, void* stream);
 
 /* Bulk write path (prefill of history): quantizes tokens 0..num_tokens-1 of
- * dense K and V (bf16 [num_tokens][Hkv][D]; V already in the pool's V basis)
- * exactly as oscar_append_demote quantizes one token, with K rotated by R_K
- * on the matrix cores, and writes token t to slot t%16 of INT2 page
+ * dense K and V (bf16 [num_tokens][Hkv][D]; V already in the pool's V basis
+ * when absorbed, else V itself) exactly as oscar_append_demote quantizes one
+ * token, with K rotated by R_K (and, v_absorbed = 0, V by R_V; r_v as for
+ * oscar_append_demote) on the matrix cores, and writes token t to slot t%16
+ * of INT2 page
  * page_ids[t/16] (int32 device [ceil(num_tokens/16)]).  Pages are written
  * whole; token slots past num_tokens in the last page are zero-filled. */
 oscar_status oscar_quantize_pack(const oscar_pool* pool, int32_t num_tokens, const void* k, const void* v,

@@ -930,26 +930,27 @@ __global__ void __launch_bounds__(kThreads)
   __syncthreads();
   if (!sm.last) return;
   const size_t p0 = head_base * U * GQA;
-  // thread (h, c) folds the partials of head h in batches of 32, loading a
-  // batch's lse and o values together (one memory round trip per batch)
-  for (int idx = tid; idx < GQA * D; idx += kThreads) {
-    const int h = idx / D, c = idx % D;
+  // Folds partials u0 .. u1-1 of head h, channel c into (M, S, A): the log2
+  // max, the sum of weights and the weighted sum of normalized outputs, in
+  // batches of 32 (one memory round trip per batch; indices past the range
+  // re-read its last partial, in bounds and without branches, with weight 0).
+  auto fold = [&](int h, int c, int u0, int u1, float& M, float& S, float& A) {
     const float* lsrc = p.part_lse + p0 + h;        // partial u at lsrc[u * GQA]
     const float* osrc = p.part_o + (p0 + h) * D + c;  // partial u at osrc[u * GQA * D]
-    float M = -INFINITY, S = 0.f, A = 0.f;
-    for (int u0 = 0; u0 < total; u0 += 32) {
+    M = -INFINITY;
+    S = 0.f;
+    A = 0.f;
+    for (int ub = u0; ub < u1; ub += 32) {
       float e[32], v[32];
-      // indices past the last partial re-read the last one (in bounds, no
-      // branches) and are then given weight zero
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
-        const int uu = min(u0 + k, total - 1);
+        const int uu = min(ub + k, u1 - 1);
         e[k] = lsrc[(size_t)uu * GQA];
         v[k] = osrc[(size_t)uu * GQA * D];
       }
 #pragma unroll
       for (int k = 0; k < 32; ++k)
-        if (u0 + k >= total) e[k] = -INFINITY;
+        if (ub + k >= u1) e[k] = -INFINITY;
       float mb = M;
 #pragma unroll
       for (int k = 0; k < 32; ++k) mb = fmaxf(mb, e[k]);
@@ -966,7 +967,59 @@ __global__ void __launch_bounds__(kThreads)
         M = mb;
       }
     }
-    p.out[((size_t)b * hq + kvh * GQA + h) * D + c] = (uint16_t)f32_to_bf16(S > 0.f ? A / S : 0.f);
+  };
+  uint16_t* outp = p.out + ((size_t)b * hq + kvh * GQA) * D;
+  if (BF16_ONLY || p.r_v == nullptr) {
+    for (int idx = tid; idx < GQA * D; idx += kThreads) {
+      const int h = idx / D, c = idx % D;
+      float M, S, A;
+      fold(h, c, 0, total, M, S, A);
+      outp[h * D + c] = (uint16_t)f32_to_bf16(S > 0.f ? A / S : 0.f);
+    }
+  } else {
+    // Values not absorbed: the INT2 partials hold V R_V.  Their merge is
+    // rotated back by R_V^T (linear, so once per head after the merge) and
+    // then merged with the BF16 units' partials, which hold V itself.
+    constexpr int PER = (GQA * D + kThreads - 1) / kThreads;
+    float M1[PER], S1[PER], A1[PER], M2[PER], S2[PER];
+    float* a2 = &sm.u.part[0][0][0];  // [GQA][D] INT2 merge, rotated basis
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = tid + k * kThreads;
+      if (idx < GQA * D) {
+        const int h = idx / D, c = idx % D;
+        float A2;
+        fold(h, c, 0, p.n_bf16_units, M1[k], S1[k], A1[k]);
+        fold(h, c, p.n_bf16_units, total, M2[k], S2[k], A2);
+        a2[h * D + c] = A2;
+      }
+    }
+    __syncthreads();
+    const float* rv = p.r_v + (size_t)kvh * D * D;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = tid + k * kThreads;
+      if (idx < GQA * D) {
+        const int h = idx / D, c = idx % D;
+        // (A2 R_V^T)[c] = sum_j A2[j] R_V[c][j]
+        const float4* row = (const float4*)(rv + (size_t)c * D);
+        const float4* a = (const float4*)(a2 + h * D);
+        float acc = 0.f;
+#pragma unroll 8
+        for (int j = 0; j < D / 4; ++j) {
+          const float4 r4 = row[j], x4 = a[j];
+          acc = fmaf(x4.x, r4.x, fmaf(x4.y, r4.y, fmaf(x4.z, r4.z, fmaf(x4.w, r4.w, acc))));
+        }
+        const float M = fmaxf(M1[k], M2[k]);
+        float o = 0.f;
+        if (M > -INFINITY) {
+          const float w1 = __builtin_amdgcn_exp2f(M1[k] - M), w2 = __builtin_amdgcn_exp2f(M2[k] - M);
+          const float Sx = w1 * S1[k] + w2 * S2[k];
+          o = Sx > 0.f ? (w1 * A1[k] + w2 * acc) / Sx : 0.f;
+        }
+        outp[h * D + c] = (uint16_t)f32_to_bf16(o);
+      }
+    }
   }
   if (tid == 0)
     __hip_atomic_store(p.counters + head_base * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -17,6 +17,7 @@ struct DecodeParams {
   const uint8_t* bf16_pool;
   const uint8_t* int2_pool;
   const float* r_k;          // [Hkv][D][D]
+  const float* r_v;          // [Hkv][D][D], or null when V is absorbed
   uint16_t* out;             // [B][Hq][D] bf16
   uint32_t* counters;        // [B][Hkv], kCounterStride words apart
   float* part_lse;           // [B][Hkv][U][GQA] log2 of the partial's softmax sum
@@ -64,6 +65,7 @@ struct WriteParams {
   int32_t pages_per_block;
   // common
   const float* r_k;          // [Hkv][D][D]
+  const float* r_v;          // [Hkv][D][D], or null when V is absorbed
   const float* tau_k;        // [Hkv]
   const float* tau_v;
   int32_t batch, num_kv_heads, sink, recent;

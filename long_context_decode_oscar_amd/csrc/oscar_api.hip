@@ -172,7 +172,7 @@ oscar_status oscar_pool_create(const oscar_config* cfg, oscar_pool** out, oscar_
   if (c.head_dim != 64 && c.head_dim != 128) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c.group_size != 64 && c.group_size != 128) return fail(OSCAR_ERR_UNSUPPORTED, "group_size must be 64 or 128");
   if (gqa != 2 && gqa != 4 && gqa != 8) return fail(OSCAR_ERR_UNSUPPORTED, "num_q_heads/num_kv_heads must be 2, 4 or 8");
-  if (c.v_absorbed != 1) return fail(OSCAR_ERR_UNSUPPORTED, "only v_absorbed = 1 is implemented");
+  if (c.v_absorbed != 0 && c.v_absorbed != 1) return fail(OSCAR_ERR_INVALID, "v_absorbed must be 0 or 1");
   oscar_pool* p = new (std::nothrow) oscar_pool;
   if (!p) return fail(OSCAR_ERR_INVALID, "out of host memory");
   p->cfg = c;
@@ -225,9 +225,10 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
   if (batch == 0) return ok();
   if (!q || !seq_lens || !bf16_pool || !int2_pool || !r_k || !out)
     return fail(OSCAR_ERR_INVALID, "q, seq_lens, pools, r_k and out must be non-null");
-  if (r_v) return fail(OSCAR_ERR_UNSUPPORTED, "r_v must be NULL: values are stored in the absorbed V basis");
-  if (!aligned16(q) || !aligned16(bf16_pool) || !aligned16(int2_pool) || !aligned16(r_k))
-    return fail(OSCAR_ERR_INVALID, "q, pools and r_k must be 16-byte aligned");
+  if (pool->cfg.v_absorbed && r_v) return fail(OSCAR_ERR_INVALID, "r_v must be NULL when V is absorbed");
+  if (!pool->cfg.v_absorbed && !r_v) return fail(OSCAR_ERR_INVALID, "r_v is required when V is not absorbed");
+  if (!aligned16(q) || !aligned16(bf16_pool) || !aligned16(int2_pool) || !aligned16(r_k) || !aligned16(r_v))
+    return fail(OSCAR_ERR_INVALID, "q, pools, r_k and r_v must be 16-byte aligned");
   oscar_status st = check_tables(bf16_page_table, bf16_pt_stride, bf16_num_pages, int2_page_table, int2_pt_stride,
                                  int2_num_pages, true);
   if (st != OSCAR_OK) return st;
@@ -244,6 +245,7 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
   p.bf16_pool = (const uint8_t*)bf16_pool;
   p.int2_pool = (const uint8_t*)int2_pool;
   p.r_k = r_k;
+  p.r_v = r_v;
   p.out = (uint16_t*)out;
   p.counters = (uint32_t*)((char*)workspace + pl.off_counters);
   p.part_lse = (float*)((char*)workspace + pl.off_lse);
@@ -336,9 +338,10 @@ oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const vo
   if (batch == 0) return ok();
   if (!k_new || !v_new || !seq_lens || !bf16_pool || !int2_pool || !r_k || !tau_k || !tau_v)
     return fail(OSCAR_ERR_INVALID, "k_new, v_new, seq_lens, pools, r_k, tau_k and tau_v must be non-null");
-  if (r_v) return fail(OSCAR_ERR_UNSUPPORTED, "r_v must be NULL: values are stored in the absorbed V basis");
-  if (!aligned16(r_k) || !aligned16(bf16_pool) || !aligned16(int2_pool))
-    return fail(OSCAR_ERR_INVALID, "pools and r_k must be 16-byte aligned");
+  if (pool->cfg.v_absorbed && r_v) return fail(OSCAR_ERR_INVALID, "r_v must be NULL when V is absorbed");
+  if (!pool->cfg.v_absorbed && !r_v) return fail(OSCAR_ERR_INVALID, "r_v is required when V is not absorbed");
+  if (!aligned16(r_k) || !aligned16(r_v) || !aligned16(bf16_pool) || !aligned16(int2_pool))
+    return fail(OSCAR_ERR_INVALID, "pools, r_k and r_v must be 16-byte aligned");
   oscar_status st = check_tables(bf16_page_table, bf16_pt_stride, bf16_num_pages, int2_page_table, int2_pt_stride,
                                  int2_num_pages, true);
   if (st != OSCAR_OK) return st;
@@ -356,6 +359,7 @@ oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const vo
   p.int2_pt_stride = int2_pt_stride;
   p.int2_num_pages = int2_num_pages;
   p.r_k = r_k;
+  p.r_v = r_v;
   p.tau_k = tau_k;
   p.tau_v = tau_v;
   p.batch = batch;
@@ -376,9 +380,10 @@ oscar_status oscar_quantize_pack(const oscar_pool* pool, int32_t num_tokens, con
   if (num_tokens == 0) return ok();
   if (!k || !v || !page_ids || !int2_pool || !r_k || !tau_k || !tau_v || int2_num_pages <= 0)
     return fail(OSCAR_ERR_INVALID, "k, v, page_ids, int2_pool, r_k, tau_k, tau_v and int2_num_pages must be given");
-  if (r_v) return fail(OSCAR_ERR_UNSUPPORTED, "r_v must be NULL: values are stored in the absorbed V basis");
-  if (!aligned16(k) || !aligned16(v) || !aligned16(int2_pool) || !aligned16(r_k))
-    return fail(OSCAR_ERR_INVALID, "k, v, int2_pool and r_k must be 16-byte aligned");
+  if (pool->cfg.v_absorbed && r_v) return fail(OSCAR_ERR_INVALID, "r_v must be NULL when V is absorbed");
+  if (!pool->cfg.v_absorbed && !r_v) return fail(OSCAR_ERR_INVALID, "r_v is required when V is not absorbed");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(int2_pool) || !aligned16(r_k) || !aligned16(r_v))
+    return fail(OSCAR_ERR_INVALID, "k, v, int2_pool, r_k and r_v must be 16-byte aligned");
   const oscar_config& c = pool->cfg;
   oscar::WriteParams p{};
   p.k = (const uint16_t*)k;
@@ -396,6 +401,7 @@ oscar_status oscar_quantize_pack(const oscar_pool* pool, int32_t num_tokens, con
     if (p.pages_per_block < 8) p.pages_per_block = 8;
   }
   p.r_k = r_k;
+  p.r_v = r_v;
   p.tau_k = tau_k;
   p.tau_v = tau_v;
   p.num_kv_heads = c.num_kv_heads;

@@ -54,27 +54,46 @@ __device__ __forceinline__ uint32_t quant_code(float c, float s, float z) {
 }
 
 // ------------------------------------------------------- append + demote --
-template <int D, int NG>
+// One workgroup of 256 threads per (sequence, KV head).  The rotation
+// operands (thread (c, part) holds column c of R over rows part*RP .. +RP,
+// for R_K and, when V is not absorbed, R_V) do not depend on the sequence,
+// so their loads are issued first and overlap the length and page-table
+// reads; the demoted token is read before the appended token is written
+// (the caller may recycle the page of the oldest recent token for the
+// newest one).
+template <int D, int NG, bool VROT>
 __global__ void __launch_bounds__(256) k_append_demote(const WriteParams p) {
   constexpr int G = D / NG;
   constexpr int KW = D / 64;
   constexpr int BLK2 = 8 * D + 128 * NG;
   constexpr int REC = D / 8;
-  __shared__ float r_s[D * D];
+  constexpr int PARTS = 256 / D, RP = D / PARTS;  // row split of the rotation
   __shared__ float kd[D];
-  __shared__ float vv[D];
-  __shared__ float yk[2][D];
+  __shared__ float vd[D];
+  __shared__ float yp[2][PARTS][D];    // [K/V][part] partial rotations
   __shared__ float red[2][D / 64][2];  // [K/V][64-channel block][min, max]
   __shared__ uint8_t codes[2][D];
   __shared__ uint32_t sz[2][NG];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int b = blockIdx.x / p.num_kv_heads, kvh = blockIdx.x % p.num_kv_heads;
+  const size_t hb = (size_t)kvh;
+  const int c = tid % D, part = tid / D;
+  float rk[RP], rv[VROT ? RP : 1];
+  {
+    const float* src = p.r_k + hb * D * D + (size_t)(part * RP) * D + c;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) rk[i] = src[(size_t)i * D];
+    if constexpr (VROT) {
+      const float* srv = p.r_v + hb * D * D + (size_t)(part * RP) * D + c;
+#pragma unroll
+      for (int i = 0; i < RP; ++i) rv[i] = srv[(size_t)i * D];
+    }
+  }
   const int L = p.seq_lens[b];
   if (L < 0) return;
   const int32_t* bpt = p.bf16_pt + (size_t)b * p.bf16_pt_stride;
   const int32_t* ipt = p.int2_pt + (size_t)b * p.int2_pt_stride;
-  const size_t hb = (size_t)kvh;
 
   // appended token goes to position L
   int aid = -1;
@@ -90,46 +109,59 @@ __global__ void __launch_bounds__(256) k_append_demote(const WriteParams p) {
     if (hs / kPage < p.int2_pt_stride) iid = ipt[hs / kPage];
     dem = did >= 0 && did < p.bf16_num_pages && iid >= 0 && iid < p.int2_num_pages;
   }
-  if (dem) {
-    const uint8_t* blk = p.bf16_pool + ((size_t)did * p.num_kv_heads + hb) * (64 * D);
-    const int slot = d % kPage;
-    if (tid < D) {
-      kd[tid] = bf16_to_f32(((const uint16_t*)blk)[slot * D + tid]);
-      vv[tid] = bf16_to_f32(((const uint16_t*)(blk + 32 * D))[(slot / 4) * D * 4 + tid * 4 + (slot % 4)]);
-    }
-    const uint4* rsrc = (const uint4*)(p.r_k + hb * D * D);
-    for (int i = tid; i < D * D / 4; i += 256) ((uint4*)r_s)[i] = rsrc[i];
+  uint8_t* blk = p.int2_pool + ((size_t)max(iid, 0) * p.num_kv_heads + hb) * BLK2;
+  const int slot = hs % kPage, jq = slot / 4, ti = slot % 4;
+  // V record words hold four tokens: read the word this token goes into now
+  uint32_t vold = 0;
+  const bool v_thread = tid >= 64 && tid < 64 + 16 * KW;
+  uint32_t* vdst = (uint32_t*)(blk + (16 * jq + (tid - 64) / KW) * REC + D / 16 + 4 * ((tid - 64) % KW));
+  if (dem && v_thread && ti != 0) vold = *vdst;
+  if (dem && tid < D) {
+    const uint8_t* bb = p.bf16_pool + ((size_t)did * p.num_kv_heads + hb) * (64 * D);
+    const int sl = d % kPage;
+    kd[tid] = bf16_to_f32(((const uint16_t*)bb)[sl * D + tid]);
+    vd[tid] = bf16_to_f32(((const uint16_t*)(bb + 32 * D))[(sl / 4) * D * 4 + tid * 4 + (sl % 4)]);
   }
-  __syncthreads();  // the demoted token is read before the append writes
+  __syncthreads();  // the demoted token is in LDS before the append writes
   if (app && tid < D) {
-    uint8_t* blk = p.bf16_pool + ((size_t)aid * p.num_kv_heads + hb) * (64 * D);
-    const int slot = L % kPage;
+    uint8_t* bb = p.bf16_pool + ((size_t)aid * p.num_kv_heads + hb) * (64 * D);
+    const int sl = L % kPage;
     const size_t src = ((size_t)b * p.num_kv_heads + hb) * D + tid;
-    ((uint16_t*)blk)[slot * D + tid] = p.k_new[src];
-    ((uint16_t*)(blk + 32 * D))[(slot / 4) * D * 4 + tid * 4 + (slot % 4)] = p.v_new[src];
+    ((uint16_t*)bb)[sl * D + tid] = p.k_new[src];
+    ((uint16_t*)(bb + 32 * D))[(sl / 4) * D * 4 + tid * 4 + (sl % 4)] = p.v_new[src];
   }
   if (!dem) return;
 
-  // y = k_d R_K: thread (c, half) sums half of the input channels (fp32 FMA)
-  if (tid < 2 * D) {
-    const int c = tid % D, hlf = tid / D;
+  // y = k_d R_K (and v_d R_V): thread (c, part) sums rows part*RP .. +RP (fp32 FMA)
+  {
     float acc = 0.f;
-    const int i0 = hlf * (D / 2);
-#pragma unroll 8
-    for (int i = i0; i < i0 + D / 2; ++i) acc = fmaf(kd[i], r_s[i * D + c], acc);
-    yk[hlf][c] = acc;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) acc = fmaf(kd[part * RP + i], rk[i], acc);
+    yp[0][part][c] = acc;
+    if constexpr (VROT) {
+      float av = 0.f;
+#pragma unroll
+      for (int i = 0; i < RP; ++i) av = fmaf(vd[part * RP + i], rv[i], av);
+      yp[1][part][c] = av;
+    }
   }
   __syncthreads();
-  // waves: channels c of K (which = 0) or V (which = 1); each 64-lane wave
-  // lies inside one group because G >= 64
-  const int which = tid / D, c = tid % D;
+  // quantization: threads (which, c), which = 0 for K and 1 for V; every
+  // 64-lane wave lies inside one group because G >= 64
+  const int which = tid / D;
   float x = 0.f;
   if (which < 2) {
-    x = which == 0 ? yk[0][c] + yk[1][c] : vv[c];
+    if (which == 0 || VROT) {
+      x = 0.f;
+#pragma unroll
+      for (int q = 0; q < PARTS; ++q) x += yp[which][q][c];
+    } else {
+      x = vd[c];
+    }
     const float tau = which == 0 ? p.tau_k[hb] : p.tau_v[hb];
     x = fminf(fmaxf(x, -tau), tau);
     const float mn = wmin(x), mx = wmax(x);
-    if (lane == 0) {
+    if ((tid & 63) == 0) {
       red[which][c / 64][0] = mn;
       red[which][c / 64][1] = mx;
     }
@@ -151,24 +183,21 @@ __global__ void __launch_bounds__(256) k_append_demote(const WriteParams p) {
   }
   __syncthreads();
   // pack into INT2 page iid, slot hs % 16
-  uint8_t* blk = p.int2_pool + ((size_t)iid * p.num_kv_heads + hb) * BLK2;
-  const int slot = hs % kPage, jq = slot / 4, ti = slot % 4;
   if (tid < 4 * KW) {  // K: records (j, slot), word w
     const int jj = tid / KW, w = tid % KW;
     uint32_t word = 0;
 #pragma unroll
     for (int m = 0; m < 16; ++m) word |= (uint32_t)codes[0][w * 64 + jj * 16 + m] << (2 * m);
     *(uint32_t*)(blk + (16 * jj + slot) * REC + 4 * w) = word;
-  } else if (tid >= 64 && tid < 64 + 16 * KW) {  // V: records (jq, r), word w
+  } else if (v_thread) {  // V: records (jq, r), word w
     const int r = (tid - 64) / KW, w = (tid - 64) % KW;
-    uint32_t* dst = (uint32_t*)(blk + (16 * jq + r) * REC + D / 16 + 4 * w);
-    uint32_t word = ti == 0 ? 0u : *dst;  // first token of a quad starts the word
+    uint32_t word = vold;  // the first token of a quad starts the word (vold = 0)
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
       const int pos = 16 * (ti & 1) + 2 * (2 * bb + (ti >> 1));
       word = (word & ~(3u << pos)) | ((uint32_t)codes[1][(4 * w + bb) * 16 + r] << pos);
     }
-    *dst = word;
+    *vdst = word;
   } else if (tid >= 128 && tid < 128 + 2 * NG) {  // scale/zero words
     const int wh = (tid - 128) / NG, g = (tid - 128) % NG;
     *(uint32_t*)(blk + 8 * D + jq * 32 * NG + wh * 16 * NG + (ti * NG + g) * 4) = sz[wh][g];
@@ -184,12 +213,17 @@ __global__ void __launch_bounds__(256) k_append_demote(const WriteParams p) {
 #define OSCAR_QP_WAVES 16
 #endif
 constexpr int kQpWaves = OSCAR_QP_WAVES;
-constexpr int kQpThreads = 64 * kQpWaves;
+// with V rotated on the matrix cores too, R_V takes another 64 KiB of LDS
+constexpr int kQpWavesVrot = 8;
+template <bool VROT>
+constexpr int qp_waves() { return VROT ? kQpWavesVrot : kQpWaves; }
 
-template <int D, int NG>
+template <int D, int NG, bool VROT>
 struct BulkSmem {
-  uint4 rb[2][D / 16][D / 32][64];  // R_hi / R_lo as MFMA A operands, output channels permuted
-  uint8_t vcode[kQpWaves][kPage][D];  // per wave: V codes, one byte each
+  static constexpr int W = qp_waves<VROT>();
+  uint4 rb[2][D / 16][D / 32][64];              // R_K hi / lo as MFMA A operands, output channels permuted
+  uint4 rbv[VROT ? 2 : 1][D / 16][D / 32][VROT ? 64 : 1];  // R_V the same way (rotated V only)
+  uint8_t vcode[W][kPage][D];                   // per wave: V codes, one byte each
 };
 
 // min / max over the 4 lanes of a quad (lanes 4t .. 4t+3)
@@ -304,10 +338,11 @@ __device__ __forceinline__ uint32_t group_codes(const float (&x)[N], float mn, f
   return sb | (zb << 16);
 }
 
-template <int D, int NG>
+template <int D, int NG, bool VROT>
 struct BulkPage {  // one page's global inputs, as loaded
   uint4 ka[D / 32];          // K as MFMA B operands: token r, channels j*D/4 + ks*8 + e
-  uint4 va[D / 64][2];       // V of token t, channels w*64 + qq*16 + 0..15
+  // V: rotated -> the same layout as K; else token t, channels w*64 + qq*16 + 0..15
+  uint4 va[VROT ? D / 32 : D / 64 * 2];
   int id;                    // physical page (-1: none)
 };
 
@@ -326,8 +361,8 @@ __device__ __forceinline__ void* uniform_ptr(const void* q) {
 // per page, based at its first token, bounds the loads: slots past the last
 // token, and every slot of a page without a physical id, read as zero, with
 // no branch around the loads.
-template <int D, int NG>
-__device__ __forceinline__ void bulk_load(BulkPage<D, NG>& pg, const WriteParams& p, int kvh, int page, int id,
+template <int D, int NG, bool VROT>
+__device__ __forceinline__ void bulk_load(BulkPage<D, NG, VROT>& pg, const WriteParams& p, int kvh, int page, int id,
                                           int lane) {
   constexpr int KB = D / 32, KW = D / 64;
   pg.id = id;
@@ -347,19 +382,77 @@ __device__ __forceinline__ void bulk_load(BulkPage<D, NG>& pg, const WriteParams
     const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, r * row + j * (D / 2) + ks * 16, 0, 0);
     pg.ka[ks] = uint4{x[0], x[1], x[2], x[3]};
   }
+  if constexpr (VROT) {
 #pragma unroll
-  for (int w = 0; w < KW; ++w) {
-    const auto x0 = __builtin_amdgcn_raw_buffer_load_b128(rv, t * row + w * 128 + qq * 32, 0, 0);
-    const auto x1 = __builtin_amdgcn_raw_buffer_load_b128(rv, t * row + w * 128 + qq * 32 + 16, 0, 0);
-    pg.va[w][0] = uint4{x0[0], x0[1], x0[2], x0[3]};
-    pg.va[w][1] = uint4{x1[0], x1[1], x1[2], x1[3]};
+    for (int ks = 0; ks < KB; ++ks) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rv, r * row + j * (D / 2) + ks * 16, 0, 0);
+      pg.va[ks] = uint4{x[0], x[1], x[2], x[3]};
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+      const auto x0 = __builtin_amdgcn_raw_buffer_load_b128(rv, t * row + w * 128 + qq * 32, 0, 0);
+      const auto x1 = __builtin_amdgcn_raw_buffer_load_b128(rv, t * row + w * 128 + qq * 32 + 16, 0, 0);
+      pg.va[2 * w] = uint4{x0[0], x0[1], x0[2], x0[3]};
+      pg.va[2 * w + 1] = uint4{x1[0], x1[1], x1[2], x1[3]};
+    }
   }
 }
 
-template <int D, int NG>
-__device__ __forceinline__ void bulk_page(const BulkPage<D, NG>& pg, const WriteParams& p, BulkSmem<D, NG>& sm,
-                                          int kvh, int page, int wave, int lane, float tau_k, float tau_v) {
-  constexpr int KW = D / 64, KB = D / 32, OT = D / 16;
+// Y^T = R^T X^T for one page on the bf16 matrix cores (R split hi + lo).  The
+// A operands hold R's columns in the order that gives lane (j, r) token r's
+// channels w*64 + j*16 + 4q + i in y[4w + q][i].
+template <int D>
+__device__ __forceinline__ void rotate_page(const uint4 (&xb)[D / 32], const uint4 (*rb)[D / 16][D / 32][64],
+                                            int lane, float (&y)[D / 16][4]) {
+  constexpr int KB = D / 32, OT = D / 16;
+#pragma unroll
+  for (int ot = 0; ot < OT; ++ot) {
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KB; ++ks) {
+      const v8bf b = __builtin_bit_cast(v8bf, xb[ks]);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rb[0][ot][ks][lane]), b, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rb[1][ot][ks][lane]), b, c, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[ot][i] = c[i];
+  }
+}
+
+// Clip and quantize one rotated page in the rotate_page layout (the token's
+// other channels sit in lanes r + 16, r + 32, r + 48).  CHANNEL_ORDER false:
+// words[w][i] holds, in byte q, the code of channel w*64 + j*16 + 4q + i;
+// true: words[w][q] holds, in byte i, that same code (channel order).  The
+// group scale words are returned in sz.
+template <int D, int NG, bool CHANNEL_ORDER>
+__device__ __forceinline__ void quant_rotated(const float (&y)[D / 16][4], float tau, uint32_t (&words)[D / 64][4],
+                                              uint32_t (&sz)[NG]) {
+  constexpr int KW = D / 64, WPG = KW / NG;  // record words per group
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float x[WPG * 16];
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < WPG * 16; ++u) {
+      const int w = g * WPG + u / 16;
+      const int i = CHANNEL_ORDER ? u % 4 : (u / 4) % 4, q = CHANNEL_ORDER ? (u / 4) % 4 : u % 4;
+      x[u] = __builtin_amdgcn_fmed3f(y[4 * w + q][i], -tau, tau);
+      mn = fminf(mn, x[u]);
+      mx = fmaxf(mx, x[u]);
+    }
+    uint32_t ww[WPG * 4];
+    sz[g] = group_codes<WPG * 16>(x, col4_min(mn), col4_max(mx), ww);
+#pragma unroll
+    for (int u = 0; u < WPG * 4; ++u) words[g * WPG + u / 4][u % 4] = ww[u];
+  }
+}
+
+template <int D, int NG, bool VROT>
+__device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const WriteParams& p,
+                                          BulkSmem<D, NG, VROT>& sm, int kvh, int page, int wave, int lane,
+                                          float tau_k, float tau_v) {
+  constexpr int KW = D / 64, OT = D / 16;
   constexpr int BLK2 = 8 * D + 128 * NG;
   constexpr int REC = D / 8;
   const int j = lane >> 4, r = lane & 15, t = lane >> 2, qq = lane & 3;
@@ -373,63 +466,52 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG>& pg, const Write
       pg.id >= 0 ? BLK2 : 0, kBufferFlags);
   constexpr int kDrop = 1 << 20;  // an offset past every block
   const int sc0 = 8 * D;          // scale words: 8*NG per token quad
-  // ---- keys: Y^T = R_K^T K^T on the bf16 matrix cores (R split hi + lo).
-  // The A operands hold R's columns in the order that gives lane (j, r)
-  // token r's channels w*64 + j*16 + 4q + i in y[4w + q][i]: the channels of
-  // the lane's own code record (j, r), word w.
+  // ---- keys: rotated on the matrix cores; each lane then holds the channels
+  // of its own code record (j, r), word w
   uint32_t kwd[KW];
   {
     float y[OT][4];
-#pragma unroll
-    for (int ot = 0; ot < OT; ++ot) {
-      v4f c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KB; ++ks) {
-        const v8bf b = __builtin_bit_cast(v8bf, pg.ka[ks]);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sm.rb[0][ot][ks][lane]), b, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sm.rb[1][ot][ks][lane]), b, c, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[ot][i] = c[i];
-    }
+    rotate_page<D>(pg.ka, sm.rb, lane, y);
     const bool tok_ok = pg.id >= 0 && tok0 + r < p.num_tokens;
-    // x[(w' * 4 + i) * 4 + q] = y[4w + q][i], w' the word inside the group:
-    // the group's codes come back as words (w', i) holding bytes q
-    constexpr int WPG = KW / NG;  // record words per group
+    uint32_t words[KW][4], sz[NG];
+    quant_rotated<D, NG, false>(y, tau_k, words, sz);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      float x[WPG * 16];
-      float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < WPG * 16; ++u) {
-        const int w = g * WPG + u / 16, i = (u / 4) % 4, q = u % 4;
-        x[u] = __builtin_amdgcn_fmed3f(y[4 * w + q][i], -tau_k, tau_k);
-        mn = fminf(mn, x[u]);
-        mx = fmaxf(mx, x[u]);
-      }
-      uint32_t words[WPG * 4];
-      const uint32_t sz = group_codes<WPG * 16>(x, col4_min(mn), col4_max(mx), words);
-#pragma unroll
-      for (int wp = 0; wp < WPG; ++wp) {
-        // byte q of word i holds code m = 4q + i at bits 8q; shifted by 2i
-        const uint32_t* d = &words[wp * 4];
-        const uint32_t word = d[0] | (d[1] << 2) | (d[2] << 4) | (d[3] << 6);
-        kwd[g * WPG + wp] = tok_ok ? word : 0u;
-      }
-      // scales of token r (zeros for slots past the last token)
-      __builtin_amdgcn_raw_buffer_store_b32(tok_ok ? sz : 0u, out,
-                                            j == g ? sc0 + 4 * ((r / 4) * 8 * NG + (r % 4) * NG + g) : kDrop, 0, 0);
+    for (int w = 0; w < KW; ++w) {
+      // byte q of word i holds code m = 4q + i at bits 8q; shifted by 2i
+      const uint32_t word = words[w][0] | (words[w][1] << 2) | (words[w][2] << 4) | (words[w][3] << 6);
+      kwd[w] = tok_ok ? word : 0u;
     }
+    // scales of token r (zeros for slots past the last token)
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      __builtin_amdgcn_raw_buffer_store_b32(tok_ok ? sz[g] : 0u, out,
+                                            j == g ? sc0 + 4 * ((r / 4) * 8 * NG + (r % 4) * NG + g) : kDrop, 0, 0);
   }
-  // ---- values (already rotated), lane = 4t + qq: channels w*64 + qq*16 + m
-  {
+  if constexpr (VROT) {
+    // ---- values rotated by R_V the same way; their codes go to LDS in
+    // channel order for the record transposition below
+    float y[OT][4];
+    rotate_page<D>(pg.va, sm.rbv, lane, y);
+    const bool tok_ok = pg.id >= 0 && tok0 + r < p.num_tokens;
+    uint32_t words[KW][4], sz[NG];
+    quant_rotated<D, NG, true>(y, tau_v, words, sz);
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      __builtin_amdgcn_raw_buffer_store_b32(
+          tok_ok ? sz[g] : 0u, out, j == g ? sc0 + 4 * ((r / 4) * 8 * NG + 4 * NG + (r % 4) * NG + g) : kDrop, 0, 0);
+#pragma unroll
+    for (int w = 0; w < KW; ++w)
+      *(uint4*)&vcode[r][w * 64 + j * 16] =
+          tok_ok ? uint4{words[w][0], words[w][1], words[w][2], words[w][3]} : uint4{0u, 0u, 0u, 0u};
+  } else {
+    // ---- values (already rotated), lane = 4t + qq: channels w*64 + qq*16 + m
     const bool tok_ok = pg.id >= 0 && tok0 + t < p.num_tokens;
     float x[KW][16];
     float mn[KW], mx[KW];
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
-      const uint32_t xs[8] = {pg.va[w][0].x, pg.va[w][0].y, pg.va[w][0].z, pg.va[w][0].w,
-                              pg.va[w][1].x, pg.va[w][1].y, pg.va[w][1].z, pg.va[w][1].w};
+      const uint4 a0 = pg.va[2 * w], a1 = pg.va[2 * w + 1];
+      const uint32_t xs[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       mn[w] = INFINITY;
       mx[w] = -INFINITY;
 #pragma unroll
@@ -500,60 +582,64 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG>& pg, const Write
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int NG>
-__global__ void __launch_bounds__(kQpThreads) k_quantize_pack(const WriteParams p) {
+// R (fp32) -> R_hi + R_lo (bf16) in A-operand order:
+// rb[hl][ot][ks][lane (j, n)] element e = R[j*D/4 + ks*8 + e][pi(ot, n)],
+// pi(ot, 4a + i) = (ot / 4)*64 + a*16 + (ot % 4)*4 + i, so that output row
+// 4a + i of tile ot is that output channel
+template <int D, int THREADS>
+__device__ __forceinline__ void split_rotation(const float* __restrict__ r, uint4 (*rb)[D / 16][D / 32][64], int tid) {
   constexpr int KB = D / 32;
-  __shared__ BulkSmem<D, NG> sm;
+  for (int idx = tid; idx < D * D / 8; idx += THREADS) {
+    const int lane_op = idx % 64, ks = (idx / 64) % KB, ot = idx / (64 * KB);
+    const int j = lane_op >> 4, n = lane_op & 15;
+    const int in0 = j * (D / 4) + ks * 8, out = (ot / 4) * 64 + (n / 4) * 16 + (ot % 4) * 4 + n % 4;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = r[(size_t)(in0 + 2 * e) * D + out], x1 = r[(size_t)(in0 + 2 * e + 1) * D + out];
+      hi[e] = pack_bf16x2(x0, x1);
+      lo[e] = pack_bf16x2(x0 - bf16_lo(hi[e]), x1 - bf16_hi(hi[e]));
+    }
+    rb[0][ot][ks][lane_op] = uint4{hi[0], hi[1], hi[2], hi[3]};
+    rb[1][ot][ks][lane_op] = uint4{lo[0], lo[1], lo[2], lo[3]};
+  }
+}
+
+template <int D, int NG, bool VROT>
+__global__ void __launch_bounds__(64 * qp_waves<VROT>()) k_quantize_pack(const WriteParams p) {
+  constexpr int W = qp_waves<VROT>(), THREADS = 64 * W;
+  __shared__ BulkSmem<D, NG, VROT> sm;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int kvh = blockIdx.y;
   const int npages = (p.num_tokens + kPage - 1) / kPage;
   const int pg0 = blockIdx.x * p.pages_per_block;
   if (pg0 >= npages) return;
   const int pg_end = min(pg0 + p.pages_per_block, npages);
-  // wave w handles pages pg0 + w + k*kQpWaves, k < my_n (at most 64: the
-  // launch caps pages per workgroup); lane k holds the k-th one's physical id
+  // wave w handles pages pg0 + w + k*W, k < my_n (at most 64: the launch caps
+  // pages per workgroup); lane k holds the k-th one's physical id
   const int first = pg0 + wave;
-  const int my_n = first < pg_end ? (pg_end - first + kQpWaves - 1) / kQpWaves : 0;
+  const int my_n = first < pg_end ? (pg_end - first + W - 1) / W : 0;
   int my_ids = -1;
   if (lane < my_n) {
-    const int id = p.page_ids[first + lane * kQpWaves];
+    const int id = p.page_ids[first + lane * W];
     my_ids = (id >= 0 && id < p.int2_num_pages) ? id : -1;
   }
   auto id_of = [&](int k) { return k < my_n ? __builtin_amdgcn_readlane(my_ids, k) : -1; };
-  BulkPage<D, NG> cur;
-  bulk_load<D, NG>(cur, p, kvh, first, id_of(0), lane);  // first page's loads overlap the R_K split
-  // R_K (fp32) -> R_hi + R_lo (bf16) in A-operand order:
-  // rb[hl][ot][ks][lane (j, n)] element e = R[j*D/4 + ks*8 + e][pi(ot, n)],
-  // pi(ot, 4a + i) = (ot / 4)*64 + a*16 + (ot % 4)*4 + i, so that output row
-  // 4a + i of tile ot is that output channel
-  {
-    const float* rk = p.r_k + (size_t)kvh * D * D;
-    for (int idx = tid; idx < D * D / 8; idx += kQpThreads) {
-      const int lane_op = idx % 64, ks = (idx / 64) % KB, ot = idx / (64 * KB);
-      const int j = lane_op >> 4, n = lane_op & 15;
-      const int in0 = j * (D / 4) + ks * 8, out = (ot / 4) * 64 + (n / 4) * 16 + (ot % 4) * 4 + n % 4;
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = rk[(size_t)(in0 + 2 * e) * D + out], x1 = rk[(size_t)(in0 + 2 * e + 1) * D + out];
-        hi[e] = pack_bf16x2(x0, x1);
-        lo[e] = pack_bf16x2(x0 - bf16_lo(hi[e]), x1 - bf16_hi(hi[e]));
-      }
-      sm.rb[0][ot][ks][lane_op] = uint4{hi[0], hi[1], hi[2], hi[3]};
-      sm.rb[1][ot][ks][lane_op] = uint4{lo[0], lo[1], lo[2], lo[3]};
-    }
-  }
+  BulkPage<D, NG, VROT> cur;
+  bulk_load<D, NG, VROT>(cur, p, kvh, first, id_of(0), lane);  // first page's loads overlap the R split
+  split_rotation<D, THREADS>(p.r_k + (size_t)kvh * D * D, sm.rb, tid);
+  if constexpr (VROT) split_rotation<D, THREADS>(p.r_v + (size_t)kvh * D * D, sm.rbv, tid);
   __syncthreads();
   const float tau_k = p.tau_k[kvh], tau_v = p.tau_v[kvh];
   // two pages per trip so that the current and next page alternate between
   // two register sets
-  BulkPage<D, NG> nxt;
+  BulkPage<D, NG, VROT> nxt;
   for (int k = 0; k < my_n; k += 2) {
-    bulk_load<D, NG>(nxt, p, kvh, first + (k + 1) * kQpWaves, id_of(k + 1), lane);
-    bulk_page<D, NG>(cur, p, sm, kvh, first + k * kQpWaves, wave, lane, tau_k, tau_v);
+    bulk_load<D, NG, VROT>(nxt, p, kvh, first + (k + 1) * W, id_of(k + 1), lane);
+    bulk_page<D, NG, VROT>(cur, p, sm, kvh, first + k * W, wave, lane, tau_k, tau_v);
     if (k + 1 >= my_n) break;
-    bulk_load<D, NG>(cur, p, kvh, first + (k + 2) * kQpWaves, id_of(k + 2), lane);
-    bulk_page<D, NG>(nxt, p, sm, kvh, first + (k + 1) * kQpWaves, wave, lane, tau_k, tau_v);
+    bulk_load<D, NG, VROT>(cur, p, kvh, first + (k + 2) * W, id_of(k + 2), lane);
+    bulk_page<D, NG, VROT>(nxt, p, sm, kvh, first + (k + 1) * W, wave, lane, tau_k, tau_v);
   }
 }
 
@@ -579,16 +665,27 @@ __global__ void __launch_bounds__(256) k_write_bf16(const WriteParams p, int fir
 
 template <int D, int NG>
 void launch_ad(const WriteParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((k_append_demote<D, NG>), dim3(p.batch * p.num_kv_heads), dim3(256), 0, s, p);
+  if (p.r_v)
+    hipLaunchKernelGGL((k_append_demote<D, NG, true>), dim3(p.batch * p.num_kv_heads), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_append_demote<D, NG, false>), dim3(p.batch * p.num_kv_heads), dim3(256), 0, s, p);
+}
+template <int D, int NG, bool VROT>
+void launch_qp_v(const WriteParams& p, hipStream_t s) {
+  constexpr int W = qp_waves<VROT>();
+  const int npages = (p.num_tokens + kPage - 1) / kPage;
+  WriteParams q = p;
+  q.pages_per_block = std::min(std::max(p.pages_per_block, 1), 64 * W);  // <= 64 pages per wave
+  const int gx = (npages + q.pages_per_block - 1) / q.pages_per_block;
+  if (gx == 0) return;
+  hipLaunchKernelGGL((k_quantize_pack<D, NG, VROT>), dim3(gx, p.num_kv_heads), dim3(64 * W), 0, s, q);
 }
 template <int D, int NG>
 void launch_qp(const WriteParams& p, hipStream_t s) {
-  const int npages = (p.num_tokens + kPage - 1) / kPage;
-  WriteParams q = p;
-  q.pages_per_block = std::min(std::max(p.pages_per_block, 1), 64 * kQpWaves);  // <= 64 pages per wave
-  const int gx = (npages + q.pages_per_block - 1) / q.pages_per_block;
-  if (gx == 0) return;
-  hipLaunchKernelGGL((k_quantize_pack<D, NG>), dim3(gx, p.num_kv_heads), dim3(kQpThreads), 0, s, q);
+  if (p.r_v)
+    launch_qp_v<D, NG, true>(p, s);
+  else
+    launch_qp_v<D, NG, false>(p, s);
 }
 
 template <int D>

@@ -31,8 +31,9 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def make_seqs(wl, inputs, r_k=None, tau_k=None, tau_v=None):
-    """Oracle pool state for every sequence of an Inputs draw."""
+def make_seqs(wl, inputs, r_k=None, tau_k=None, tau_v=None, r_v=None):
+    """Oracle pool state for every sequence of an Inputs draw.  With r_v the
+    pool does not absorb V: the history stores V R_V."""
     c = inputs.calib
     r_k = c.r_k if r_k is None else r_k
     tau_k = c.tau_k if tau_k is None else tau_k
@@ -41,15 +42,16 @@ def make_seqs(wl, inputs, r_k=None, tau_k=None, tau_v=None):
     for b, L in enumerate(wl.seq_lens):
         k = inputs.k[b][:L].float().numpy()
         v = inputs.v[b][:L].float().numpy()
-        s = oracle.SeqPool(wl.num_kv_heads, wl.head_dim, wl.group_size, wl.sink, wl.recent)
-        seqs.append(s.prefill(k, v, r_k, tau_k, tau_v))
+        s = oracle.SeqPool(wl.num_kv_heads, wl.head_dim, wl.group_size, wl.sink, wl.recent,
+                           v_absorbed=r_v is None)
+        seqs.append(s.prefill(k, v, r_k, tau_k, tau_v, r_v))
     return seqs
 
 
-def pool_config(wl):
+def pool_config(wl, v_absorbed=True):
     import long_context_decode_oscar_amd as oscar
-    return oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16, wl.sink, wl.recent, 1,
-                            0.0)
+    return oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16, wl.sink, wl.recent,
+                            1 if v_absorbed else 0, 0.0)
 
 
 def to_dev(x, dtype=None):

@@ -30,8 +30,8 @@ CASES = {
 }
 
 
-def _decode(oscar, wl, seqs, q, pools, r_k, max_len=None):
-    pool = oscar.OscarPool(pool_config(wl))
+def _decode(oscar, wl, seqs, q, pools, r_k, max_len=None, r_v=None):
+    pool = oscar.OscarPool(pool_config(wl, v_absorbed=r_v is None))
     dev = upload(pools)
     lens = torch.tensor([s.L for s in seqs], dtype=torch.int32, device="cuda")
     max_len = max_len or max(s.L for s in seqs)
@@ -39,7 +39,7 @@ def _decode(oscar, wl, seqs, q, pools, r_k, max_len=None):
     ws = pool.alloc_workspace(len(seqs), max_len)
     log(f"decode launch: batch={len(seqs)} max_len={max_len}")
     oscar.oscar_decode_attention(pool, q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"], dev["bf16_pool"],
-                                 dev["int2_pool"], to_dev(r_k), out, ws)
+                                 dev["int2_pool"], to_dev(r_k), out, ws, r_v=None if r_v is None else to_dev(r_v))
     torch.cuda.synchronize()
     return out, (pool, dev, lens, ws, max_len)
 
@@ -54,6 +54,20 @@ def test_decode_matches_oracle(gpu_lib, name):
     out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
     ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
     check_decode(out, ref, what=name)
+
+
+@pytest.mark.parametrize("name", ["d64-gqa2-boundary-lengths", "d128-gqa4-ragged", "d128-g64-gqa8"])
+def test_decode_values_not_absorbed(gpu_lib, name):
+    """v_absorbed = 0: the BF16 segments hold V, the history V R_V; decode
+    rotates the merged history partial back by R_V^T."""
+    wl = CASES[name]
+    inp = draw_inputs(wl)
+    r_v = inp.calib.r_v
+    seqs = make_seqs(wl, inp, r_v=r_v)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k, r_v=r_v)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k, r_v)
+    check_decode(out, ref, what=f"{name} (V not absorbed)")
 
 
 def test_decode_deterministic_and_workspace_reusable(gpu_lib):

@@ -28,19 +28,19 @@ def _identity(hkv, d):
     return np.stack([np.eye(d, dtype=np.float32)] * hkv)
 
 
-def _bulk(oscar, wl, k, v, r_k, tau_k, tau_v, seed=0):
+def _bulk(oscar, wl, k, v, r_k, tau_k, tau_v, seed=0, r_v=None):
     """Quantize dense k, v [T, Hkv, D] into fresh random pages; returns the
-    logical history read back per head."""
+    logical history read back per head.  With r_v, V is rotated too."""
     t = k.shape[0]
     npg = (t + 15) // 16
-    pool = oscar.OscarPool(pool_config(wl))
+    pool = oscar.OscarPool(pool_config(wl, v_absorbed=r_v is None))
     rng = np.random.default_rng(seed)
     n_phys = npg + 3
     ids = rng.permutation(n_phys)[:npg].astype(np.int32)
     int2 = torch.randint(0, 256, (n_phys, pool.int2_page_bytes), dtype=torch.uint8, device="cuda")
     log(f"quantize_pack launch: T={t} pages={npg}")
     oscar.oscar_quantize_pack(pool, to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16), to_dev(ids), int2,
-                              to_dev(r_k), to_dev(tau_k), to_dev(tau_v))
+                              to_dev(r_k), to_dev(tau_k), to_dev(tau_v), r_v=None if r_v is None else to_dev(r_v))
     torch.cuda.synchronize()
     host = int2.cpu().numpy()
     hist = pool_io.read_history(host, ids, t, wl.num_kv_heads, wl.head_dim, wl.n_groups)
@@ -87,6 +87,25 @@ def test_quantize_pack_page_split(gpu_lib, monkeypatch, name, ppb):
                     f"{name} V head {h} pages/block={ppb}")
 
 
+@pytest.mark.parametrize("identity", [True, False])
+@pytest.mark.parametrize("name", list(WL))
+def test_quantize_pack_values_rotated(gpu_lib, name, identity):
+    """v_absorbed = 0: V is rotated by R_V on the matrix cores like K.  With
+    R_V = I the V codes are bit-exact; with the calibrated R_V the flip rule
+    applies."""
+    wl = WL[name]
+    inp = draw_inputs(wl, with_q=False)
+    k, v = inp.k[0][:1000].float().numpy(), inp.v[0][:1000].float().numpy()
+    c = inp.calib
+    r_v = _identity(wl.num_kv_heads, wl.head_dim) if identity else c.r_v
+    kc, ks, kz, vc, vs, vz = _bulk(gpu_lib, wl, k, v, c.r_k, c.tau_k, c.tau_v, seed=wl.seed + 7, r_v=r_v)
+    for h in range(wl.num_kv_heads):
+        check_write((kc[:, h], ks[:, h], kz[:, h]), k[:, h], c.r_k[h], c.tau_k[h], wl.group_size,
+                    f"{name} K head {h} (V rotated too)")
+        check_write((vc[:, h], vs[:, h], vz[:, h]), v[:, h], None if identity else r_v[h], c.tau_v[h],
+                    wl.group_size, f"{name} V head {h} rotated (R_V = I: {identity})")
+
+
 def test_quantize_pack_full_size_sampled(gpu_lib):
     """Bulk prefill of 131,072 tokens x 8 KV heads x 128 (the bulk workload);
     every page is read back and a sample of pages checked against the oracle."""
@@ -105,7 +124,7 @@ def test_quantize_pack_full_size_sampled(gpu_lib):
                     f"bulk V head {h} (64 sampled pages)")
 
 
-@pytest.mark.parametrize("rotated", [False, True])
+@pytest.mark.parametrize("rotated", [False, True, "values too"])
 @pytest.mark.parametrize("name", ["d128-g128", "d64-g64", "d128-g64"])
 def test_append_demote_steps_then_decode(gpu_lib, name, rotated):
     """Three sequences (one still too short to demote) take 40 decode-time
@@ -118,26 +137,29 @@ def test_append_demote_steps_then_decode(gpu_lib, name, rotated):
     inp = draw_inputs(wl)
     c = inp.calib
     r_k = c.r_k if rotated else _identity(wl.num_kv_heads, wl.head_dim)
+    r_v = c.r_v if rotated == "values too" else None  # V not absorbed: rotated at demotion
     seqs = []
     for b in range(3):
         k, v = inp.k[b][: l0[b]].float().numpy(), inp.v[b][: l0[b]].float().numpy()
-        seqs.append(oracle.SeqPool(wl.num_kv_heads, wl.head_dim, wl.group_size, wl.sink, wl.recent)
-                    .prefill(k, v, r_k, c.tau_k, c.tau_v))
+        seqs.append(oracle.SeqPool(wl.num_kv_heads, wl.head_dim, wl.group_size, wl.sink, wl.recent,
+                                   v_absorbed=r_v is None).prefill(k, v, r_k, c.tau_k, c.tau_v, r_v))
     cap = [(max(0, x + steps - 320) + 15) // 16 + 1 for x in l0]
     extra = {b: list(range((l0[b] + steps + 15) // 16)) for b in range(3)}
     pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=5,
                                 int2_capacity=cap, extra_bf16_pages=extra, garbage=False)
     dev = upload(pools)
-    pool = gpu_lib.OscarPool(pool_config(wl))
+    pool = gpu_lib.OscarPool(pool_config(wl, v_absorbed=r_v is None))
     rk, tk, tv = to_dev(r_k), to_dev(c.tau_k), to_dev(c.tau_v)
+    rv = None if r_v is None else to_dev(r_v)
     for st in range(steps):
         lens = torch.tensor([x + st for x in l0], dtype=torch.int32, device="cuda")
         kn = torch.stack([inp.k[b][l0[b] + st] for b in range(3)]).cuda()
         vn = torch.stack([inp.v[b][l0[b] + st] for b in range(3)]).cuda()
         gpu_lib.oscar_append_demote(pool, kn, vn, lens, dev["bf16_pt"], dev["int2_pt"], dev["bf16_pool"],
-                                    dev["int2_pool"], rk, tk, tv)
+                                    dev["int2_pool"], rk, tk, tv, r_v=rv)
         for b in range(3):
-            seqs[b].append_demote(kn[b].float().cpu().numpy(), vn[b].float().cpu().numpy(), r_k, c.tau_k, c.tau_v)
+            seqs[b].append_demote(kn[b].float().cpu().numpy(), vn[b].float().cpu().numpy(), r_k, c.tau_k, c.tau_v,
+                                  r_v)
     torch.cuda.synchronize()
     host2 = dev["int2_pool"].cpu().numpy()
     host16 = dev["bf16_pool"].cpu().numpy()
@@ -151,8 +173,9 @@ def test_append_demote_steps_then_decode(gpu_lib, name, rotated):
                 hist_pos = wl.sink + new
                 check_write((kc[new, h], ks[new, h], kz[new, h]), s.k[hist_pos, h], r_k[h] if rotated else None,
                             c.tau_k[h], wl.group_size, f"{name} demoted K seq {b} head {h}")
-                check_write((vc[new, h], vs[new, h], vz[new, h]), s.v[hist_pos, h], None, c.tau_v[h],
-                            wl.group_size, f"{name} demoted V seq {b} head {h}")
+                check_write((vc[new, h], vs[new, h], vz[new, h]), s.v[hist_pos, h],
+                            None if r_v is None else r_v[h], c.tau_v[h], wl.group_size,
+                            f"{name} demoted V seq {b} head {h}")
         # appended tokens landed in the BF16 pool
         for pos in range(l0[b], l0[b] + steps):
             blk = host16[pools["bf16_pt"][b, pos // 16]].reshape(wl.num_kv_heads, -1)
@@ -163,7 +186,7 @@ def test_append_demote_steps_then_decode(gpu_lib, name, rotated):
     out = torch.full(inp.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
     ws = pool.alloc_workspace(3, max(s.L for s in seqs))
     gpu_lib.oscar_decode_attention(pool, inp.q.cuda(), lens, max(s.L for s in seqs), dev["bf16_pt"], dev["int2_pt"],
-                                   dev["bf16_pool"], dev["int2_pool"], rk, out, ws)
+                                   dev["bf16_pool"], dev["int2_pool"], rk, out, ws, r_v=rv)
     torch.cuda.synchronize()
-    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), r_k)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), r_k, r_v)
     check_decode(out, ref, what=f"{name} decode after demotion rotated={rotated}")

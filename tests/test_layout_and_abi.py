@@ -102,6 +102,7 @@ def test_pool_create_validation_and_layout():
     assert p.bf16_head_block_bytes == 8192 and p.bf16_page_bytes == 8 * 8192
     assert oscar.OscarPool(_cfg(head_dim=64, group_size=64, num_q_heads=4, num_kv_heads=2)).int2_head_block_bytes == 640
     assert oscar.OscarPool(_cfg(group_size=64)).int2_head_block_bytes == 8 * 128 + 256
+    assert oscar.OscarPool(_cfg(v_absorbed=0)).int2_page_bytes == 8 * 1152  # values not absorbed
     cases = [
         (dict(num_q_heads=30), oscar.OSCAR_ERR_INVALID),
         (dict(group_size=96), oscar.OSCAR_ERR_INVALID),
@@ -112,7 +113,7 @@ def test_pool_create_validation_and_layout():
         (dict(group_size=32), oscar.OSCAR_ERR_UNSUPPORTED),
         (dict(page_size=32, sink_tokens=64), oscar.OSCAR_ERR_UNSUPPORTED),
         (dict(num_q_heads=8), oscar.OSCAR_ERR_UNSUPPORTED),
-        (dict(v_absorbed=0), oscar.OSCAR_ERR_UNSUPPORTED),
+        (dict(v_absorbed=2), oscar.OSCAR_ERR_INVALID),
     ]
     for kw, status in cases:
         with pytest.raises(oscar.OscarError) as e:
@@ -149,7 +150,7 @@ def test_decode_validation_fails_before_launch():
     assert call(q=None) == oscar.OSCAR_ERR_INVALID
     assert call(ipool=F + 4) == oscar.OSCAR_ERR_INVALID  # misaligned
     assert call(bs=0) == oscar.OSCAR_ERR_INVALID
-    assert call(rv=F) == oscar.OSCAR_ERR_UNSUPPORTED
+    assert call(rv=F) == oscar.OSCAR_ERR_INVALID  # r_v given although V is absorbed
     assert call() == oscar.OSCAR_ERR_WORKSPACE  # 16 bytes is too small
     assert call(ws=F + 64, wsb=1 << 30) == oscar.OSCAR_ERR_WORKSPACE  # misaligned workspace
     assert b"workspace" in lib.oscar_last_error()
@@ -159,6 +160,13 @@ def test_decode_validation_fails_before_launch():
     assert lib.oscar_merge(4, 128, None, F, F, F, None) == oscar.OSCAR_ERR_INVALID
     assert lib.oscar_quantize_pack(p.handle, 16, F, F, F, 0, F, F, None, F, F, None) == oscar.OSCAR_ERR_INVALID
     assert lib.oscar_append_demote(p.handle, 1, F, F, F, F, 8, 4, F, 8, 4, F, F, F, F, F, F, None) == \
-        oscar.OSCAR_ERR_UNSUPPORTED  # r_v given
+        oscar.OSCAR_ERR_INVALID  # r_v given although V is absorbed
+    # values not absorbed: r_v is required
+    pn = oscar.OscarPool(_cfg(v_absorbed=0))
+    assert lib.oscar_append_demote(pn.handle, 1, F, F, F, F, 8, 4, F, 8, 4, F, F, F, None, F, F, None) == \
+        oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_quantize_pack(pn.handle, 16, F, F, F, 4, F, F, None, F, F, None) == oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_decode_attention(pn.handle, 1, 1000, F, F, F, 8, 4, F, 8, 4, F, F, F, None, F, F, 16, None) == \
+        oscar.OSCAR_ERR_INVALID
     assert lib.oscar_bf16_decode_attention(p.handle, 1, 100, F, F, F, 8, 4, F, F, F, 0, None) == \
         oscar.OSCAR_ERR_WORKSPACE
