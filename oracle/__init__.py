@@ -16,7 +16,12 @@ What it computes, and where the pages say so:
   * decode attention as one softmax over the dequantized, inverse-rotated,
     concatenated pool in fp64 (``attention``), and the log-sum-exp merge of
     partial attentions (``merge``; ModelScope/CSDN page, decode paragraph on
-    the split INT2/BF16 kernels and the online-softmax merge).
+    the split INT2/BF16 kernels and the online-softmax merge);
+  * offline calibration (query and score-weighted value covariances, their
+    eigenbases, R = U H P_br, clip thresholds) and the synthetic error chain
+    that compares rotations by logit error, score KL and output MSE
+    (``calibration``; MarkTechPost article, "What OSCAR Does Differently";
+    ModelScope/CSDN page, motivation section, Figure 1).
 
 Floating point: fp64 except where the method's encoding fixes an fp32 or bf16
 rounding (the quantizer's scale, zero and code decisions), which are done in
@@ -33,3 +38,5 @@ from .quant import (  # noqa: F401
 from .pool import LogicalPool, SeqPool  # noqa: F401
 from .attention import decode_attention, bf16_decode_attention, attention_one_head  # noqa: F401
 from .merge import merge_partials  # noqa: F401
+from . import calibration  # noqa: F401
+from .calibration import calibrate  # noqa: F401

@@ -1,27 +1,27 @@
 """Seeded synthetic inputs for the OSCAR INT2 decode path.
 
 This package is the only code shared by the CPU oracle (``oracle/``), the GPU
-tests and ``bench.py``.  It draws random tensors and builds the fixed offline
-parameters the hot path consumes (the rotations R_K, R_V and the clip
-thresholds), following the calibration recipe the OSCAR pages describe
-(MarkTechPost article, "What OSCAR Does Differently": R = U * H_Had * P_br with
-U the eigenvectors of the query covariance C_Q for keys and of the
-score-weighted value covariance C_S for values).
+tests and ``bench.py``.  It draws random tensors only: workload shapes,
+calibration activations, cache contents, queries and page tables.
 
-It holds none of the hot path's arithmetic: no rotation of cache tokens, no
-clipping, quantization or packing, no attention.  Those live, independently,
-in ``oracle/`` (plain CPU reference) and in the HIP library.
+It holds none of the method's arithmetic: no covariance, eigenbasis, rotation
+construction or clip threshold, no rotation of cache tokens, no quantization
+or packing, no attention.  Those live, independently, in ``oracle/`` (plain
+CPU reference) and in the HIP library.  The offline parameters the cache
+tensors depend on (values are stored multiplied by R_V) are passed in.
 """
 
 from .recipes import (  # noqa: F401
+    CALIB_TOKENS,
     CONFIGS,
     Workload,
     Calibration,
+    CalibrationDraw,
     Inputs,
-    bit_reversal_permutation,
-    calibrate,
+    draw_calibration,
     draw_inputs,
-    hadamard_matrix,
+    make_calibration,
     make_workload,
+    query_eigenvalues,
     random_page_table,
 )

@@ -11,22 +11,18 @@ Distributions (one recipe for every workload):
              fold R_V into the projection weights offline, MarkTechPost
              article, "The Serving System"), then rounded to bf16.
 
-Offline parameters (per KV head, from a separate 2048-token calibration draw):
-  * R_K = U_Q H P_br, U_Q the eigenvectors of C_Q = (1/N) sum q^T q
-    (MarkTechPost article, "What OSCAR Does Differently", rotation equation);
-  * R_V = U_S H P_br, U_S the eigenvectors of C_S = (1/N) V^T S^T S V with S
-    the causal softmax score matrix of the calibration draw, averaged over the
-    KV head's query heads (same section);
-  * H the Sylvester Walsh-Hadamard matrix scaled by 1/sqrt(D), P_br the
-    bit-reversal permutation (same section, "Pbr" and "HHad" bullets);
-  * tau_K, tau_V: the 0.995 quantile of |x R| over the rotated calibration
-    values, numpy 'linear' interpolation in fp64, rounded to fp32.
+Calibration activations (per KV head, a separate 2048-token draw, rounded to
+fp32): the group's queries, keys with the same outlier recipe, values in the
+model basis.  This module draws them; the offline parameters computed from
+them (R_K, R_V, tau_K, tau_V) come from the library's calibration kernels in
+the benchmark and from the oracle in the tests, and are passed back in through
+``make_calibration``.
 
 Row-vector convention throughout: a rotated vector is x' = x R with R stored
 row-major as [D_in][D_out].
 
-Random streams: numpy PCG64(seed) for calibration (drawn per KV head in head
-order: Haar basis, outlier channels, calibration queries, keys, values), and a
+Random streams: numpy PCG64(seed) for the calibration draw (per KV head in
+head order: Haar basis, outlier channels, calibration queries, keys, values), and a
 torch generator seeded with ``seed * 1000 + 7`` on the requested device for the
 bulk tensors (keys, values, queries, new tokens, in that order).
 """
@@ -141,48 +137,10 @@ def make_workload(base: Workload, **changes) -> Workload:
 # offline calibration (produces the hot path's fixed inputs)
 # --------------------------------------------------------------------------
 
-def hadamard_matrix(d: int) -> np.ndarray:
-    """Sylvester-ordered Walsh-Hadamard matrix scaled by 1/sqrt(d) (fp64)."""
-    assert d > 0 and d & (d - 1) == 0
-    h = np.ones((1, 1))
-    while h.shape[0] < d:
-        h = np.block([[h, h], [h, -h]])
-    return h / math.sqrt(d)
-
-
-def bit_reversal_permutation(d: int) -> np.ndarray:
-    """perm[i] = index i with its log2(d) bits reversed."""
-    bits = int(round(math.log2(d)))
-    assert 1 << bits == d
-    return np.array([int(format(i, f"0{bits}b")[::-1], 2) if bits else 0 for i in range(d)])
-
-
 def _haar(rng: np.random.Generator, d: int) -> np.ndarray:
     a = rng.standard_normal((d, d))
     q, r = np.linalg.qr(a)
     return q * np.sign(np.diag(r))
-
-
-def _sorted_eigvecs(c: np.ndarray) -> np.ndarray:
-    """Eigenvectors as columns, eigenvalues descending, each column's
-    largest-magnitude entry made positive."""
-    w, u = np.linalg.eigh(c)
-    u = u[:, np.argsort(w)[::-1]]
-    idx = np.argmax(np.abs(u), axis=0)
-    return u * np.sign(u[idx, np.arange(u.shape[1])])
-
-
-@dataclasses.dataclass
-class Calibration:
-    r_k: np.ndarray  # [Hkv, D, D] float32
-    r_v: np.ndarray  # [Hkv, D, D] float32
-    tau_k: np.ndarray  # [Hkv] float32
-    tau_v: np.ndarray  # [Hkv] float32
-    q_basis: np.ndarray  # [Hkv, D, D] float64, the Haar U of Sigma_Q
-    q_eigs: np.ndarray  # [D] float64
-    outliers: np.ndarray  # [Hkv, 4] int64
-    c_q: np.ndarray  # [Hkv, D, D] float64 empirical query covariance
-    c_s: np.ndarray  # [Hkv, D, D] float64 empirical score-weighted V covariance
 
 
 def query_eigenvalues(d: int) -> np.ndarray:
@@ -190,17 +148,23 @@ def query_eigenvalues(d: int) -> np.ndarray:
     return lam * (d / lam.sum())
 
 
-def calibrate(num_kv_heads: int, gqa: int, head_dim: int, seed: int,
-              n_cal: int = CALIB_TOKENS) -> Calibration:
+@dataclasses.dataclass
+class CalibrationDraw:
+    """Seeded calibration activations of one KV head's group (fp32 values)."""
+    q: np.ndarray  # [gqa, n, d] queries of the group's query heads
+    k: np.ndarray  # [n, d] keys (with the outlier channels)
+    v: np.ndarray  # [n, d] values (model basis)
+    u: np.ndarray  # [d, d] fp64 Haar basis of Sigma_Q
+    outliers: np.ndarray  # [4] outlier channels of k
+
+
+def draw_calibration(num_kv_heads: int, gqa: int, head_dim: int, seed: int,
+                     n_cal: int = CALIB_TOKENS) -> list:
+    """Calibration activations per KV head (random draws only)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     d = head_dim
     lam = query_eigenvalues(d)
-    had = hadamard_matrix(d)
-    perm = np.zeros((d, d))
-    perm[np.arange(d), bit_reversal_permutation(d)] = 1.0  # (y P)[j] = y[br(j)]
-    sm = 1.0 / math.sqrt(d)
-    causal = np.tril(np.ones((n_cal, n_cal), dtype=bool))
-    out = {k: [] for k in ("r_k", "r_v", "tau_k", "tau_v", "U", "out", "c_q", "c_s")}
+    draws = []
     for _ in range(num_kv_heads):
         u = _haar(rng, d)
         outl = np.sort(rng.choice(d, OUTLIER_CHANNELS, replace=False))
@@ -209,35 +173,33 @@ def calibrate(num_kv_heads: int, gqa: int, head_dim: int, seed: int,
         k_cal = rng.standard_normal((n_cal, d))
         k_cal[:, outl] *= OUTLIER_SCALE
         v_cal = rng.standard_normal((n_cal, d))
-        qf = q_cal.reshape(-1, d)
-        c_q = qf.T @ qf / qf.shape[0]
-        r_k = _sorted_eigvecs(c_q) @ had @ perm
-        c_s = np.zeros((d, d))
-        for h in range(gqa):
-            logits = sm * q_cal[h] @ k_cal.T
-            logits = np.where(causal, logits, -np.inf)
-            logits -= logits.max(axis=1, keepdims=True)
-            s = np.exp(logits)
-            s /= s.sum(axis=1, keepdims=True)
-            sv = s @ v_cal
-            c_s += sv.T @ sv / n_cal
-        c_s /= gqa
-        r_v = _sorted_eigvecs(c_s) @ had @ perm
-        out["r_k"].append(r_k)
-        out["r_v"].append(r_v)
-        out["tau_k"].append(np.quantile(np.abs(k_cal @ r_k), CLIP_QUANTILE))
-        out["tau_v"].append(np.quantile(np.abs(v_cal @ r_v), CLIP_QUANTILE))
-        out["U"].append(u)
-        out["out"].append(outl)
-        out["c_q"].append(c_q)
-        out["c_s"].append(c_s)
+        draws.append(CalibrationDraw(q=q_cal.astype(np.float32), k=k_cal.astype(np.float32),
+                                     v=v_cal.astype(np.float32), u=u, outliers=outl))
+    return draws
+
+
+@dataclasses.dataclass
+class Calibration:
+    """Offline parameters of the hot path (computed elsewhere: by the oracle
+    in tests, by the library's calibration kernels in the benchmark) plus the
+    draw parameters the bulk tensors are generated from."""
+    r_k: np.ndarray  # [Hkv, D, D] float32
+    r_v: np.ndarray  # [Hkv, D, D] float32
+    tau_k: np.ndarray  # [Hkv] float32
+    tau_v: np.ndarray  # [Hkv] float32
+    q_basis: np.ndarray  # [Hkv, D, D] float64, the Haar U of Sigma_Q
+    q_eigs: np.ndarray  # [D] float64
+    outliers: np.ndarray  # [Hkv, 4] int64
+
+
+def make_calibration(draws: list, r_k, r_v, tau_k, tau_v) -> Calibration:
+    """Bundle offline parameters with the draws' basis and outlier channels."""
     return Calibration(
-        r_k=np.stack(out["r_k"]).astype(np.float32),
-        r_v=np.stack(out["r_v"]).astype(np.float32),
-        tau_k=np.array(out["tau_k"], dtype=np.float32),
-        tau_v=np.array(out["tau_v"], dtype=np.float32),
-        q_basis=np.stack(out["U"]), q_eigs=lam, outliers=np.stack(out["out"]),
-        c_q=np.stack(out["c_q"]), c_s=np.stack(out["c_s"]))
+        r_k=np.ascontiguousarray(r_k, dtype=np.float32), r_v=np.ascontiguousarray(r_v, dtype=np.float32),
+        tau_k=np.asarray(tau_k, dtype=np.float32).reshape(-1),
+        tau_v=np.asarray(tau_v, dtype=np.float32).reshape(-1),
+        q_basis=np.stack([d.u for d in draws]), q_eigs=query_eigenvalues(draws[0].u.shape[0]),
+        outliers=np.stack([d.outliers for d in draws]))
 
 
 # --------------------------------------------------------------------------
@@ -260,12 +222,9 @@ class Inputs:
     q: object
 
 
-def draw_inputs(wl: Workload, calib: Optional[Calibration] = None, device="cpu",
-                with_q: bool = True) -> Inputs:
+def draw_inputs(wl: Workload, calib: Calibration, device="cpu", with_q: bool = True) -> Inputs:
     import torch
 
-    if calib is None:
-        calib = calibrate(wl.num_kv_heads, wl.gqa, wl.head_dim, wl.seed)
     gen = torch.Generator(device=device)
     gen.manual_seed(wl.seed * 1000 + 7)
     d, hkv = wl.head_dim, wl.num_kv_heads

@@ -13,6 +13,7 @@ Tolerances (stated for the path's fp32 accumulation with bf16 I/O):
     within 1e-5 * scale of the boundary between the two codes.
 """
 
+import functools
 import math
 import sys
 
@@ -29,6 +30,25 @@ FLIP_TOL = 1e-5
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+@functools.lru_cache(maxsize=16)
+def _oracle_calibration(num_kv_heads, gqa, head_dim, seed):
+    draws = synthetic.draw_calibration(num_kv_heads, gqa, head_dim, seed)
+    c = oracle.calibrate([(d.q, d.k, d.v) for d in draws])
+    return synthetic.make_calibration(draws, c["r_k"], c["r_v"], c["tau_k"], c["tau_v"])
+
+
+def calibration(wl):
+    """Offline parameters for a workload, from the oracle's calibration of the
+    seeded calibration draw."""
+    return _oracle_calibration(wl.num_kv_heads, wl.gqa, wl.head_dim, wl.seed)
+
+
+def draw_inputs(wl, calib=None, **kw):
+    """The seeded cache tensors and queries of a workload, with the oracle's
+    offline parameters unless ``calib`` is given."""
+    return synthetic.draw_inputs(wl, calibration(wl) if calib is None else calib, **kw)
 
 
 def make_seqs(wl, inputs, r_k=None, tau_k=None, tau_v=None, r_v=None):

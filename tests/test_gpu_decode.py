@@ -10,7 +10,8 @@ import torch
 import oracle
 import pool_io
 from harness import DECODE_TOL, check_decode, log, make_seqs, pool_config, to_dev, upload
-from synthetic import CONFIGS, draw_inputs, make_workload
+from synthetic import CONFIGS, make_workload
+from harness import draw_inputs
 
 pytestmark = pytest.mark.gpu
 

@@ -13,7 +13,8 @@ import torch
 import oracle
 import pool_io
 from harness import check_decode, check_write, log, pool_config
-from synthetic import CONFIGS, draw_inputs
+from synthetic import CONFIGS
+from harness import draw_inputs
 
 pytestmark = pytest.mark.gpu
 
