@@ -28,6 +28,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -37,6 +39,26 @@ METRIC = "INT2 decode-attn KV GB/s & tokens/s at 100K ctx; % of HBM peak"
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+_CALIB_CACHE = {}
+
+
+def gpu_calibration(oscar, wl):
+    """Offline parameters of a workload from the library's calibration kernels
+    (oscar_calibrate) on the seeded 2048-token calibration draw."""
+    import torch
+    from synthetic import draw_calibration, make_calibration
+    key = (wl.num_kv_heads, wl.gqa, wl.head_dim, wl.seed)
+    if key not in _CALIB_CACHE:
+        draws = draw_calibration(*key)
+        q = torch.from_numpy(np.stack([d.q for d in draws])).cuda()
+        k = torch.from_numpy(np.stack([d.k for d in draws])).cuda()
+        v = torch.from_numpy(np.stack([d.v for d in draws])).cuda()
+        res = oscar.oscar_calibrate(q, k, v, clip_quantile=0.995)
+        torch.cuda.synchronize()
+        _CALIB_CACHE[key] = make_calibration(draws, *(res[n].cpu().numpy() for n in ("r_k", "r_v", "tau_k", "tau_v")))
+    return _CALIB_CACHE[key]
 
 
 def parse():
@@ -53,7 +75,7 @@ def parse():
                     help="only run N eager decode steps over the cold pool copies, then one plain copy of "
                          "--probe-bytes (for rocprofv3 counters); prints no JSON")
     ap.add_argument("--probe-bytes", type=int, default=256 * 2**20)
-    ap.add_argument("--only", default="all", choices=["all", "headline", "bulk", "demote", "mixed"],
+    ap.add_argument("--only", default="all", choices=["all", "headline", "bulk", "demote", "mixed", "calib"],
                     help="run one section only (the JSON line then holds what was measured)")
     return ap.parse_args()
 
@@ -241,7 +263,7 @@ def bench_decode_workload(oscar, name, steps, warmup, repeats, cold_bytes):
     wl = CONFIGS[name]
     kv = wl.kv_bytes()
     uniq = unique_kv_bytes(wl)
-    inp = draw_inputs(wl, device="cuda")
+    inp = draw_inputs(wl, gpu_calibration(oscar, wl), device="cuda")
     pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
                                             wl.sink, wl.recent, 1, 0.0))
     n_copies = max(2, math.ceil(cold_bytes / uniq))
@@ -371,13 +393,17 @@ def traffic_for(workload, files=DECODE_SOURCES):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, repeats=3):
+def cpu_baseline(wl, repeats=3):
     """The oracle's decode (R1-R3) of the whole step, timed on this host's
     cores: every KV head of every sequence over its full context.  The
-    oracle's own write path builds its pool first (not timed)."""
-    import numpy as np
+    oracle's own calibration and write path build its inputs and pool first
+    (not timed), from the same seeded draws."""
     import oracle
-    c = inp.calib
+    from synthetic import draw_calibration, draw_inputs, make_calibration
+    draws = draw_calibration(wl.num_kv_heads, wl.gqa, wl.head_dim, wl.seed)
+    oc = oracle.calibrate([(d.q, d.k, d.v) for d in draws])
+    c = make_calibration(draws, oc["r_k"], oc["r_v"], oc["tau_k"], oc["tau_v"])
+    inp = draw_inputs(wl, c, device="cpu")
     seqs = []
     for b, L in enumerate(wl.seq_lens):
         k = inp.k[b][:L].float().cpu().numpy()
@@ -414,7 +440,7 @@ def bench_bulk_quant(oscar, steps=10, warmup=3, repeats=5, profile_launches=0):
     import torch
     from synthetic import CONFIGS, draw_inputs
     wl = CONFIGS["bulk-quant-t131k"]
-    inp = draw_inputs(wl, with_q=False, device="cuda")
+    inp = draw_inputs(wl, gpu_calibration(oscar, wl), with_q=False, device="cuda")
     k, v = inp.k[0].contiguous(), inp.v[0].contiguous()
     t = k.shape[0]
     c = inp.calib
@@ -448,6 +474,93 @@ def bench_bulk_quant(oscar, steps=10, warmup=3, repeats=5, profile_launches=0):
             "kernel": "k_quantize_pack (bf16-MFMA key rotation + clip + quantize + pack)"}
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def bench_calibration(oscar, steps=10, warmup=2, repeats=5, profile_launches=0):
+    """Offline calibration of one layer at the Qwen3-8B shape (8 KV heads x 4
+    query heads, D = 128) from the seeded 2048-token calibration draw:
+    oscar_calibrate (query covariance, causal calibration attention, score-
+    weighted value covariance, two Jacobi eigenbases + Hadamard mixes, two
+    clip quantiles), then the rotation error chain (quantize, dequantize,
+    reference-vs-quantized attention) for the calibrated rotation, the
+    Hadamard transform alone and no rotation."""
+    import torch
+    from synthetic import CONFIGS, draw_calibration
+    wl = CONFIGS["qwen3-8b-l100k"]
+    hkv, g, d = wl.num_kv_heads, wl.gqa, wl.head_dim
+    draws = draw_calibration(hkv, g, d, wl.seed)
+    n = draws[0].k.shape[0]
+    q = torch.from_numpy(np.stack([x.q for x in draws])).cuda()
+    k = torch.from_numpy(np.stack([x.k for x in draws])).cuda()
+    v = torch.from_numpy(np.stack([x.v for x in draws])).cuda()
+    ws = oscar._ws(oscar._size_out("oscar_calib_workspace_bytes", hkv, g, n, d), "cuda")
+    res = oscar.oscar_calibrate(q, k, v, workspace=ws)
+    attn_out = torch.empty(hkv, g, n, d, dtype=torch.float32, device="cuda")
+    if profile_launches:
+        for _ in range(profile_launches):
+            oscar.oscar_calibrate(q, k, v, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"profile run: {profile_launches} calibrations done")
+        return None
+    ms_cal, _ = time_steps(lambda i: oscar.oscar_calibrate(q, k, v, workspace=ws), steps, warmup, repeats)
+    ms_attn, _ = time_steps(lambda i: oscar.oscar_calib_attention(q, k, v, attn_out), steps, warmup, repeats)
+    flops = hkv * g * 4 * d * n * (n + 1) // 2  # Q K^T and P V over the causal pairs
+    tflops = flops / (ms_attn * 1e-3) / 1e12
+    log(f"calibration: {ms_cal * 1e3:.1f} us per layer; causal attention {ms_attn * 1e3:.1f} us "
+        f"({tflops:.1f} TFLOP/s fp32)")
+
+    # rotation error chain
+    eye = torch.eye(d, dtype=torch.float32, device="cuda").expand(hkv, d, d).contiguous()
+    had = torch.empty_like(eye)
+    oscar.oscar_calib_rotation(eye, had, mix=True)  # identity covariance: U = I, R = H P_br
+    tau_h = {x: torch.empty(hkv, dtype=torch.float32, device="cuda") for x in "kv"}
+    oscar.oscar_calib_clip(k, had, 0.995, tau_h["k"])
+    oscar.oscar_calib_clip(v, had, 0.995, tau_h["v"])
+    inf = torch.full((hkv,), float("inf"), dtype=torch.float32, device="cuda")
+    variants = {"oscar": (res["r_k"], res["r_v"], res["tau_k"], res["tau_v"]),
+                "hadamard_only": (had, had, tau_h["k"], tau_h["v"]),
+                "none": (eye, eye, inf, inf)}
+    pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, hkv, d, wl.group_size, 16, wl.sink, wl.recent, 0, 0.0))
+    npg = (n + 15) // 16
+    ids = torch.arange(npg, dtype=torch.int32, device="cuda")
+    int2 = torch.zeros(npg, pool.int2_page_bytes, dtype=torch.uint8, device="cuda")
+    k_tok = k.transpose(0, 1).to(torch.bfloat16).contiguous()  # the cache's bf16 content, [N, Hkv, D]
+    v_tok = v.transpose(0, 1).to(torch.bfloat16).contiguous()
+    k_ref, v_ref = k_tok.float().transpose(0, 1), v_tok.float().transpose(0, 1)
+    kh = torch.empty(n, hkv, d, dtype=torch.float32, device="cuda")
+    vh = torch.empty_like(kh)
+    stats = torch.empty(hkv, g, n, 4, dtype=torch.float32, device="cuda")
+    pairs = hkv * g * n * (n + 1) / 2
+    chain = {}
+    for name, (rk, rv, tk, tv) in variants.items():
+        def run(i, rk=rk, rv=rv, tk=tk, tv=tv):
+            oscar.oscar_quantize_pack(pool, k_tok, v_tok, ids, int2, rk, tk, tv, r_v=rv)
+            oscar.oscar_dequantize(pool, n, ids, int2, rk, rv, kh, vh)
+            oscar.oscar_attention_error(q, k_ref, v_ref, kh.transpose(0, 1), vh.transpose(0, 1), stats)
+        run(0)
+        torch.cuda.synchronize()
+        st = stats.double()
+        chain[name] = {"logit_mse": round(float(st[..., 1].sum() / pairs), 5),
+                       "score_kl": round(float(st[..., 0].mean()), 5),
+                       "out_rel_mse": round(float(st[..., 2].sum() / st[..., 3].sum()), 5)}
+        if name == "oscar":
+            ms_chain, _ = time_steps(run, steps, warmup, repeats)
+    log(f"error chain: {chain}")
+    del ws, attn_out, int2
+    torch.cuda.empty_cache()
+    return {"workload": f"calibration of one layer: {hkv} KV heads x {g} query heads, D={d}, {n}-token draw",
+            "us_per_calibration": round(ms_cal * 1e3, 1),
+            "calib_attention": {"us_per_launch": round(ms_attn * 1e3, 1), "flops_per_launch": flops,
+                                "TFLOPs": round(tflops, 2), "pct_fp32_mfma_peak": round(100 * tflops /
+                                                                                      FP32_MFMA_PEAK_TFLOPS, 2),
+                                "kernel": "k_calib_attention (fp32 MFMA causal attention)"},
+            "error_chain": chain, "us_per_error_chain": round(ms_chain * 1e3, 1),
+            "error_chain_note": "quantize_pack -> dequantize -> attention_error on the calibration draw itself; "
+                                "logit_mse per causal pair, score_kl per query row, out_rel_mse = "
+                                "sum ||o - o^||^2 / sum ||o||^2"}
+
+
 def copy_probe(nbytes):
     """One plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -477,6 +590,12 @@ def main():
         print(json.dumps({args.only: bench_decode_workload(oscar, name, max(10, args.steps // 4), args.warmup,
                                                            args.repeats, args.cold_bytes)}), flush=True)
         return
+    if args.only == "calib":
+        if args.profile_steps:
+            bench_calibration(oscar, profile_launches=args.profile_steps)
+            return
+        print(json.dumps({"calibration": bench_calibration(oscar)}), flush=True)
+        return
     if args.only == "bulk":
         if args.profile_steps:
             bench_bulk_quant(oscar, profile_launches=args.profile_steps)
@@ -487,7 +606,7 @@ def main():
     wl = CONFIGS[args.workload]
     kv = wl.kv_bytes()
     log(f"workload {wl.name}: KV bytes/step {kv['total']:,} (INT2 {kv['int2']:,}, BF16 {kv['bf16']:,})")
-    inp = draw_inputs(wl, device="cuda")
+    inp = draw_inputs(wl, gpu_calibration(oscar, wl), device="cuda")
     pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
                                             wl.sink, wl.recent, 1, 0.0))
     n_copies = max(1, math.ceil(args.cold_bytes / kv["total"]))
@@ -565,10 +684,11 @@ def main():
             "mixed_prefix_gqa8": bench_decode_workload(oscar, "qwen3-32b-b8-mixed-prefix", max(10, args.steps // 4),
                                                        args.warmup, args.repeats, args.cold_bytes),
             "bulk_quantize": bench_bulk_quant(oscar),
+            "calibration": bench_calibration(oscar),
         }
     result["copy_ceiling_GBps"] = round(copy_ceiling_gbps(), 1)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, inp)
+        result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
 
 

@@ -220,6 +220,98 @@ oscar_status oscar_bf16_decode_attention(const oscar_pool* pool, int32_t batch, 
                                          int32_t bf16_num_pages, const void* bf16_pool, void* out,
                                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Offline calibration (MarkTechPost article on OSCAR, "What OSCAR Does
+ * Differently"; ModelScope/CSDN page, design section: per layer and head, a
+ * fixed rotation and clip threshold are estimated from a small calibration
+ * set).  All fp32.  Calibration activations of one layer:
+ *   q: [Hkv][g][N][D] contiguous, the queries of the g query heads that read
+ *      each KV head (model basis, before any rotation);
+ *   k, v: element (h, n, c) at h * kv_head_stride + n * kv_token_stride + c
+ *      (strides in elements, multiples of 4, kv_token_stride >= D), e.g.
+ *      [Hkv][N][D] or [N][Hkv][D]; values in the model basis.
+ * head_dim is 64 or 128.  Pointers are device memory, 16-byte aligned; every
+ * head's addressed span must stay below 2 GiB.
+ * ------------------------------------------------------------------------ */
+
+/* C = scale * X^T X for each of `heads` matrices X [rows][head_dim], row r of
+ * head h at x + h * head_stride + r * row_stride.  out: fp32
+ * [heads][head_dim][head_dim].  The sum over rows is split over workgroups
+ * and reduced in a fixed order (deterministic). */
+oscar_status oscar_calib_gram_workspace_bytes(int32_t heads, int32_t rows, int32_t head_dim, size_t* bytes);
+oscar_status oscar_calib_gram(int32_t heads, int32_t rows, int32_t head_dim, const float* x, int64_t head_stride,
+                              int64_t row_stride, float scale, float* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Causal softmax attention of the calibration draw: for KV head h, query head
+ * j and row n, out[h][j][n] = sum_{t <= n} p_t v_t with p = softmax over
+ * t <= n of sm * q[h][j][n] . k_t (sm_scale 0 selects 1/sqrt(head_dim)).
+ * out: fp32 [Hkv][g][N][D]; lse: fp32 [Hkv][g][N] natural-log normalizer, or
+ * NULL.  The score-weighted value covariance C_S of a KV head is the gram of
+ * its g*N output rows scaled by 1/(g*N). */
+oscar_status oscar_calib_attention(int32_t kv_heads, int32_t gqa, int32_t tokens, int32_t head_dim, float sm_scale,
+                                   const float* q, const float* k, const float* v, int64_t kv_head_stride,
+                                   int64_t kv_token_stride, float* out, float* lse, void* stream);
+
+/* Eigenbasis and rotation of symmetric matrices cov [heads][D][D]: U holds
+ * the eigenvectors as columns ordered by descending eigenvalue, each column
+ * signed so that its largest-magnitude entry (the first of equal ones) is
+ * positive; with mix = 1, r = U H P_br (H the Sylvester Walsh-Hadamard
+ * matrix / sqrt(D); column j of H P_br is column bitreverse(j) of H), with
+ * mix = 0, r = U.  r: fp32 [heads][D][D] row-major [D_in][D_out];
+ * eigvals: fp32 [heads][D] descending, or NULL.  One-sided Jacobi in fp32. */
+oscar_status oscar_calib_rotation(int32_t heads, int32_t head_dim, const float* cov, int32_t mix, float* r,
+                                  float* eigvals, void* stream);
+
+/* Clip thresholds: tau[h] = the `quantile` quantile (linear interpolation
+ * between the order statistics at rank (M-1)*quantile, M = rows*D) of
+ * |x R[h]| over all rows of head h (x laid out as for oscar_calib_gram;
+ * r NULL: no rotation), rounded to fp32.  The order statistics are exact
+ * (radix selection); y = x R is fp32 on the matrix cores. */
+oscar_status oscar_calib_clip_workspace_bytes(int32_t heads, int32_t rows, int32_t head_dim, size_t* bytes);
+oscar_status oscar_calib_clip(int32_t heads, int32_t rows, int32_t head_dim, const float* x, int64_t head_stride,
+                              int64_t row_stride, const float* r, double quantile, float* tau, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* The whole calibration of one layer: C_Q = gram(q)/(g N), R_K = U_Q H P_br,
+ * C_S from the causal attention outputs, R_V = U_S H P_br, tau_K and tau_V
+ * the clip_quantile quantiles of |k R_K| and |v R_V| (the pages give the
+ * clip as a ratio without fixing its estimator; the synthetic workloads use
+ * the 0.995 quantile).  r_k, r_v: fp32 [Hkv][D][D]; tau_k, tau_v: fp32
+ * [Hkv]; c_q, c_s: fp32 [Hkv][D][D] or NULL. */
+oscar_status oscar_calib_workspace_bytes(int32_t kv_heads, int32_t gqa, int32_t tokens, int32_t head_dim,
+                                         size_t* bytes);
+oscar_status oscar_calibrate(int32_t kv_heads, int32_t gqa, int32_t tokens, int32_t head_dim, float sm_scale,
+                             const float* q, const float* k, const float* v, int64_t kv_head_stride,
+                             int64_t kv_token_stride, double clip_quantile, float* r_k, float* r_v, float* tau_k,
+                             float* tau_v, float* c_q, float* c_s, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Rotation error chain (ModelScope/CSDN page, motivation section and its
+ * Figure 1: rotations are judged by attention-score KL and attention output
+ * error, not by K/V reconstruction error).
+ *
+ * oscar_dequantize: reads INT2 history records of tokens 0..num_tokens-1
+ * (token t in slot t%16 of page page_ids[t/16], the layout written by
+ * oscar_quantize_pack) and writes k_out, v_out fp32 [num_tokens][Hkv][D]:
+ * s (code - z) R_K^T for keys and s (code - z) R_V^T for values; a NULL
+ * r_k / r_v returns that tensor in its stored basis.
+ *
+ * oscar_attention_error: causal attention of q (layout as above) over the
+ * reference (k, v) and over the quantized (k_hat, v_hat), same strides; per
+ * KV head h, query head j and row n, stats[h][j][n] = {KL(p || p^),
+ * sum_{t <= n} (l^_t - l_t)^2, ||o - o^||^2, ||o||^2} with l = sm q.k,
+ * p = softmax(l), o = p v (fp32 [Hkv][g][N][4]).  Both softmaxes are taken
+ * against one running maximum, so a row whose every quantized logit sits
+ * more than ~87 below every reference logit underflows (not met in practice). */
+oscar_status oscar_dequantize(const oscar_pool* pool, int32_t num_tokens, const int32_t* page_ids,
+                              int32_t int2_num_pages, const void* int2_pool, const float* r_k, const float* r_v,
+                              float* k_out, float* v_out, void* stream);
+oscar_status oscar_attention_error(int32_t kv_heads, int32_t gqa, int32_t tokens, int32_t head_dim, float sm_scale,
+                                   const float* q, const float* k, const float* v, const float* k_hat,
+                                   const float* v_hat, int64_t kv_head_stride, int64_t kv_token_stride,
+                                   float* stats, void* stream);
+
 const char* oscar_status_string(oscar_status status);
 /* Reason for the last error returned on this thread ("" if none). */
 const char* oscar_last_error(void);

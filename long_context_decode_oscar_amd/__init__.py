@@ -25,6 +25,9 @@ EXPORTED = (
     "oscar_pool_create", "oscar_pool_destroy", "oscar_decode_workspace_bytes", "oscar_append_demote",
     "oscar_decode_attention", "oscar_merge", "oscar_quantize_pack", "oscar_bf16_decode_attention",
     "oscar_write_bf16", "oscar_status_string", "oscar_last_error",
+    "oscar_calib_gram_workspace_bytes", "oscar_calib_gram", "oscar_calib_attention", "oscar_calib_rotation",
+    "oscar_calib_clip_workspace_bytes", "oscar_calib_clip", "oscar_calib_workspace_bytes", "oscar_calibrate",
+    "oscar_dequantize", "oscar_attention_error",
 )
 
 
@@ -74,6 +77,17 @@ def load(path: str = LIB_PATH):
     lib.oscar_quantize_pack.argtypes = [P, I, P, P, P, I, P, P, P, P, P, P]
     lib.oscar_bf16_decode_attention.argtypes = [P, I, I, P, P, P, I, I, P, P, P, S, P]
     lib.oscar_write_bf16.argtypes = [P, I, I, P, P, P, I, I, P, P]
+    L = ctypes.c_int64
+    lib.oscar_calib_gram_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(S)]
+    lib.oscar_calib_gram.argtypes = [I, I, I, P, L, L, F, P, P, S, P]
+    lib.oscar_calib_attention.argtypes = [I, I, I, I, F, P, P, P, L, L, P, P, P]
+    lib.oscar_calib_rotation.argtypes = [I, I, P, I, P, P, P]
+    lib.oscar_calib_clip_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(S)]
+    lib.oscar_calib_clip.argtypes = [I, I, I, P, L, L, P, ctypes.c_double, P, P, S, P]
+    lib.oscar_calib_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(S)]
+    lib.oscar_calibrate.argtypes = [I, I, I, I, F, P, P, P, L, L, ctypes.c_double, P, P, P, P, P, P, P, S, P]
+    lib.oscar_dequantize.argtypes = [P, I, P, I, P, P, P, P, P, P]
+    lib.oscar_attention_error.argtypes = [I, I, I, I, F, P, P, P, P, P, L, L, P, P]
     lib.oscar_status_string.argtypes = [ctypes.c_int]
     lib.oscar_status_string.restype = ctypes.c_char_p
     lib.oscar_last_error.argtypes = []
@@ -241,3 +255,133 @@ def oscar_write_bf16(pool: OscarPool, k, v, first_position: int, bf16_page_table
         _ptr(bf16_page_table_row, "bf16_page_table_row", torch.int32), bf16_page_table_row.numel(),
         _pages(bf16_pool, pool.bf16_page_bytes), _ptr(bf16_pool, "bf16_pool", torch.uint8), _stream(stream)),
         "oscar_write_bf16")
+
+
+# ---------------------------------------------------------------------------
+# offline calibration and the rotation error chain
+# ---------------------------------------------------------------------------
+
+def _rows_view(x, name):
+    """A [heads, rows, D] fp32 device view whose last dimension is dense:
+    returns (pointer, head stride, row stride) in elements."""
+    import torch
+    if not x.is_cuda or x.dtype != torch.float32 or x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError(f"{name} must be a float32 device tensor [heads, rows, D] with unit last stride")
+    return x.data_ptr(), x.stride(0), x.stride(1)
+
+
+def _ws(nbytes, device):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _size_out(fn, *args):
+    n = ctypes.c_size_t()
+    _check(getattr(load(), fn)(*args, ctypes.byref(n)), fn)
+    return n.value
+
+
+def oscar_calib_gram(x, scale: float, out, workspace=None, stream=None):
+    """out[h] = scale * x[h]^T x[h] for x [heads, rows, D] (any head/row
+    strides)."""
+    import torch
+    heads, rows, d = x.shape
+    px, hs, rs = _rows_view(x, "x")
+    if workspace is None:
+        workspace = _ws(_size_out("oscar_calib_gram_workspace_bytes", heads, rows, d), x.device)
+    _check(load().oscar_calib_gram(heads, rows, d, px, hs, rs, float(scale), _ptr(out, "out", torch.float32),
+                                   _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)),
+           "oscar_calib_gram")
+    return out
+
+
+def oscar_calib_attention(q, k, v, out, lse=None, sm_scale: float = 0.0, stream=None):
+    """Causal attention of the calibration draw: q [Hkv, g, N, D] contiguous,
+    k and v [Hkv, N, D] views with unit last stride and equal strides."""
+    import torch
+    hkv, g, n, d = q.shape
+    pk, hs, ns = _rows_view(k, "k")
+    pv, hs2, ns2 = _rows_view(v, "v")
+    if (hs, ns) != (hs2, ns2):
+        raise ValueError("k and v must have the same strides")
+    _check(load().oscar_calib_attention(hkv, g, n, d, float(sm_scale), _ptr(q, "q", torch.float32), pk, pv, hs, ns,
+                                        _ptr(out, "out", torch.float32), _ptr(lse, "lse", torch.float32),
+                                        _stream(stream)),
+           "oscar_calib_attention")
+    return out
+
+
+def oscar_calib_rotation(cov, r, eigvals=None, mix: bool = True, stream=None):
+    """Eigenbasis of cov [heads, D, D] and R = U H P_br (mix) or U."""
+    import torch
+    heads, d, _ = cov.shape
+    _check(load().oscar_calib_rotation(heads, d, _ptr(cov, "cov", torch.float32), int(bool(mix)),
+                                       _ptr(r, "r", torch.float32), _ptr(eigvals, "eigvals", torch.float32),
+                                       _stream(stream)),
+           "oscar_calib_rotation")
+    return r
+
+
+def oscar_calib_clip(x, r, quantile: float, tau, workspace=None, stream=None):
+    """tau[h] = quantile of |x[h] R[h]| (r None: of |x[h]|); x [heads, rows, D]."""
+    import torch
+    heads, rows, d = x.shape
+    px, hs, rs = _rows_view(x, "x")
+    if workspace is None:
+        workspace = _ws(_size_out("oscar_calib_clip_workspace_bytes", heads, rows, d), x.device)
+    _check(load().oscar_calib_clip(heads, rows, d, px, hs, rs, _ptr(r, "r", torch.float32), float(quantile),
+                                   _ptr(tau, "tau", torch.float32), _ptr(workspace, "workspace", torch.uint8),
+                                   workspace.numel(), _stream(stream)),
+           "oscar_calib_clip")
+    return tau
+
+
+def oscar_calibrate(q, k, v, clip_quantile: float = 0.995, sm_scale: float = 0.0, workspace=None, stream=None):
+    """The whole calibration of one layer on the GPU.  q [Hkv, g, N, D]
+    contiguous fp32; k, v [Hkv, N, D] fp32 views.  Returns a dict of device
+    tensors r_k, r_v [Hkv, D, D], tau_k, tau_v [Hkv], c_q, c_s [Hkv, D, D]."""
+    import torch
+    hkv, g, n, d = q.shape
+    pk, hs, ns = _rows_view(k, "k")
+    pv, hs2, ns2 = _rows_view(v, "v")
+    if (hs, ns) != (hs2, ns2):
+        raise ValueError("k and v must have the same strides")
+    dev = q.device
+    res = {name: torch.empty(hkv, d, d, dtype=torch.float32, device=dev) for name in ("r_k", "r_v", "c_q", "c_s")}
+    res["tau_k"] = torch.empty(hkv, dtype=torch.float32, device=dev)
+    res["tau_v"] = torch.empty(hkv, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _ws(_size_out("oscar_calib_workspace_bytes", hkv, g, n, d), dev)
+    _check(load().oscar_calibrate(
+        hkv, g, n, d, float(sm_scale), _ptr(q, "q", torch.float32), pk, pv, hs, ns, float(clip_quantile),
+        res["r_k"].data_ptr(), res["r_v"].data_ptr(), res["tau_k"].data_ptr(), res["tau_v"].data_ptr(),
+        res["c_q"].data_ptr(), res["c_s"].data_ptr(), _ptr(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)), "oscar_calibrate")
+    return res
+
+
+def oscar_dequantize(pool: OscarPool, num_tokens: int, page_ids, int2_pool, r_k, r_v, k_out, v_out, stream=None):
+    """INT2 history records of tokens 0..num_tokens-1 back to fp32
+    [num_tokens, Hkv, D]; r_k / r_v (or None) are the rotations to undo."""
+    import torch
+    _check(load().oscar_dequantize(
+        pool.handle, int(num_tokens), _ptr(page_ids, "page_ids", torch.int32), _pages(int2_pool, pool.int2_page_bytes),
+        _ptr(int2_pool, "int2_pool", torch.uint8), _ptr(r_k, "r_k", torch.float32), _ptr(r_v, "r_v", torch.float32),
+        _ptr(k_out, "k_out", torch.float32), _ptr(v_out, "v_out", torch.float32), _stream(stream)),
+        "oscar_dequantize")
+
+
+def oscar_attention_error(q, k, v, k_hat, v_hat, stats, sm_scale: float = 0.0, stream=None):
+    """Per causal query row of q [Hkv, g, N, D]: {KL(p || p^), summed squared
+    logit error, ||o - o^||^2, ||o||^2} into stats [Hkv, g, N, 4]; k, v,
+    k_hat, v_hat [Hkv, N, D] views sharing one set of strides."""
+    import torch
+    hkv, g, n, d = q.shape
+    views = [_rows_view(t, name) for t, name in ((k, "k"), (v, "v"), (k_hat, "k_hat"), (v_hat, "v_hat"))]
+    if len({(hs, ns) for _, hs, ns in views}) != 1:
+        raise ValueError("k, v, k_hat and v_hat must share strides")
+    _, hs, ns = views[0]
+    _check(load().oscar_attention_error(
+        hkv, g, n, d, float(sm_scale), _ptr(q, "q", torch.float32), views[0][0], views[1][0], views[2][0],
+        views[3][0], hs, ns, _ptr(stats, "stats", torch.float32), _stream(stream)), "oscar_attention_error")
+    return stats

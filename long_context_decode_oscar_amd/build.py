@@ -16,7 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liboscar.so")
-SOURCES = ["oscar_api.hip", "decode.hip", "write.hip"]
+SOURCES = ["oscar_api.hip", "decode.hip", "write.hip", "calib.hip"]
 ARCH = os.environ.get("OSCAR_OFFLOAD_ARCH", "gfx950")
 
 

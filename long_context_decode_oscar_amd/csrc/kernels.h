@@ -76,4 +76,66 @@ bool launch_quantize_pack(const WriteParams& p, int head_dim, int n_groups, hipS
 // through bf16_pt (one sequence)
 bool launch_write_bf16(const WriteParams& p, int head_dim, int first_position, hipStream_t stream);
 
+// ---- offline calibration and the rotation error chain (calib.hip) ----
+
+// out[h] = scale * X[h]^T X[h], X[h] row r at x + h*head_stride + r*row_stride
+struct GramParams {
+  const float* x;
+  int64_t head_stride, row_stride;  // elements
+  int32_t heads, rows;
+  int32_t rows_per_split, splits;   // rows_per_split a multiple of 16
+  float scale;
+  float* part;                      // [splits][heads][D][D] partial sums
+  float* out;                       // [heads][D][D]
+};
+bool launch_gram(GramParams p, int dim, hipStream_t stream);
+
+struct CalibAttnParams {
+  const float* q;                   // [kv_heads][gqa][tokens][D]
+  const float* k;                   // element (h, n, c) at h*kv_hs + n*kv_ns + c
+  const float* v;
+  const float* k_hat;               // error chain: quantized keys / values,
+  const float* v_hat;               // same strides
+  float* out;                       // attention: [kv_heads][gqa][tokens][D]
+  float* lse;                       // attention: [kv_heads][gqa][tokens] or null
+  float* stats;                     // error chain: [kv_heads][gqa][tokens][4]
+  int64_t kv_hs, kv_ns;
+  int32_t kv_heads, gqa, tokens;
+  float scale_log2;                 // softmax scale * log2(e)
+};
+bool launch_calib_attention(const CalibAttnParams& p, int dim, bool err, hipStream_t stream);
+
+struct EigParams {
+  const float* cov;                 // [heads][D][D] symmetric
+  float* r_out;                     // [heads][D][D]
+  float* eigvals;                   // [heads][D] descending, or null
+  int32_t heads, mix;               // mix: R = U H P_br, else R = U
+};
+bool launch_eigen_rotation(const EigParams& p, int dim, hipStream_t stream);
+
+struct ClipParams {
+  const float* x;                   // row r of head h at x + h*head_stride + r*row_stride
+  int64_t head_stride, row_stride;
+  int32_t heads, rows, dim;
+  const float* r;                   // [heads][D][D] or null (no rotation)
+  uint32_t* keys;                   // [heads][rows*D] workspace
+  uint32_t* hist;                   // [heads][chunks][2][256] workspace
+  uint32_t* sel;                    // [heads][2][2] workspace
+  float* tau;                       // [heads]
+  int32_t chunks;
+  uint32_t rank_lo, rank_hi;        // 0-based ranks of the two order statistics
+  double frac;                      // interpolation weight between them
+};
+bool launch_clip(const ClipParams& p, hipStream_t stream);
+
+struct DequantParams {
+  const int32_t* page_ids;          // [ceil(num_tokens / 16)]
+  const uint8_t* int2_pool;
+  const float* r;                   // [Hkv][D][D] rotation to undo, or null
+  float* out;                       // [num_tokens][Hkv][D]
+  int32_t num_tokens, int2_num_pages, num_kv_heads;
+  int32_t which;                    // 0: keys, 1: values
+};
+bool launch_dequantize(const DequantParams& p, int dim, int n_groups, hipStream_t stream);
+
 }  // namespace oscar

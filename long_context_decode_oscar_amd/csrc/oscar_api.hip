@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <new>
 #include <string>
 
@@ -134,6 +135,133 @@ Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
   pl.off_o = pl.off_lse + up(parts * sizeof(float));
   pl.bytes = pl.off_o + up(parts * c.head_dim * sizeof(float));
   return pl;
+}
+
+// ---- calibration helpers ----
+constexpr size_t kSpan = (size_t)1 << 31;
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool supported_dim(int d) { return d == 64 || d == 128; }
+
+// Row split of a gram: about 256 workgroups in all, each taking a multiple
+// of 16 rows; returns the rows per split and sets `splits` so that the
+// splits cover every row.
+int gram_rows_per_split(int heads, int rows, int* splits) {
+  const int blocks16 = (rows + 15) / 16;
+  const int want = std::min(std::max(1, 256 / std::max(1, heads)), std::max(1, blocks16));
+  const int rps = ((rows + want - 1) / want + 15) / 16 * 16;
+  *splits = (rows + rps - 1) / rps;
+  return rps;
+}
+int gram_splits(int heads, int rows) {
+  int s = 0;
+  gram_rows_per_split(heads, rows, &s);
+  return s;
+}
+size_t gram_ws(int heads, int rows, int d) { return (size_t)gram_splits(heads, rows) * heads * d * d * 4; }
+
+int clip_chunks(int heads) { return std::max(1, std::min(64, 256 / std::max(1, heads))); }
+struct ClipWs {
+  size_t keys, hist, sel, bytes;
+};
+ClipWs clip_ws(int heads, int rows, int d) {
+  ClipWs w;
+  w.keys = 0;
+  w.hist = up256((size_t)heads * rows * d * 4);
+  w.sel = w.hist + up256((size_t)heads * clip_chunks(heads) * 512 * 4);
+  w.bytes = w.sel + up256((size_t)heads * 16);
+  return w;
+}
+
+// x rows as used by gram / clip: one head's span must fit a buffer descriptor
+oscar_status check_rows(const char* what, const float* x, int heads, int rows, int d, int64_t head_stride,
+                        int64_t row_stride) {
+  if (heads <= 0 || rows <= 0) return fail(OSCAR_ERR_INVALID, "%s: heads and rows must be positive", what);
+  if (!supported_dim(d)) return fail(OSCAR_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128", what);
+  if (!x || !aligned16(x)) return fail(OSCAR_ERR_INVALID, "%s: x must be non-null and 16-byte aligned", what);
+  if (row_stride < d || row_stride % 4 || head_stride < 0 || head_stride % 4)
+    return fail(OSCAR_ERR_INVALID, "%s: row_stride must be >= head_dim and strides multiples of 4", what);
+  if ((size_t)rows * (size_t)row_stride * 4 >= kSpan) return fail(OSCAR_ERR_UNSUPPORTED, "%s: head span >= 2 GiB", what);
+  return OSCAR_OK;
+}
+
+// calibration attention arguments (shared by oscar_calib_attention and
+// oscar_attention_error)
+oscar_status check_attn(int kv_heads, int gqa, int tokens, int d, const float* q, const float* k, const float* v,
+                        int64_t hs, int64_t ns) {
+  if (kv_heads <= 0 || gqa <= 0 || tokens <= 0)
+    return fail(OSCAR_ERR_INVALID, "kv_heads, gqa and tokens must be positive");
+  if (!supported_dim(d)) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!q || !k || !v || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(OSCAR_ERR_INVALID, "q, k and v must be non-null and 16-byte aligned");
+  if (ns < d || ns % 4 || hs < 0 || hs % 4)
+    return fail(OSCAR_ERR_INVALID, "kv_token_stride must be >= head_dim and strides multiples of 4");
+  if ((size_t)tokens * d * 4 >= kSpan || (size_t)tokens * (size_t)ns * 4 >= kSpan)
+    return fail(OSCAR_ERR_UNSUPPORTED, "per-head span >= 2 GiB");
+  return OSCAR_OK;
+}
+
+float attn_scale_log2(float sm, int d) { return (sm > 0.f ? sm : 1.f / sqrtf((float)d)) * 1.4426950408889634f; }
+
+oscar_status run_gram(int heads, int rows, int d, const float* x, int64_t hs, int64_t rs, float scale, float* out,
+                      void* ws, hipStream_t stream) {
+  oscar::GramParams p{};
+  p.x = x;
+  p.head_stride = hs;
+  p.row_stride = rs;
+  p.heads = heads;
+  p.rows = rows;
+  p.rows_per_split = gram_rows_per_split(heads, rows, &p.splits);
+  p.scale = scale;
+  p.part = (float*)ws;
+  p.out = out;
+  if (!oscar::launch_gram(p, d, stream)) return fail(OSCAR_ERR_UNSUPPORTED, "no gram kernel for this shape");
+  return check_hip("gram launch");
+}
+
+oscar_status run_clip(int heads, int rows, int d, const float* x, int64_t hs, int64_t rs, const float* r,
+                      double quantile, float* tau, void* ws, hipStream_t stream) {
+  const ClipWs w = clip_ws(heads, rows, d);
+  oscar::ClipParams p{};
+  p.x = x;
+  p.head_stride = hs;
+  p.row_stride = rs;
+  p.heads = heads;
+  p.rows = rows;
+  p.dim = d;
+  p.r = r;
+  p.keys = (uint32_t*)((char*)ws + w.keys);
+  p.hist = (uint32_t*)((char*)ws + w.hist);
+  p.sel = (uint32_t*)((char*)ws + w.sel);
+  p.tau = tau;
+  p.chunks = clip_chunks(heads);
+  const double m = (double)rows * d;
+  const double hpos = (m - 1.0) * quantile;
+  const double lo = floor(hpos);
+  p.rank_lo = (uint32_t)lo;
+  p.rank_hi = (uint32_t)std::min(lo + 1.0, m - 1.0);
+  p.frac = hpos - lo;
+  if (!oscar::launch_clip(p, stream)) return fail(OSCAR_ERR_UNSUPPORTED, "no clip kernel for this shape");
+  return check_hip("clip launch");
+}
+
+oscar_status run_rotation(int heads, int d, const float* cov, int mix, float* r, float* eig, hipStream_t stream) {
+  oscar::EigParams p{cov, r, eig, heads, mix};
+  if (!oscar::launch_eigen_rotation(p, d, stream)) return fail(OSCAR_ERR_UNSUPPORTED, "eigen kernel unavailable");
+  return check_hip("eigen/rotation launch");
+}
+
+struct CalibWs {
+  size_t part, o, cq, cs, clip, bytes;
+};
+CalibWs calib_ws(int hkv, int gqa, int n, int d) {
+  CalibWs w;
+  w.part = 0;
+  w.o = up256(gram_ws(hkv, gqa * n, d));
+  w.cq = w.o + up256((size_t)hkv * gqa * n * d * 4);
+  w.cs = w.cq + up256((size_t)hkv * d * d * 4);
+  w.clip = w.cs + up256((size_t)hkv * d * d * 4);
+  w.bytes = w.clip + clip_ws(hkv, n, d).bytes;
+  return w;
 }
 
 }  // namespace
@@ -433,6 +561,174 @@ oscar_status oscar_write_bf16(const oscar_pool* pool, int32_t num_tokens, int32_
   if (!oscar::launch_write_bf16(p, pool->cfg.head_dim, first_position, (hipStream_t)stream))
     return fail(OSCAR_ERR_UNSUPPORTED, "no BF16 writer for this shape");
   return check_hip("bf16 write launch");
+}
+
+oscar_status oscar_calib_gram_workspace_bytes(int32_t heads, int32_t rows, int32_t head_dim, size_t* bytes) {
+  if (!bytes || heads <= 0 || rows <= 0) return fail(OSCAR_ERR_INVALID, "bytes must be non-null, heads and rows positive");
+  if (!supported_dim(head_dim)) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  *bytes = gram_ws(heads, rows, head_dim);
+  return ok();
+}
+
+oscar_status oscar_calib_gram(int32_t heads, int32_t rows, int32_t head_dim, const float* x, int64_t head_stride,
+                              int64_t row_stride, float scale, float* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  oscar_status st = check_rows("gram", x, heads, rows, head_dim, head_stride, row_stride);
+  if (st != OSCAR_OK) return st;
+  if (!out) return fail(OSCAR_ERR_INVALID, "out must be non-null");
+  if (!workspace || workspace_bytes < gram_ws(heads, rows, head_dim))
+    return fail(OSCAR_ERR_WORKSPACE, "gram needs %zu bytes of workspace", gram_ws(heads, rows, head_dim));
+  return run_gram(heads, rows, head_dim, x, head_stride, row_stride, scale, out, workspace, (hipStream_t)stream);
+}
+
+oscar_status oscar_calib_attention(int32_t kv_heads, int32_t gqa, int32_t tokens, int32_t head_dim, float sm_scale,
+                                   const float* q, const float* k, const float* v, int64_t kv_head_stride,
+                                   int64_t kv_token_stride, float* out, float* lse, void* stream) {
+  oscar_status st = check_attn(kv_heads, gqa, tokens, head_dim, q, k, v, kv_head_stride, kv_token_stride);
+  if (st != OSCAR_OK) return st;
+  if (!out || !aligned16(out)) return fail(OSCAR_ERR_INVALID, "out must be non-null and 16-byte aligned");
+  oscar::CalibAttnParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.kv_hs = kv_head_stride;
+  p.kv_ns = kv_token_stride;
+  p.kv_heads = kv_heads;
+  p.gqa = gqa;
+  p.tokens = tokens;
+  p.scale_log2 = attn_scale_log2(sm_scale, head_dim);
+  if (!oscar::launch_calib_attention(p, head_dim, false, (hipStream_t)stream))
+    return fail(OSCAR_ERR_UNSUPPORTED, "no calibration attention kernel for this shape");
+  return check_hip("calibration attention launch");
+}
+
+oscar_status oscar_calib_rotation(int32_t heads, int32_t head_dim, const float* cov, int32_t mix, float* r,
+                                  float* eigvals, void* stream) {
+  if (heads <= 0) return fail(OSCAR_ERR_INVALID, "heads must be positive");
+  if (!supported_dim(head_dim)) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!cov || !r) return fail(OSCAR_ERR_INVALID, "cov and r must be non-null");
+  if (mix != 0 && mix != 1) return fail(OSCAR_ERR_INVALID, "mix must be 0 or 1");
+  return run_rotation(heads, head_dim, cov, mix, r, eigvals, (hipStream_t)stream);
+}
+
+oscar_status oscar_calib_clip_workspace_bytes(int32_t heads, int32_t rows, int32_t head_dim, size_t* bytes) {
+  if (!bytes || heads <= 0 || rows <= 0) return fail(OSCAR_ERR_INVALID, "bytes must be non-null, heads and rows positive");
+  if (!supported_dim(head_dim)) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  *bytes = clip_ws(heads, rows, head_dim).bytes;
+  return ok();
+}
+
+oscar_status oscar_calib_clip(int32_t heads, int32_t rows, int32_t head_dim, const float* x, int64_t head_stride,
+                              int64_t row_stride, const float* r, double quantile, float* tau, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  oscar_status st = check_rows("clip", x, heads, rows, head_dim, head_stride, row_stride);
+  if (st != OSCAR_OK) return st;
+  if (!tau) return fail(OSCAR_ERR_INVALID, "tau must be non-null");
+  if (!(quantile >= 0.0 && quantile <= 1.0)) return fail(OSCAR_ERR_INVALID, "quantile must be in [0, 1]");
+  if ((size_t)rows * head_dim >= ((size_t)1 << 32)) return fail(OSCAR_ERR_UNSUPPORTED, "too many values per head");
+  const size_t need = clip_ws(heads, rows, head_dim).bytes;
+  if (!workspace || workspace_bytes < need) return fail(OSCAR_ERR_WORKSPACE, "clip needs %zu bytes of workspace", need);
+  return run_clip(heads, rows, head_dim, x, head_stride, row_stride, r, quantile, tau, workspace,
+                  (hipStream_t)stream);
+}
+
+oscar_status oscar_calib_workspace_bytes(int32_t kv_heads, int32_t gqa, int32_t tokens, int32_t head_dim,
+                                         size_t* bytes) {
+  if (!bytes || kv_heads <= 0 || gqa <= 0 || tokens <= 0)
+    return fail(OSCAR_ERR_INVALID, "bytes must be non-null, kv_heads, gqa and tokens positive");
+  if (!supported_dim(head_dim)) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  *bytes = calib_ws(kv_heads, gqa, tokens, head_dim).bytes;
+  return ok();
+}
+
+oscar_status oscar_calibrate(int32_t kv_heads, int32_t gqa, int32_t tokens, int32_t head_dim, float sm_scale,
+                             const float* q, const float* k, const float* v, int64_t kv_head_stride,
+                             int64_t kv_token_stride, double clip_quantile, float* r_k, float* r_v, float* tau_k,
+                             float* tau_v, float* c_q, float* c_s, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  oscar_status st = check_attn(kv_heads, gqa, tokens, head_dim, q, k, v, kv_head_stride, kv_token_stride);
+  if (st != OSCAR_OK) return st;
+  if (!r_k || !r_v || !tau_k || !tau_v) return fail(OSCAR_ERR_INVALID, "r_k, r_v, tau_k and tau_v must be non-null");
+  if (!(clip_quantile >= 0.0 && clip_quantile <= 1.0)) return fail(OSCAR_ERR_INVALID, "clip_quantile must be in [0, 1]");
+  const int rows = gqa * tokens;
+  if ((size_t)rows * head_dim * 4 >= kSpan) return fail(OSCAR_ERR_UNSUPPORTED, "per-head query span >= 2 GiB");
+  const CalibWs w = calib_ws(kv_heads, gqa, tokens, head_dim);
+  if (!workspace || workspace_bytes < w.bytes || ((uintptr_t)workspace & 255u))
+    return fail(OSCAR_ERR_WORKSPACE, "calibration needs %zu bytes of 256-byte aligned workspace", w.bytes);
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  float* cq = c_q ? c_q : (float*)(ws + w.cq);
+  float* cs = c_s ? c_s : (float*)(ws + w.cs);
+  float* o = (float*)(ws + w.o);
+  const int64_t qhs = (int64_t)rows * head_dim;
+  const float inv_rows = 1.f / (float)rows;
+  if ((st = run_gram(kv_heads, rows, head_dim, q, qhs, head_dim, inv_rows, cq, ws + w.part, s)) != OSCAR_OK) return st;
+  if ((st = run_rotation(kv_heads, head_dim, cq, 1, r_k, nullptr, s)) != OSCAR_OK) return st;
+  st = oscar_calib_attention(kv_heads, gqa, tokens, head_dim, sm_scale, q, k, v, kv_head_stride, kv_token_stride, o,
+                             nullptr, stream);
+  if (st != OSCAR_OK) return st;
+  if ((st = run_gram(kv_heads, rows, head_dim, o, qhs, head_dim, inv_rows, cs, ws + w.part, s)) != OSCAR_OK) return st;
+  if ((st = run_rotation(kv_heads, head_dim, cs, 1, r_v, nullptr, s)) != OSCAR_OK) return st;
+  if ((st = run_clip(kv_heads, tokens, head_dim, k, kv_head_stride, kv_token_stride, r_k, clip_quantile, tau_k,
+                     ws + w.clip, s)) != OSCAR_OK)
+    return st;
+  return run_clip(kv_heads, tokens, head_dim, v, kv_head_stride, kv_token_stride, r_v, clip_quantile, tau_v,
+                  ws + w.clip, s);
+}
+
+oscar_status oscar_dequantize(const oscar_pool* pool, int32_t num_tokens, const int32_t* page_ids,
+                              int32_t int2_num_pages, const void* int2_pool, const float* r_k, const float* r_v,
+                              float* k_out, float* v_out, void* stream) {
+  if (!pool) return fail(OSCAR_ERR_INVALID, "pool must be non-null");
+  if (num_tokens < 0) return fail(OSCAR_ERR_INVALID, "negative num_tokens");
+  if (num_tokens == 0) return ok();
+  if (!page_ids || !int2_pool || !k_out || !v_out || int2_num_pages <= 0)
+    return fail(OSCAR_ERR_INVALID, "page_ids, int2_pool, k_out, v_out and int2_num_pages must be given");
+  if (!aligned16(int2_pool)) return fail(OSCAR_ERR_INVALID, "int2_pool must be 16-byte aligned");
+  const oscar_config& c = pool->cfg;
+  oscar::DequantParams p{};
+  p.page_ids = page_ids;
+  p.int2_pool = (const uint8_t*)int2_pool;
+  p.num_tokens = num_tokens;
+  p.int2_num_pages = int2_num_pages;
+  p.num_kv_heads = c.num_kv_heads;
+  for (int which = 0; which < 2; ++which) {
+    p.which = which;
+    p.r = which ? r_v : r_k;
+    p.out = which ? v_out : k_out;
+    if (!oscar::launch_dequantize(p, c.head_dim, pool->n_groups, (hipStream_t)stream))
+      return fail(OSCAR_ERR_UNSUPPORTED, "no dequantize kernel for this shape");
+  }
+  return check_hip("dequantize launch");
+}
+
+oscar_status oscar_attention_error(int32_t kv_heads, int32_t gqa, int32_t tokens, int32_t head_dim, float sm_scale,
+                                   const float* q, const float* k, const float* v, const float* k_hat,
+                                   const float* v_hat, int64_t kv_head_stride, int64_t kv_token_stride,
+                                   float* stats, void* stream) {
+  oscar_status st = check_attn(kv_heads, gqa, tokens, head_dim, q, k, v, kv_head_stride, kv_token_stride);
+  if (st != OSCAR_OK) return st;
+  if (!k_hat || !v_hat || !aligned16(k_hat) || !aligned16(v_hat))
+    return fail(OSCAR_ERR_INVALID, "k_hat and v_hat must be non-null and 16-byte aligned");
+  if (!stats || !aligned16(stats)) return fail(OSCAR_ERR_INVALID, "stats must be non-null and 16-byte aligned");
+  oscar::CalibAttnParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.k_hat = k_hat;
+  p.v_hat = v_hat;
+  p.stats = stats;
+  p.kv_hs = kv_head_stride;
+  p.kv_ns = kv_token_stride;
+  p.kv_heads = kv_heads;
+  p.gqa = gqa;
+  p.tokens = tokens;
+  p.scale_log2 = attn_scale_log2(sm_scale, head_dim);
+  if (!oscar::launch_calib_attention(p, head_dim, true, (hipStream_t)stream))
+    return fail(OSCAR_ERR_UNSUPPORTED, "no attention error kernel for this shape");
+  return check_hip("attention error launch");
 }
 
 }  // extern "C"

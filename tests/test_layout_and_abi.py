@@ -170,3 +170,50 @@ def test_decode_validation_fails_before_launch():
         oscar.OSCAR_ERR_INVALID
     assert lib.oscar_bf16_decode_attention(p.handle, 1, 100, F, F, F, 8, 4, F, F, F, 0, None) == \
         oscar.OSCAR_ERR_WORKSPACE
+
+
+def test_calibration_validation_fails_before_launch():
+    import long_context_decode_oscar_amd as oscar
+    lib = oscar.load()
+    F = 1 << 20  # fake, aligned, never-dereferenced addresses
+    n = ctypes.c_size_t()
+    assert lib.oscar_calib_gram_workspace_bytes(8, 8192, 128, ctypes.byref(n)) == oscar.OSCAR_OK
+    assert n.value >= 8 * 128 * 128 * 4
+    assert lib.oscar_calib_gram_workspace_bytes(8, 8192, 96, ctypes.byref(n)) == oscar.OSCAR_ERR_UNSUPPORTED
+    assert lib.oscar_calib_clip_workspace_bytes(8, 2048, 128, ctypes.byref(n)) == oscar.OSCAR_OK
+    assert n.value >= 8 * 2048 * 128 * 4  # one key per rotated value
+    assert lib.oscar_calib_workspace_bytes(8, 4, 2048, 128, ctypes.byref(n)) == oscar.OSCAR_OK
+    assert n.value >= 8 * 4 * 2048 * 128 * 4  # the attention outputs
+    # gram: bad dims, null input, strides, workspace
+    assert lib.oscar_calib_gram(8, 64, 96, F, 64 * 96, 96, 1.0, F, F, 1 << 30, None) == oscar.OSCAR_ERR_UNSUPPORTED
+    assert lib.oscar_calib_gram(8, 64, 128, None, 64 * 128, 128, 1.0, F, F, 1 << 30, None) == oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_calib_gram(8, 64, 128, F, 64 * 128, 100, 1.0, F, F, 1 << 30, None) == oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_calib_gram(8, 64, 128, F, 64 * 128, 128, 1.0, F, F, 16, None) == oscar.OSCAR_ERR_WORKSPACE
+    assert lib.oscar_calib_gram(1, 1 << 22, 128, F, 0, 128, 1.0, F, F, 1 << 40, None) == \
+        oscar.OSCAR_ERR_UNSUPPORTED  # a 2 GiB head span
+    # attention: shapes, alignment, strides
+    assert lib.oscar_calib_attention(8, 4, 0, 128, 0.0, F, F, F, 2048 * 128, 128, F, None, None) == \
+        oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_calib_attention(8, 4, 64, 128, 0.0, F + 4, F, F, 64 * 128, 128, F, None, None) == \
+        oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_calib_attention(8, 4, 64, 128, 0.0, F, F, F, 64 * 128, 64, F, None, None) == \
+        oscar.OSCAR_ERR_INVALID  # token stride below head_dim
+    assert lib.oscar_calib_attention(8, 4, 64, 128, 0.0, F, F, F, 64 * 128, 128, None, None, None) == \
+        oscar.OSCAR_ERR_INVALID
+    # rotation / clip / whole calibration
+    assert lib.oscar_calib_rotation(8, 128, F, 2, F, None, None) == oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_calib_rotation(8, 32, F, 1, F, None, None) == oscar.OSCAR_ERR_UNSUPPORTED
+    assert lib.oscar_calib_clip(8, 64, 128, F, 64 * 128, 128, None, 1.5, F, F, 1 << 30, None) == \
+        oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_calib_clip(8, 64, 128, F, 64 * 128, 128, None, 0.995, F, F, 64, None) == \
+        oscar.OSCAR_ERR_WORKSPACE
+    assert lib.oscar_calibrate(8, 4, 64, 128, 0.0, F, F, F, 64 * 128, 128, 0.995, F, F, F, F, None, None, F + 64,
+                               1 << 30, None) == oscar.OSCAR_ERR_WORKSPACE  # misaligned workspace
+    assert lib.oscar_calibrate(8, 4, 64, 128, 0.0, F, F, F, 64 * 128, 128, 0.995, None, F, F, F, None, None, F,
+                               1 << 30, None) == oscar.OSCAR_ERR_INVALID
+    # dequantize / error chain
+    p = oscar.OscarPool(_cfg())
+    assert lib.oscar_dequantize(p.handle, 32, F, 0, F, None, None, F, F, None) == oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_dequantize(p.handle, 0, None, 0, None, None, None, None, None, None) == oscar.OSCAR_OK
+    assert lib.oscar_attention_error(8, 4, 64, 128, 0.0, F, F, F, None, F, 64 * 128, 128, F, None) == \
+        oscar.OSCAR_ERR_INVALID
