@@ -337,8 +337,10 @@ __device__ __forceinline__ void tournament_pair(int r, int k, int& a, int& b) {
     a = D - 1;
     b = r;
   } else {
-    a = (r + k) % (D - 1);
-    b = (r - k + D - 1) % (D - 1);
+    a = r + k;
+    a -= a >= D - 1 ? D - 1 : 0;
+    b = r - k;
+    b += b < 0 ? D - 1 : 0;
   }
 }
 
@@ -347,6 +349,7 @@ struct EigSmem {
   float w[D * D];  // column-major working matrix W = C V (later U)
   float v[D * D];  // column-major accumulated rotations V
   float lam[D];
+  float nrm[D];  // squared column norms of W during a sweep
   int pos[D];
   int rotated;
 };
@@ -354,12 +357,15 @@ struct EigSmem {
 template <int D>
 __global__ void __launch_bounds__(64 * (D / 8)) k_eigen_rotation(const EigParams p) {
   constexpr int NTHR = 64 * (D / 8);
-  constexpr int RL = D / 64;        // rows per lane
-  constexpr int PPW = 4;            // pairs per wave per round (D/2 pairs, D/8 waves)
+  constexpr int RL = D / 64;        // rows per lane in whole-wave loops; 16-byte pieces per lane in sweeps
+  constexpr int PPW = 4;            // pairs per wave per round (D/2 pairs, D/8 waves), one per 16-lane row
   extern __shared__ __align__(16) unsigned char smem_raw[];
   EigSmem<D>& sm = *reinterpret_cast<EigSmem<D>*>(smem_raw);
   const int h = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const float* c = p.cov + (size_t)h * D * D;
+  const bool second = h >= p.split;
+  const int hm = second ? h - p.split : h;
+  const float* c = (second ? p.cov2 : p.cov) + (size_t)hm * D * D;
+  float* const eigvals = second ? p.eigvals2 : p.eigvals;
   for (int e = tid; e < D * D; e += NTHR) {
     const int row = e / D, cl = e % D;
     sm.w[cl * D + row] = c[e];
@@ -394,45 +400,59 @@ __global__ void __launch_bounds__(64 * (D / 8)) k_eigen_rotation(const EigParams
     __syncthreads();
   }
   for (int sweep = 0; sweep < (phase == 0 ? kMaxSweeps : kRefineSweeps); ++sweep) {
+    // exact squared column norms at the start of every sweep; within the
+    // sweep a rotation updates them as alpha - t gamma and beta + t gamma
+    for (int i = wave; i < D; i += D / 8) {
+      float sq = 0.f;
+#pragma unroll
+      for (int u = 0; u < RL; ++u) sq += sm.w[i * D + lane + 64 * u] * sm.w[i * D + lane + 64 * u];
+      sq = wave_sum(sq);
+      if (lane == 0) sm.nrm[i] = sq;
+    }
     if (tid == 0) sm.rotated = 0;
     __syncthreads();
     int any = 0;
+    // each 16-lane row of a wave owns one pair per round; lane sl of the row
+    // holds rows 4 sl + 64 j + e (e < 4) of the pair's columns, so a row of
+    // lanes reads a column as contiguous 16-byte pieces
+    const int grp = lane >> 4, sl = lane & 15;
     for (int r = 0; r < D - 1; ++r) {
-      float al[PPW], be[PPW], ga[PPW];
-      int pa[PPW], pb[PPW];
+      int pa, pb;
+      tournament_pair<D>(r, wave * PPW + grp, pa, pb);
+      v4f xa[RL], xb[RL];
+      float sg = 0.f;
 #pragma unroll
-      for (int k = 0; k < PPW; ++k) {
-        tournament_pair<D>(r, wave * PPW + k, pa[k], pb[k]);
-        float sa = 0.f, sb = 0.f, sg = 0.f;
+      for (int j = 0; j < RL; ++j) {
+        xa[j] = *(const v4f*)&sm.w[pa * D + 64 * j + 4 * sl];
+        xb[j] = *(const v4f*)&sm.w[pb * D + 64 * j + 4 * sl];
 #pragma unroll
-        for (int u = 0; u < RL; ++u) {
-          const float x = sm.w[pa[k] * D + lane + 64 * u], y = sm.w[pb[k] * D + lane + 64 * u];
-          sa += x * x;
-          sb += y * y;
-          sg += x * y;
-        }
-        al[k] = wave_sum(sa);
-        be[k] = wave_sum(sb);
-        ga[k] = wave_sum(sg);
+        for (int e = 0; e < 4; ++e) sg = fmaf(xa[j][e], xb[j][e], sg);
       }
+      sg += dpp_row_ror<8>(sg);
+      sg += dpp_row_ror<4>(sg);
+      sg += dpp_row_ror<2>(sg);
+      const float ga = sg + dpp_row_ror<1>(sg);
+      const float al = sm.nrm[pa], be = sm.nrm[pb];
+      if (fabsf(ga) > kJacobiTol * __builtin_amdgcn_sqrtf(al * be) && ga != 0.f) {
+        any = 1;
+        const float zeta = (be - al) * __builtin_amdgcn_rcpf(2.f * ga);
+        const float az = fabsf(zeta);
+        const float t = copysignf(az > 1.0e18f ? 0.5f * __builtin_amdgcn_rcpf(az)
+                                               : __builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(1.f + az * az)),
+                                  zeta);
+        const float cs = __builtin_amdgcn_rsqf(1.f + t * t), sn = cs * t;
 #pragma unroll
-      for (int k = 0; k < PPW; ++k) {
-        if (fabsf(ga[k]) > kJacobiTol * sqrtf(al[k] * be[k]) && ga[k] != 0.f) {
-          any = 1;
-          const float zeta = (be[k] - al[k]) / (2.f * ga[k]);
-          const float t = fabsf(zeta) > 1.0e18f ? 0.5f / zeta
-                                                 : copysignf(1.f, zeta) / (fabsf(zeta) + sqrtf(1.f + zeta * zeta));
-          const float cs = 1.f / sqrtf(1.f + t * t), sn = cs * t;
-#pragma unroll
-          for (int u = 0; u < RL; ++u) {
-            const int ia = pa[k] * D + lane + 64 * u, ib = pb[k] * D + lane + 64 * u;
-            const float x = sm.w[ia], y = sm.w[ib];
-            sm.w[ia] = cs * x - sn * y;
-            sm.w[ib] = sn * x + cs * y;
-            const float vx = sm.v[ia], vy = sm.v[ib];
-            sm.v[ia] = cs * vx - sn * vy;
-            sm.v[ib] = sn * vx + cs * vy;
-          }
+        for (int j = 0; j < RL; ++j) {
+          const int ia = pa * D + 64 * j + 4 * sl, ib = pb * D + 64 * j + 4 * sl;
+          const v4f va = *(const v4f*)&sm.v[ia], vb = *(const v4f*)&sm.v[ib];
+          *(v4f*)&sm.w[ia] = cs * xa[j] - sn * xb[j];
+          *(v4f*)&sm.w[ib] = sn * xa[j] + cs * xb[j];
+          *(v4f*)&sm.v[ia] = cs * va - sn * vb;
+          *(v4f*)&sm.v[ib] = sn * va + cs * vb;
+        }
+        if (sl == 0) {
+          sm.nrm[pa] = al - t * ga;
+          sm.nrm[pb] = be + t * ga;
         }
       }
       __syncthreads();
@@ -494,7 +514,7 @@ __global__ void __launch_bounds__(64 * (D / 8)) k_eigen_rotation(const EigParams
     const int i = e / D, row = e % D;
     sm.w[sm.pos[i] * D + row] = sm.v[i * D + row];
   }
-  if (p.eigvals && tid < D) p.eigvals[(size_t)h * D + sm.pos[tid]] = sm.lam[tid];
+  if (eigvals && tid < D) eigvals[(size_t)hm * D + sm.pos[tid]] = sm.lam[tid];
   __syncthreads();
   if (p.mix) {
     // rows of U times the Sylvester Hadamard matrix: butterflies over the
@@ -512,7 +532,7 @@ __global__ void __launch_bounds__(64 * (D / 8)) k_eigen_rotation(const EigParams
   }
   const float norm = p.mix ? 1.f / sqrtf((float)D) : 1.f;
   constexpr int LOG = D == 128 ? 7 : 6;
-  float* out = p.r_out + (size_t)h * D * D;
+  float* out = (second ? p.r_out2 : p.r_out) + (size_t)hm * D * D;
   for (int e = tid; e < D * D; e += NTHR) {
     const int row = e / D, j = e % D;
     // output column j takes column br(j) of U H
@@ -609,31 +629,43 @@ __global__ void __launch_bounds__(256) k_select_hist(const ClipParams p, int pas
 // each target rank, extend the prefix.  The last pass turns the two order
 // statistics into tau = a + t (b - a) (fp64, rounded to fp32).
 __global__ void __launch_bounds__(256) k_select_scan(const ClipParams p, int pass, int chunks) {
-  __shared__ uint32_t tot[2][256];
+  __shared__ uint32_t cum[2][256];
   __shared__ uint32_t res[2][2];
   const int h = blockIdx.x, tid = threadIdx.x;
-  for (int t = 0; t < 2; ++t) {
-    uint32_t s = 0;
-    for (int c = 0; c < chunks; ++c) s += p.hist[((size_t)h * chunks + c) * 512 + t * 256 + tid];
-    tot[t][tid] = s;
+  uint32_t tot[2] = {0u, 0u};
+  const uint32_t* hp = p.hist + (size_t)h * chunks * 512 + tid;
+#pragma unroll 8
+  for (int c = 0; c < chunks; ++c) {
+    tot[0] += hp[(size_t)c * 512];
+    tot[1] += hp[(size_t)c * 512 + 256];
   }
+  cum[0][tid] = tot[0];
+  cum[1][tid] = tot[1];
   __syncthreads();
-  if (tid < 2) {
+  // inclusive prefix sums over the 256 digits
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t a = cum[0][tid] + (tid >= off ? cum[0][tid - off] : 0u);
+    const uint32_t b = cum[1][tid] + (tid >= off ? cum[1][tid - off] : 0u);
+    __syncthreads();
+    cum[0][tid] = a;
+    cum[1][tid] = b;
+    __syncthreads();
+  }
+  for (int t = 0; t < 2; ++t) {
     uint32_t prefix, rank;
     if (pass == 0) {
       prefix = 0;
-      rank = tid == 0 ? p.rank_lo : p.rank_hi;
+      rank = t == 0 ? p.rank_lo : p.rank_hi;
     } else {
-      prefix = p.sel[(h * 2 + tid) * 2];
-      rank = p.sel[(h * 2 + tid) * 2 + 1];
+      prefix = p.sel[(h * 2 + t) * 2];
+      rank = p.sel[(h * 2 + t) * 2 + 1];
     }
-    uint32_t cum = 0, d = 0;
-    for (; d < 255; ++d) {
-      if (rank < cum + tot[tid][d]) break;
-      cum += tot[tid][d];
+    const uint32_t below = cum[t][tid] - tot[t];
+    // the digit whose bucket holds the rank (the last digit takes any rest)
+    if (below <= rank && (rank < cum[t][tid] || tid == 255)) {
+      res[t][0] = (prefix << 8) | (uint32_t)tid;
+      res[t][1] = rank - below;
     }
-    res[tid][0] = (prefix << 8) | d;
-    res[tid][1] = rank - cum;
   }
   __syncthreads();
   if (tid < 2) {

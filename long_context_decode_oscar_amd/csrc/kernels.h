@@ -105,11 +105,17 @@ struct CalibAttnParams {
 };
 bool launch_calib_attention(const CalibAttnParams& p, int dim, bool err, hipStream_t stream);
 
+// Workgroup h < split takes matrix h of cov / r_out / eigvals, workgroup
+// h >= split matrix h - split of cov2 / r_out2 / eigvals2 (two sets of
+// matrices in one launch).
 struct EigParams {
-  const float* cov;                 // [heads][D][D] symmetric
-  float* r_out;                     // [heads][D][D]
-  float* eigvals;                   // [heads][D] descending, or null
-  int32_t heads, mix;               // mix: R = U H P_br, else R = U
+  const float* cov;                 // [split][D][D] symmetric
+  float* r_out;                     // [split][D][D]
+  float* eigvals;                   // [split][D] descending, or null
+  const float* cov2;                // [heads - split][D][D] (if heads > split)
+  float* r_out2;
+  float* eigvals2;
+  int32_t heads, split, mix;        // mix: R = U H P_br, else R = U
 };
 bool launch_eigen_rotation(const EigParams& p, int dim, hipStream_t stream);
 

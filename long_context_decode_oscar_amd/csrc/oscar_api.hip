@@ -244,8 +244,11 @@ oscar_status run_clip(int heads, int rows, int d, const float* x, int64_t hs, in
   return check_hip("clip launch");
 }
 
-oscar_status run_rotation(int heads, int d, const float* cov, int mix, float* r, float* eig, hipStream_t stream) {
-  oscar::EigParams p{cov, r, eig, heads, mix};
+// Eigenbases of `heads` matrices of cov (and, with heads2 > 0, of heads2
+// more from cov2) in one launch.
+oscar_status run_rotation(int heads, int d, const float* cov, int mix, float* r, float* eig, hipStream_t stream,
+                          int heads2 = 0, const float* cov2 = nullptr, float* r2 = nullptr) {
+  oscar::EigParams p{cov, r, eig, cov2, r2, nullptr, heads + heads2, heads, mix};
   if (!oscar::launch_eigen_rotation(p, d, stream)) return fail(OSCAR_ERR_UNSUPPORTED, "eigen kernel unavailable");
   return check_hip("eigen/rotation launch");
 }
@@ -665,12 +668,12 @@ oscar_status oscar_calibrate(int32_t kv_heads, int32_t gqa, int32_t tokens, int3
   const int64_t qhs = (int64_t)rows * head_dim;
   const float inv_rows = 1.f / (float)rows;
   if ((st = run_gram(kv_heads, rows, head_dim, q, qhs, head_dim, inv_rows, cq, ws + w.part, s)) != OSCAR_OK) return st;
-  if ((st = run_rotation(kv_heads, head_dim, cq, 1, r_k, nullptr, s)) != OSCAR_OK) return st;
   st = oscar_calib_attention(kv_heads, gqa, tokens, head_dim, sm_scale, q, k, v, kv_head_stride, kv_token_stride, o,
                              nullptr, stream);
   if (st != OSCAR_OK) return st;
   if ((st = run_gram(kv_heads, rows, head_dim, o, qhs, head_dim, inv_rows, cs, ws + w.part, s)) != OSCAR_OK) return st;
-  if ((st = run_rotation(kv_heads, head_dim, cs, 1, r_v, nullptr, s)) != OSCAR_OK) return st;
+  // both eigenbases in one launch (one workgroup per matrix)
+  if ((st = run_rotation(kv_heads, head_dim, cq, 1, r_k, nullptr, s, kv_heads, cs, r_v)) != OSCAR_OK) return st;
   if ((st = run_clip(kv_heads, tokens, head_dim, k, kv_head_stride, kv_token_stride, r_k, clip_quantile, tau_k,
                      ws + w.clip, s)) != OSCAR_OK)
     return st;

@@ -13,10 +13,14 @@ Tolerances (fp32 arithmetic in the kernels, fp64 in the oracle):
     where the column's two largest magnitudes differ by >= 1e-3;
   * clip thresholds: exactly the oracle's order statistics without rotation
     (within one fp32 ulp of numpy's quantile); 1e-5 relative with a given
-    rotation; 5e-4 relative at the end of the whole calibration, where R is
-    the library's own: the eigenvectors of clustered small eigenvalues are
-    only defined to ~eps * lambda_max / gap, and the fp32 covariance alone
-    moves tau by up to ~1e-4 (the same Jacobi emulated in numpy fp32 does);
+    rotation; at the end of the whole calibration, where R is the library's
+    own, 1e-5 relative to the quantile of |x R| for that R, and 5e-4 relative
+    to the oracle's tau when every column of U has the oracle's sign: the
+    eigenvectors of clustered small eigenvalues are only defined to
+    ~eps * lambda_max / gap, and the fp32 covariance alone moves tau by up to
+    ~1e-4 (the same Jacobi emulated in numpy fp32 does).  A column whose two
+    largest magnitudes differ by less than its fp32 accuracy may take either
+    sign (several results are correct); then only the property is checked;
   * dequantization: 1e-5 relative to each vector's norm; error statistics:
     KL to 2e-5 + 2e-3 KL, squared errors to 1e-3 relative.
 """
@@ -205,17 +209,31 @@ def test_calibrate_matches_oracle(gpu_lib, hkv, g, d, n):
     for h in range(hkv):
         assert _rel_max(got["c_q"][h], ref["c_q"][h]) <= 1e-5, h
         assert _rel_max(got["c_s"][h], ref["c_s"][h]) <= 1e-5, h
-        for key, cov in (("r_k", "c_q"), ("r_v", "c_s")):
+        for key, cov, tkey, x in (("r_k", "c_q", "tau_k", draws[h].k), ("r_v", "c_s", "tau_v", draws[h].v)):
             r = got[key][h].astype(np.float64)
             assert np.max(np.abs(r @ r.T - np.eye(d))) <= 2e-5, (key, h)
             dg = np.diag(r.T @ ref[cov][h] @ r)
             assert np.max(np.abs(dg - np.trace(ref[cov][h]) / d)) <= 1e-4 * np.trace(ref[cov][h]) / d, (key, h)
+            u = r @ cal.mix_matrix(d).T
+            u_ref = ref[key + "64"][h] @ cal.mix_matrix(d).T
             # the attention-importance direction: U's first column matches
-            u0 = (r @ cal.mix_matrix(d).T)[:, 0]
-            u0_ref = (ref[key + "64"][h] @ cal.mix_matrix(d).T)[:, 0]
-            assert float(u0 @ u0_ref) >= 1 - 1e-4, (key, h)
-        for key in ("tau_k", "tau_v"):
-            assert abs(float(got[key][h]) - float(ref[key][h])) <= 5e-4 * float(ref[key][h]), (key, h)
+            assert float(u[:, 0] @ u_ref[:, 0]) >= 1 - 1e-4, (key, h)
+            # column signs: the convention (largest-magnitude entry positive)
+            # decides a sign only where that entry stands out beyond the
+            # eigenvectors' fp32 accuracy; elsewhere either sign is a valid
+            # result, and through H P_br the sign moves tau
+            dots = np.sum(u * u_ref, axis=0)
+            mags = np.sort(np.abs(u_ref), axis=0)
+            flipped = np.nonzero(dots < 0)[0]
+            assert np.all(mags[-1, flipped] - mags[-2, flipped] < 1e-3), (key, h, flipped)
+            # tau is the quantile of |x R| for the R returned (a property of the
+            # result, checked in fp64 here)
+            want = np.float32(np.quantile(np.abs(x.astype(np.float64) @ r), 0.995))
+            assert abs(float(got[tkey][h]) - float(want)) <= 1e-5 * float(want), (tkey, h)
+            if flipped.size == 0:
+                assert abs(float(got[tkey][h]) - float(ref[tkey][h])) <= 5e-4 * float(ref[tkey][h]), (tkey, h)
+            else:
+                log(f"{key} head {h}: columns {flipped.tolist()} signed the other way (tie within fp32)")
     log(f"calibrate: tau_k {got['tau_k'][:4]} vs {ref['tau_k'][:4]}")
 
 
