@@ -20,6 +20,7 @@ Prints one JSON line.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -83,7 +84,7 @@ def parse():
 class Decoder:
     """Pre-marshalled oscar_decode_attention calls, one per pool copy."""
 
-    def __init__(self, oscar, pool, wl, q, lens, copies, r_k, out, ws, bf16_only=False):
+    def __init__(self, oscar, pool, wl, q, lens, copies, r_k, out, ws, bf16_only=False, groups=None):
         import torch
         lib = oscar.load()
         self.lib = lib
@@ -103,6 +104,14 @@ class Decoder:
                                   b16.data_ptr(), i2.data_ptr(), r_k.data_ptr(), None,
                                   out.data_ptr(), ws.data_ptr(), ws.numel()))
         self.fn = lib.oscar_bf16_decode_attention if bf16_only else lib.oscar_decode_attention
+        if groups:
+            # prefix groups: oscar_decode_attention_cascade (group array
+            # inserted before the workspace arguments)
+            arr, ng = oscar._groups(groups)
+            self._groups = arr
+            gp = ctypes.cast(arr, ctypes.c_void_p)
+            self.args = [a[:-2] + (gp, ng) + a[-2:] for a in self.args]
+            self.fn = lib.oscar_decode_attention_cascade
 
     def __call__(self, i):
         # launch on the current stream (the capture stream inside a graph capture)
@@ -284,6 +293,27 @@ def bench_decode_workload(oscar, name, steps, warmup, repeats, cold_bytes):
     else:
         step = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws)
     ms, ms_min = time_steps(step, steps, warmup, repeats, use_graph=True)
+    cascade = None
+    if wl.shared_prefix_seqs:
+        # the same step with the shared prefix pages attended once per group
+        # of sequences (oscar_decode_attention_cascade)
+        groups = [(0, wl.shared_prefix_seqs, max(0, wl.shared_prefix_tokens - wl.sink) // 16)]
+        cws_n = oscar.cascade_workspace_bytes(pool, wl.batch, max(wl.seq_lens), copies[0]["int2_pt"].shape[1], groups)
+        cws = torch.zeros(cws_n, dtype=torch.uint8, device="cuda")
+        out_c = torch.empty_like(q)
+        cstep = Decoder(oscar, pool, wl, q, lens, copies, r_k, out_c, cws, groups=groups)
+        ms_c, ms_c_min = time_steps(cstep, steps, warmup, repeats, use_graph=True)
+        step(0)
+        cstep(0)
+        torch.cuda.synchronize()
+        # the two paths agree to the decode tolerance (2e-3 of each head's norm)
+        dif = (out.float() - out_c.float()).abs().amax(dim=-1) / out.float().norm(dim=-1).clamp_min(1e-30)
+        cascade = {"groups": groups, "us_per_step": round(ms_c * 1e3, 3), "us_min": round(ms_c_min * 1e3, 3),
+                   "speedup_vs_plain": round(ms / ms_c, 3), "max_rel_diff_vs_plain": round(float(dif.max()), 6),
+                   "GBps_unique": round(uniq / (ms_c * 1e-3) / 1e9, 2),
+                   "pct_hbm_peak_unique": round(100 * uniq / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+        log(f"{name} cascade: {ms_c * 1e3:.2f} us/step ({ms / ms_c:.2f}x), max rel diff {float(dif.max()):.2e}")
+        del cstep, cws
     # append/demote (and the write it does) counted on top of the KV read
     # (per sequence and KV head: bf16 K, V written by the append and read by
     # the demotion, the INT2 token written)
@@ -305,6 +335,7 @@ def bench_decode_workload(oscar, name, steps, warmup, repeats, cold_bytes):
     if wl.shared_prefix_seqs:
         res["shared_prefix"] = f"{wl.shared_prefix_seqs} sequences share {wl.shared_prefix_tokens} tokens"
         res["logical_GBps"] = round(kv["total"] / (ms * 1e-3) / 1e9, 2)
+        res["cascade"] = cascade
     del step, copies
     torch.cuda.empty_cache()
     return res

@@ -174,6 +174,46 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
                                     const float* r_k, const float* r_v, void* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* Prefix-shared ("cascade") decode.  The pages keep the paged pool's prefix
+ * sharing intact (MarkTechPost article, "Visual Explainer / How-To", the
+ * inference step: the radix cache and prefix reuse work unchanged) and report
+ * the largest gains where long prefixes are shared (ModelScope/CSDN page,
+ * evaluation section, Figure 6).  Shared pages are stored once; this call
+ * also reads them once per group of sequences.  A prefix group names sequences
+ * first_seq .. first_seq + num_seqs - 1 whose INT2 page tables hold the same
+ * physical pages for logical history pages 0 .. shared_pages - 1, as far as
+ * each member's history reaches (the caller guarantees this; the pages are
+ * read through the table of the member with the longest history).
+ * Groups must be ordered by first_seq and disjoint; a group with
+ * shared_pages = 0 is ignored.  The shared pages are attended once for up to
+ * 16 / (Hq/Hkv) member sequences together (2 at GQA 8, 4 at GQA 4), in a
+ * launch of prefix workgroups that precedes the decode launch; each member's
+ * own history pages and its BF16 segments are attended by the decode launch,
+ * which merges the prefix partials in.  A member whose history is shorter
+ * than the shared range sees only its own tokens.  The result equals
+ * oscar_decode_attention's up to fp32 summation order.  At most 32 units
+ * (groups split into 16 / (Hq/Hkv) sequences) per call (else
+ * OSCAR_ERR_UNSUPPORTED).  groups: host array.  workspace:
+ * oscar_decode_cascade_workspace_bytes(...) bytes, 256-byte aligned, zeroed
+ * before first use (as for oscar_decode_attention). */
+typedef struct {
+  int32_t first_seq;
+  int32_t num_seqs;
+  int32_t shared_pages;
+} oscar_prefix_group;
+
+oscar_status oscar_decode_cascade_workspace_bytes(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
+                                                  int32_t int2_pt_stride, const oscar_prefix_group* groups,
+                                                  int32_t num_groups, size_t* bytes);
+oscar_status oscar_decode_attention_cascade(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
+                                            const void* q, const int32_t* seq_lens,
+                                            const int32_t* bf16_page_table, int32_t bf16_pt_stride,
+                                            int32_t bf16_num_pages, const int32_t* int2_page_table,
+                                            int32_t int2_pt_stride, int32_t int2_num_pages, const void* bf16_pool,
+                                            const void* int2_pool, const float* r_k, const float* r_v, void* out,
+                                            const oscar_prefix_group* groups, int32_t num_groups, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
 /* Log-sum-exp merge of partial attentions (ModelScope/CSDN page, design
  * section, online-softmax merge).  Row i (0 <= i < rows) merges partials
  * row_offsets[i] .. row_offsets[i+1]-1:

@@ -28,6 +28,7 @@ EXPORTED = (
     "oscar_calib_gram_workspace_bytes", "oscar_calib_gram", "oscar_calib_attention", "oscar_calib_rotation",
     "oscar_calib_clip_workspace_bytes", "oscar_calib_clip", "oscar_calib_workspace_bytes", "oscar_calibrate",
     "oscar_dequantize", "oscar_attention_error",
+    "oscar_decode_cascade_workspace_bytes", "oscar_decode_attention_cascade",
 )
 
 
@@ -43,6 +44,10 @@ class CConfig(ctypes.Structure):
         ("group_size", ctypes.c_int32), ("page_size", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
         ("recent_tokens", ctypes.c_int32), ("v_absorbed", ctypes.c_int32), ("sm_scale", ctypes.c_float),
     ]
+
+
+class CPrefixGroup(ctypes.Structure):
+    _fields_ = [("first_seq", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("shared_pages", ctypes.c_int32)]
 
 
 class CLayout(ctypes.Structure):
@@ -88,6 +93,8 @@ def load(path: str = LIB_PATH):
     lib.oscar_calibrate.argtypes = [I, I, I, I, F, P, P, P, L, L, ctypes.c_double, P, P, P, P, P, P, P, S, P]
     lib.oscar_dequantize.argtypes = [P, I, P, I, P, P, P, P, P, P]
     lib.oscar_attention_error.argtypes = [I, I, I, I, F, P, P, P, P, P, L, L, P, P]
+    lib.oscar_decode_cascade_workspace_bytes.argtypes = [P, I, I, I, P, I, ctypes.POINTER(S)]
+    lib.oscar_decode_attention_cascade.argtypes = [P, I, I, P, P, P, I, I, P, I, I, P, P, P, P, P, P, I, P, S, P]
     lib.oscar_status_string.argtypes = [ctypes.c_int]
     lib.oscar_status_string.restype = ctypes.c_char_p
     lib.oscar_last_error.argtypes = []
@@ -210,6 +217,45 @@ def oscar_decode_attention(pool: OscarPool, q, seq_lens, max_seq_len: int, bf16_
         _ptr(r_k, "r_k", torch.float32), _ptr(r_v, "r_v", torch.float32), _ptr(out, "out", torch.bfloat16),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)),
         "oscar_decode_attention")
+    return out
+
+
+def _groups(groups):
+    """[(first_seq, num_seqs, shared_pages), ...] -> (ctypes array or None, count)."""
+    groups = list(groups or [])
+    if not groups:
+        return None, 0
+    arr = (CPrefixGroup * len(groups))(*[CPrefixGroup(int(a), int(b), int(c)) for a, b, c in groups])
+    return arr, len(groups)
+
+
+def cascade_workspace_bytes(pool: OscarPool, batch: int, max_seq_len: int, int2_pt_stride: int, groups) -> int:
+    arr, ng = _groups(groups)
+    n = ctypes.c_size_t()
+    _check(load().oscar_decode_cascade_workspace_bytes(pool.handle, batch, max_seq_len, int2_pt_stride,
+                                                       ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
+                                                       ng, ctypes.byref(n)), "oscar_decode_cascade_workspace_bytes")
+    return n.value
+
+
+def oscar_decode_attention_cascade(pool: OscarPool, q, seq_lens, max_seq_len: int, bf16_page_table,
+                                   int2_page_table, bf16_pool, int2_pool, r_k, out, workspace, groups, r_v=None,
+                                   stream=None):
+    """Decode with prefix groups [(first_seq, num_seqs, shared_pages), ...]
+    whose INT2 page tables share their first shared_pages history pages."""
+    import torch
+    arr, ng = _groups(groups)
+    _check(load().oscar_decode_attention_cascade(
+        pool.handle, q.shape[0], int(max_seq_len), _ptr(q, "q", torch.bfloat16), _ptr(seq_lens, "seq_lens", torch.int32),
+        _ptr(bf16_page_table, "bf16_page_table", torch.int32), bf16_page_table.shape[1],
+        _pages(bf16_pool, pool.bf16_page_bytes),
+        _ptr(int2_page_table, "int2_page_table", torch.int32), int2_page_table.shape[1],
+        _pages(int2_pool, pool.int2_page_bytes),
+        _ptr(bf16_pool, "bf16_pool", torch.uint8), _ptr(int2_pool, "int2_pool", torch.uint8),
+        _ptr(r_k, "r_k", torch.float32), _ptr(r_v, "r_v", torch.float32), _ptr(out, "out", torch.bfloat16),
+        ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, ng,
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)),
+        "oscar_decode_attention_cascade")
     return out
 
 

@@ -188,6 +188,15 @@ struct Acc {
     for (int g = 0; g < NG; ++g) Z[g] *= f;
   }
   // lazy running max: raise m only when some logit exceeds it by kLazy
+  __device__ __forceinline__ void update_max(const float lg[4], const float lg2[4]) {
+    const float lmax = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
+                             fmaxf(fmaxf(lg2[0], lg2[1]), fmaxf(lg2[2], lg2[3])));
+    if (__any(lmax > m + kLazy)) {
+      const float mn = fmaxf(m, col_max(lmax));
+      scale(__builtin_amdgcn_exp2f(m - mn));
+      m = mn;
+    }
+  }
   __device__ __forceinline__ void update_max(const float lg[4]) {
     const float lmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
     if (__any(lmax > m + kLazy)) {
@@ -605,6 +614,16 @@ __global__ void __launch_bounds__(kThreads)
   // value arrives: for an INT2 chunk the page ids of its planned page range
   // (clamped to the page table) and R_K and q for the rotation prologue.
   const int L_in = seq_lens[b];
+  // prefix-shared unit of this sequence: its first S_u history pages and the
+  // unit's prefix partials come from the prefix launch
+  int S_u = 0, cch = 0;
+  if (!BF16_ONLY) {
+    for (int i = 0; i < p.n_casc; ++i)
+      if (b >= p.casc[i].first && b < p.casc[i].first + p.casc[i].count) {
+        S_u = p.casc[i].shared_pages;
+        cch = p.casc[i].chunks;
+      }
+  }
   constexpr int TPB = 64 / C::SLOTS;  // tiles whose page ids one VGPR holds
   constexpr int CG = D / 4, RS = kThreads / CG, RPS = D / RS;
   const int cg = tid % CG, rs = tid / CG;
@@ -616,8 +635,8 @@ __global__ void __launch_bounds__(kThreads)
   if (int2_planned) {
     // lane i*SLOTS + s: slot s of this wave's i-th tile, wave + i*kWaves
     const int i = lane / C::SLOTS, s = lane % C::SLOTS;
-    const int lp = c_int2 * p.pages_per_chunk + (wave + i * kWaves) * C::SLOTS + s;
-    const int pend = min((c_int2 + 1) * p.pages_per_chunk, p.int2_pt_stride);
+    const int lp = S_u + c_int2 * p.pages_per_chunk + (wave + i * kWaves) * C::SLOTS + s;
+    const int pend = min(S_u + (c_int2 + 1) * p.pages_per_chunk, p.int2_pt_stride);
     if (lp < pend) pid_raw = int2_pt_all[(size_t)b * p.int2_pt_stride + lp];
     // thread (rs, cg) owns rows [rs*RPS, rs*RPS + RPS) of R_K and output
     // channels 4cg .. 4cg+3 of q' = q R_K
@@ -661,7 +680,8 @@ __global__ void __launch_bounds__(kThreads)
     first = u * p.pages_per_chunk;
     end = (u == chunks - 1) ? npages : min(first + p.pages_per_chunk, npages);
   } else {
-    const int chunks = min((hist_pages + p.pages_per_chunk - 1) / p.pages_per_chunk, p.max_chunks);
+    const int own_pages = max(hist_pages - S_u, 0);
+    const int chunks = min((own_pages + p.pages_per_chunk - 1) / p.pages_per_chunk, p.max_chunks);
     total = p.n_bf16_units + chunks;
     if (u < p.n_bf16_units) {
       const int nlist = n_sp + n_rp;
@@ -671,7 +691,7 @@ __global__ void __launch_bounds__(kThreads)
       const int c = u - p.n_bf16_units;
       if (c >= chunks) return;
       int2_unit = true;
-      first = c * p.pages_per_chunk;
+      first = S_u + c * p.pages_per_chunk;
       end = (c == chunks - 1) ? hist_pages : min(first + p.pages_per_chunk, hist_pages);
     }
   }
@@ -886,7 +906,8 @@ __global__ void __launch_bounds__(kThreads)
 
   // ---- merge the waves' partials into this workgroup's partial
   const size_t head_base = (size_t)b * p.num_kv_heads + kvh;
-  const size_t pidx = (head_base * U + u) * GQA;
+  const int US = p.slots_per_head;
+  const size_t pidx = (head_base * US + u) * GQA;
   for (int idx = tid; idx < GQA * D; idx += kThreads) {
     const int h = idx / D, c = idx % D;
     float mx = -INFINITY;
@@ -929,7 +950,7 @@ __global__ void __launch_bounds__(kThreads)
   }
   __syncthreads();
   if (!sm.last) return;
-  const size_t p0 = head_base * U * GQA;
+  const size_t p0 = head_base * US * GQA;
   // Folds partials u0 .. u1-1 of head h, channel c into (M, S, A): the log2
   // max, the sum of weights and the weighted sum of normalized outputs, in
   // batches of 32 (one memory round trip per batch; indices past the range
@@ -973,7 +994,7 @@ __global__ void __launch_bounds__(kThreads)
     for (int idx = tid; idx < GQA * D; idx += kThreads) {
       const int h = idx / D, c = idx % D;
       float M, S, A;
-      fold(h, c, 0, total, M, S, A);
+      fold(h, c, 0, total + cch, M, S, A);
       outp[h * D + c] = (uint16_t)f32_to_bf16(S > 0.f ? A / S : 0.f);
     }
   } else {
@@ -990,7 +1011,7 @@ __global__ void __launch_bounds__(kThreads)
         const int h = idx / D, c = idx % D;
         float A2;
         fold(h, c, 0, p.n_bf16_units, M1[k], S1[k], A1[k]);
-        fold(h, c, p.n_bf16_units, total, M2[k], S2[k], A2);
+        fold(h, c, p.n_bf16_units, total + cch, M2[k], S2[k], A2);
         a2[h * D + c] = A2;
       }
     }
@@ -1023,6 +1044,404 @@ __global__ void __launch_bounds__(kThreads)
   }
   if (tid == 0)
     __hip_atomic_store(p.counters + head_base * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------ prefix (cascade) unit --
+// Workgroups of the prefix launch: one per (unit, KV head, chunk of the
+// shared pages).  The pages are attended once for all of the unit's queries:
+// the 16 score columns are (member sequence, query head) pairs and every
+// column sees every page, so a tile holds two consecutive pages (the k = 32
+// of one fp16 P.V MFMA) and each lane carries 4 tokens of both.  Compared
+// with one pass per sequence, the code unpacking, the score MFMAs and the
+// P.V operand construction of a page are shared by 16 / GQA sequences.
+template <int D, int NG>
+struct PTile {
+  static constexpr int KW = D / 64;
+  uint32_t kw[2][KW];
+  uint32_t vw[2][KW];
+  uint32_t sc[2][8 * NG];  // per page: this lane's quad, K (s,z) x 4 tokens x NG, then V
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int w = 0; w < KW; ++w) asm volatile("" : "+v"(kw[s][w]), "+v"(vw[s][w]));
+#pragma unroll
+      for (int w = 0; w < 8 * NG; ++w) asm volatile("" : "+v"(sc[s][w]));
+    }
+  }
+};
+
+template <int D, int NG>
+struct PSmem {
+  union {
+    float part[kWaves][16][D + 1];  // per-wave partials per column, [D] = lse (log2)
+    float qpart[kWaves][16][D];     // prologue: per-wave partial sums of q R_K
+  } u;
+  v4i bq[2][D / 64][64];            // int8 q' B operands (dense: every column)
+  float kap[16];
+  int sig[16 * NG];
+};
+
+// Loads the tile of logical pages lp0, lp0 + 1 (physical ids from lanes idx0,
+// idx0 + 1 of `pids`; idx0 < 0: no page).  Scale words of tokens at or past
+// `valid_len` (the longest member history) are zeroed.
+template <int D, int NG>
+__device__ __forceinline__ void pt_fetch(PTile<D, NG>& t, const uint8_t* __restrict__ hpool, size_t page_bytes,
+                                         int pids, int idx0, int lp0, int valid_len, int lane) {
+  constexpr int BLK2 = 8 * D + 128 * NG, REC = D / 8;
+  const int j = lane >> 4;
+  const int i0 = idx0 >= 0 ? idx0 : 0;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int v = __builtin_amdgcn_readlane(pids, i0 + s);
+    const int id = idx0 >= 0 ? v : -1;
+    // an absent page reads as zeros (num_records 0)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(hpool + (size_t)max(id, 0) * page_bytes), (short)0, id >= 0 ? BLK2 : 0, kBufferFlags);
+    if constexpr (D == 128) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * REC, 0, 0);
+      t.kw[s][0] = x[0];
+      t.kw[s][1] = x[1];
+      t.vw[s][0] = x[2];
+      t.vw[s][1] = x[3];
+    } else {
+      const auto y = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * REC, 0, 0);
+      t.kw[s][0] = y[0];
+      t.vw[s][0] = y[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NG; ++i) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, 8 * D + j * 32 * NG + 16 * i, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t.sc[s][4 * i + e] = x[e];
+    }
+    const int nv = min(max(valid_len - ((lp0 + s) * kPage + 4 * j), 0), 4);
+    if (nv < 4) {
+#pragma unroll
+      for (int w = 0; w < 8 * NG; ++w)
+        if ((w % (4 * NG)) / NG >= nv) t.sc[s][w] = 0u;
+    }
+  }
+}
+
+// Softmax of one prefix tile (both pages, every column): logits with tokens
+// past the column's member history masked, online max and sum, and the dense
+// fp16 P.V B operands.
+template <int D, int NG>
+__device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores<NG> (&S)[2], Acc<D, NG>& st,
+                                           float kappa, const float (&sig)[NG], int lp0, int hist_len, int lane,
+                                           v4i (&bw)[NG]) {
+  const int j = lane >> 4;
+  float lg[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float sint = (float)(S[s].a[g][i] * 256 + S[s].b[g][i]);
+        const uint32_t sz = t.sc[s][i * NG + g];
+        acc += bf16_lo(sz) * (sint - bf16_hi(sz) * sig[g]);
+      }
+      const bool ok = (lp0 + s) * kPage + 4 * j + i < hist_len;
+      lg[s][i] = fmaf(acc, kappa, ok ? 0.f : -INFINITY);
+    }
+  st.update_max(lg[0], lg[1]);
+  float pr[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[s][i] = __builtin_amdgcn_exp2f(lg[s][i] - st.m);
+  st.l += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    uint32_t u[2][2];
+    float zsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float w[4], zb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t sz = t.sc[s][4 * NG + i * NG + g];
+        w[i] = pr[s][i] * bf16_lo(sz);
+        zb[i] = bf16_hi(sz) + (i < 2 ? kBiasLo : kBiasHi);
+      }
+      const h2 w01 = __builtin_convertvector(f2{w[0], w[1]}, h2);
+      const h2 w23 = __builtin_convertvector(f2{w[2], w[3]}, h2);
+      zsum += ((float)w01[0] * zb[0] + (float)w01[1] * zb[1]) + ((float)w23[0] * zb[2] + (float)w23[1] * zb[3]);
+      u[s][0] = __builtin_bit_cast(uint32_t, w01);
+      u[s][1] = __builtin_bit_cast(uint32_t, w23);
+    }
+    st.Z[g] += zsum;
+    bw[g] = v4i{(int)u[0][0], (int)u[0][1], (int)u[1][0], (int)u[1][1]};
+  }
+}
+
+template <int D, int NG, int GQA>
+__global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p) {
+  constexpr int KW = D / 64, G = D / NG, BLK2 = 8 * D + 128 * NG;
+  constexpr int MEMBERS = 16 / GQA;  // member sequences per unit (columns = members x heads)
+  __shared__ PSmem<D, NG> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, j = lane >> 4;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  // which unit, KV head and chunk
+  int ui = 0;
+  for (int i = 1; i < p.n_casc; ++i)
+    if (lin >= p.casc[i].wg_start) ui = i;
+  const CascUnit cu = p.casc[ui];
+  const int rem = lin - cu.wg_start;
+  const int kvh = rem / cu.chunks, c = rem % cu.chunks;
+  const int hq = p.num_kv_heads * GQA;
+  const int mcol = n / GQA, hcol = n % GQA;  // this lane's column: member, head
+  const int US = p.slots_per_head;
+
+  // member histories (the same clamps as the decode launch)
+  int hist_len_m[MEMBERS], own_chunks_m[MEMBERS];
+  int valid_len = 0, src = cu.first;
+#pragma unroll
+  for (int m = 0; m < MEMBERS; ++m) {
+    hist_len_m[m] = 0;
+    own_chunks_m[m] = 0;
+    if (m < cu.count) {
+      int L = min(max(p.seq_lens[cu.first + m], 0), p.max_len);
+      L = min(L, kPage * p.bf16_pt_stride);
+      L = min(L, p.sink + p.recent + kPage * p.int2_pt_stride);
+      const int hl = max(p.sink, L - p.recent) - p.sink;
+      const int hp = (hl + kPage - 1) / kPage;
+      hist_len_m[m] = min(hl, kPage * cu.shared_pages);
+      own_chunks_m[m] = min((max(hp - cu.shared_pages, 0) + p.pages_per_chunk - 1) / p.pages_per_chunk, p.max_chunks);
+      if (hist_len_m[m] > valid_len) {
+        valid_len = hist_len_m[m];
+        src = cu.first + m;
+      }
+    }
+  }
+  int my_hist = 0;
+#pragma unroll
+  for (int m = 0; m < MEMBERS; ++m)
+    if (m == mcol) my_hist = hist_len_m[m];
+
+  // page ids of the chunk's pages, through the table of the member with the
+  // longest history (each member's table maps the shared pages its own
+  // history covers, and they are the same physical pages)
+  const int first = c * cu.pages_per_chunk;
+  const int end = min(first + cu.pages_per_chunk, cu.shared_pages);
+  const int ntiles = (end - first + 1) / 2;
+  constexpr int TPB = 32;  // tiles whose page ids one VGPR holds
+  const int nt_w = wave < ntiles ? min((ntiles - 1 - wave) / kWaves + 1, TPB) : 0;
+  int pids;
+  {
+    const int i = lane >> 1, s = lane & 1;
+    const int lp = first + (wave + i * kWaves) * 2 + s;
+    int id = -1;
+    if (i < nt_w && lp < end && lp * kPage < valid_len && lp < p.int2_pt_stride)
+      id = p.int2_pt[(size_t)src * p.int2_pt_stride + lp];
+    pids = (id >= 0 && id < p.int2_num_pages) ? id : -1;
+  }
+  const size_t page_bytes = (size_t)p.num_kv_heads * BLK2;
+  const uint8_t* __restrict__ hpool = p.int2_pool + (size_t)kvh * BLK2;
+
+  constexpr int R = kRing;
+  PTile<D, NG> ring[R];
+  auto fetch = [&](PTile<D, NG>& t, int i) {
+    pt_fetch<D, NG>(t, hpool, page_bytes, pids, i < nt_w ? 2 * i : -1, first + (wave + i * kWaves) * 2, valid_len,
+                    lane);
+  };
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r) fetch(ring[r], r);
+
+  // ---- prologue: q' = q R_K for the 16 columns, int8 split, B operands
+  constexpr int CG = D / 4, RS = kThreads / CG, RPS = D / RS;
+  const int cg = tid % CG, rs = tid / CG;
+  {
+    float4 rr[RPS];
+    const float* rbase = p.r_k + (size_t)kvh * D * D + (size_t)(rs * RPS) * D + 4 * cg;
+#pragma unroll
+    for (int r = 0; r < RPS; ++r) rr[r] = *(const float4*)(rbase + (size_t)r * D);
+#pragma unroll
+    for (int m = 0; m < MEMBERS; ++m) {
+      float qacc[GQA][4];
+#pragma unroll
+      for (int h = 0; h < GQA; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qacc[h][e] = 0.f;
+      if (m < cu.count) {
+        const uint16_t* qb = p.q + ((size_t)(cu.first + m) * hq + kvh * GQA) * D + rs * RPS;
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) {
+#pragma unroll
+          for (int i = 0; i < RPS; ++i) {
+            const float qv = bf16_to_f32(qb[h * D + i]);
+            qacc[h][0] = fmaf(qv, rr[i].x, qacc[h][0]);
+            qacc[h][1] = fmaf(qv, rr[i].y, qacc[h][1]);
+            qacc[h][2] = fmaf(qv, rr[i].z, qacc[h][2]);
+            qacc[h][3] = fmaf(qv, rr[i].w, qacc[h][3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GQA; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (CG == 16) qacc[h][e] = xor16_add(qacc[h][e]);
+          qacc[h][e] = xor32_add(qacc[h][e]);
+        }
+      if (lane < CG) {
+#pragma unroll
+        for (int h = 0; h < GQA; ++h)
+          *(float4*)&sm.u.qpart[wave][m * GQA + h][4 * cg] = float4{qacc[h][0], qacc[h][1], qacc[h][2], qacc[h][3]};
+      }
+    }
+  }
+  __syncthreads();
+  for (int col = wave; col < 16; col += kWaves) {
+    constexpr int CPL = D / 64;
+    float x[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += sm.u.qpart[w][col][CPL * lane + e];
+      x[e] = v;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = wave_max(amax);
+    const float sq = amax > 0.f ? amax / 127.f : 1.f;
+    const float inv_sq = 1.f / sq;
+    int sg = 0;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const int ch = CPL * lane + e;
+      const float y = x[e] * inv_sq;
+      const float a = fminf(fmaxf(rintf(y), -127.f), 127.f);
+      const float bt = fminf(fmaxf(rintf((y - a) * 256.f), -127.f), 127.f);
+      sg += 256 * (int)a + (int)bt;
+      const int w = ch / 64, jj = (ch % 64) / 16, mm = ch % 16;
+      const int byte = 4 * (mm % 4) + mm / 4;
+      const int l = 16 * jj + col;
+      ((int8_t*)&sm.bq[0][w][l])[byte] = (int8_t)a;
+      ((int8_t*)&sm.bq[1][w][l])[byte] = (int8_t)bt;
+    }
+    if constexpr (NG == 1) {
+      sg = wave_sum_i(sg);
+      if (lane == 0) sm.sig[col] = sg;
+    } else {
+      sg = half_sum_i(sg);
+      if ((lane & 31) == 0) sm.sig[col * NG + (lane >> 5)] = sg;
+    }
+    if (lane == 0) sm.kap[col] = p.sm_log2 * sq * (1.f / 256.f);
+  }
+  __syncthreads();
+  const float kappa = sm.kap[n];
+  float sig[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) sig[g] = (float)sm.sig[n * NG + g];
+  uint32_t exp_lo = kExpLo, exp_hi = kExpHi;
+  asm volatile("" : "+v"(exp_lo), "+v"(exp_hi));
+  v4i bqr[2][KW];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int w = 0; w < KW; ++w) bqr[t][w] = sm.bq[t][w][lane];
+  __syncthreads();  // the union's qpart is reused for the partials below
+
+  auto scores = [&](const PTile<D, NG>& t, I2Scores<NG> (&S)[2]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) S[s].a[g] = S[s].b[g] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < KW; ++w) {
+        const uint32_t x = t.kw[s][w];
+        const v4i a = {(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
+                       (int)((x >> 6) & 0x03030303u)};
+        const int g = (NG == 1) ? 0 : w;
+        S[s].a[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[0][w], S[s].a[g], 0, 0, 0);
+        S[s].b[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[1][w], S[s].b[g], 0, 0, 0);
+      }
+    }
+  };
+
+  Acc<D, NG> st;
+  st.init();
+  if (nt_w > 0) {
+    I2Scores<NG> S[2];
+    scores(ring[0], S);
+    int i = 0;
+    while (true) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (i >= nt_w) break;
+        fetch(ring[(r + R - 1) % R], i + R - 1);
+        v4i bw[NG];
+        pt_softmax<D, NG>(ring[r], S, st, kappa, sig, first + (wave + i * kWaves) * 2, my_hist, lane, bw);
+        scores(ring[(r + 1) % R], S);
+        pv_block_pair<D, NG, 0>(st, ring[r].vw[0][0], ring[r].vw[1][0], bw, exp_lo, exp_hi);
+        if constexpr (KW > 1) pv_block_pair<D, NG, 1>(st, ring[r].vw[0][1], ring[r].vw[1][1], bw, exp_lo, exp_hi);
+        ring[r].pin();
+        ring[(r + 1) % R].pin();
+        ++i;
+      }
+      if (i >= nt_w) break;
+    }
+  }
+  // ---- wave epilogue: one (o, lse) per column (no two columns share a head)
+  st.l = col_sum(st.l);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) st.Z[g] = col_sum(st.Z[g]);
+  {
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+#pragma unroll
+    for (int cbk = 0; cbk < D / 16; ++cbk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = (cbk * 16) / G;
+        sm.u.part[wave][n][cbk * 16 + 4 * j + i] = (st.o[cbk][i] - st.Z[g]) * inv;
+      }
+    if (j == 0) sm.u.part[wave][n][D] = st.l > 0.f ? st.m + __log2f(st.l) : -INFINITY;
+  }
+  __syncthreads();
+  // ---- merge the waves and store each column's partial in its member's
+  //      slot n_bf16_units + own chunks + c
+  for (int idx = tid; idx < 16 * D; idx += kThreads) {
+    const int col = idx / D, ch = idx % D;
+    const int m = col / GQA, h = col % GQA;
+    if (m >= cu.count) continue;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.u.part[w][col][D]);
+    float o = 0.f, lse = -INFINITY;
+    if (mx > -INFINITY) {
+      float sw = 0.f, so = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float e = __builtin_amdgcn_exp2f(sm.u.part[w][col][D] - mx);
+        sw += e;
+        so += e * sm.u.part[w][col][ch];
+      }
+      o = so / sw;
+      lse = mx + __log2f(sw);
+    }
+    int oc = 0;
+#pragma unroll
+    for (int mm = 0; mm < MEMBERS; ++mm)
+      if (mm == m) oc = own_chunks_m[mm];
+    const size_t head_base = (size_t)(cu.first + m) * p.num_kv_heads + kvh;
+    const size_t pidx = (head_base * US + p.n_bf16_units + oc + c) * GQA + h;
+    p.part_o[pidx * D + ch] = o;
+    if (ch == 0) p.part_lse[pidx] = lse;
+  }
+}
+
+template <int D, int NG, int GQA>
+bool launch_prefix_t(const DecodeParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA>), dim3(grid), dim3(kThreads), 0, stream, p);
+  return true;
 }
 
 // --------------------------------------------------------- oscar_merge --
@@ -1078,6 +1497,23 @@ bool launch_decode(const DecodeParams& p, int head_dim, int n_groups, int gqa, b
   OSCAR_DEC(64, 1, 4)
   OSCAR_DEC(64, 1, 8)
 #undef OSCAR_DEC
+  return false;
+}
+
+bool launch_decode_prefix(const DecodeParams& p, int head_dim, int n_groups, int gqa, int grid, hipStream_t stream) {
+  if (grid <= 0) return true;
+#define OSCAR_PRE(D, NG, G) \
+  if (head_dim == D && n_groups == NG && gqa == G) return launch_prefix_t<D, NG, G>(p, grid, stream);
+  OSCAR_PRE(128, 1, 2)
+  OSCAR_PRE(128, 1, 4)
+  OSCAR_PRE(128, 1, 8)
+  OSCAR_PRE(128, 2, 2)
+  OSCAR_PRE(128, 2, 4)
+  OSCAR_PRE(128, 2, 8)
+  OSCAR_PRE(64, 1, 2)
+  OSCAR_PRE(64, 1, 4)
+  OSCAR_PRE(64, 1, 8)
+#undef OSCAR_PRE
   return false;
 }
 

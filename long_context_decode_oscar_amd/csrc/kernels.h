@@ -9,6 +9,22 @@ namespace oscar {
 // decode ticket counters: one per (sequence, KV head), each on its own 128-byte line
 constexpr int kCounterStride = 32;
 
+// Prefix-shared ("cascade") decode: a unit is up to 16 / GQA consecutive
+// sequences whose INT2 page tables share their first `shared_pages` logical
+// history pages.  One launch of prefix workgroups attends those pages once
+// for all the unit's queries (chunk c of the unit's range writes partial slot
+// n_bf16_units + own chunks of the member + c of every member); the decode
+// launch that follows covers each sequence's own history from page
+// shared_pages on and merges the prefix partials in.
+constexpr int kMaxCascUnits = 32;
+struct CascUnit {
+  int32_t first, count;      // member sequences first .. first + count - 1
+  int32_t shared_pages;      // shared logical history pages [0, shared_pages)
+  int32_t chunks;            // prefix chunks of the unit (per KV head)
+  int32_t pages_per_chunk;   // even
+  int32_t wg_start;          // first prefix workgroup of the unit
+};
+
 struct DecodeParams {
   const uint16_t* q;         // [B][Hq][D] bf16
   const int32_t* seq_lens;   // [B]
@@ -30,13 +46,18 @@ struct DecodeParams {
   int32_t bf16_pages_per_unit;
   int32_t max_chunks;        // INT2 (or, BF16-only, BF16) chunks per (sequence, KV head)
   int32_t pages_per_chunk;
-  int32_t units_per_head;    // n_bf16_units + max_chunks
+  int32_t units_per_head;    // workgroups per (sequence, KV head): n_bf16_units + max_chunks
+  int32_t slots_per_head;    // partial slots per (sequence, KV head): units_per_head + max prefix chunks
   float sm_log2;             // softmax scale * log2(e)
+  int32_t n_casc;            // prefix-shared units (0: plain decode)
+  CascUnit casc[kMaxCascUnits];
 };
 
 // Returns false if the (head_dim, n_groups, gqa) combination has no kernel.
 bool launch_decode(const DecodeParams& p, int head_dim, int n_groups, int gqa, bool bf16_only, int grid,
                    hipStream_t stream);
+// The prefix workgroups of p.casc (grid = sum of Hkv * chunks over units).
+bool launch_decode_prefix(const DecodeParams& p, int head_dim, int n_groups, int gqa, int grid, hipStream_t stream);
 
 struct MergeParams {
   int32_t rows, head_dim;

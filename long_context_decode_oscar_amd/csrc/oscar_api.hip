@@ -70,7 +70,7 @@ constexpr int kDecodeWaves = 8;  // waves per decode workgroup (decode.hip)
 
 struct Plan {
   bool fits;  // false: the history needs more than kMaxChunks chunks
-  int n_bf16_units, bf16_pages_per_unit, max_chunks, pages_per_chunk, units, grid;
+  int n_bf16_units, bf16_pages_per_unit, max_chunks, pages_per_chunk, units, slots, grid;
   size_t off_counters, off_lse, off_o, bytes;
 };
 
@@ -127,6 +127,7 @@ Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
   pl.units = pl.n_bf16_units + pl.max_chunks;
   if (pl.units < 1) pl.units = 1;
   pl.grid = batch * hkv * pl.units;
+  pl.slots = pl.units;
   const size_t heads = (size_t)batch * hkv;
   const size_t parts = heads * pl.units * pool->gqa;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -134,6 +135,78 @@ Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
   pl.off_lse = up(heads * oscar::kCounterStride * sizeof(uint32_t));
   pl.off_o = pl.off_lse + up(parts * sizeof(float));
   pl.bytes = pl.off_o + up(parts * c.head_dim * sizeof(float));
+  return pl;
+}
+
+// ---- prefix-shared (cascade) planning ----
+struct CascPlan {
+  int n = 0;              // units
+  int max_chunks = 0;     // largest prefix chunk count of a unit
+  int grid = 0;           // prefix workgroups
+  oscar::CascUnit units[oscar::kMaxCascUnits];
+};
+
+// Splits each group into units of at most 16 / gqa sequences and the shared
+// pages of each unit into chunks, about one prefix workgroup per CU in all.
+oscar_status plan_cascade(const oscar_pool* pool, int batch, int int2_pt_stride, const oscar_prefix_group* groups,
+                          int num_groups, CascPlan* cp) {
+  const int hkv = pool->cfg.num_kv_heads, members = 16 / pool->gqa;
+  if (num_groups < 0) return fail(OSCAR_ERR_INVALID, "negative num_groups");
+  if (num_groups > 0 && !groups) return fail(OSCAR_ERR_INVALID, "groups must be non-null when num_groups > 0");
+  long long total_pages = 0;
+  int prev_end = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    const oscar_prefix_group& pg = groups[g];
+    if (pg.num_seqs < 1 || pg.first_seq < prev_end || (long long)pg.first_seq + pg.num_seqs > batch)
+      return fail(OSCAR_ERR_INVALID, "prefix group %d: groups must be ordered, disjoint and inside the batch", g);
+    if (pg.shared_pages < 0 || pg.shared_pages > int2_pt_stride)
+      return fail(OSCAR_ERR_INVALID, "prefix group %d: shared_pages must be in [0, int2_pt_stride]", g);
+    prev_end = pg.first_seq + pg.num_seqs;
+    if (pg.shared_pages == 0) continue;
+    for (int m = 0; m < pg.num_seqs; m += members) {
+      if (cp->n == oscar::kMaxCascUnits)
+        return fail(OSCAR_ERR_UNSUPPORTED, "more than %d prefix units of %d sequences", oscar::kMaxCascUnits, members);
+      oscar::CascUnit& u = cp->units[cp->n++];
+      u.first = pg.first_seq + m;
+      u.count = std::min(members, pg.num_seqs - m);
+      u.shared_pages = pg.shared_pages;
+      total_pages += pg.shared_pages;
+    }
+  }
+  const int target = env_int("OSCAR_TARGET_WGS", num_cus());
+  int wg = 0;
+  for (int i = 0; i < cp->n; ++i) {
+    oscar::CascUnit& u = cp->units[i];
+    // chunks of this unit in proportion to its pages, a tile being 2 pages
+    // and a chunk at most 32 tiles per wave
+    long long want = (long long)target * u.shared_pages / (hkv * std::max(1LL, total_pages));
+    want = std::max(1LL, want);
+    int ppc = (int)((u.shared_pages + want - 1) / want);
+    ppc = std::min(std::max(2, (ppc + 1) / 2 * 2), 2 * 32 * kDecodeWaves);
+    u.pages_per_chunk = ppc;
+    u.chunks = (u.shared_pages + ppc - 1) / ppc;
+    u.wg_start = wg;
+    wg += hkv * u.chunks;
+    cp->max_chunks = std::max(cp->max_chunks, u.chunks);
+  }
+  cp->grid = wg;
+  return OSCAR_OK;
+}
+
+// Workspace of a decode with prefix units: every (sequence, KV head) gets the
+// unit slots of the largest unit on top of the plain plan's.
+Plan cascade_plan(const oscar_pool* pool, int batch, int max_len, const CascPlan& cp) {
+  Plan pl = make_plan(pool, batch, max_len, false);
+  const int hkv = pool->cfg.num_kv_heads;
+  pl.slots = pl.units + cp.max_chunks;
+  const size_t heads = (size_t)batch * hkv;
+  const size_t parts = heads * pl.slots * pool->gqa;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  pl.off_lse = up(heads * oscar::kCounterStride * sizeof(uint32_t));
+  pl.off_o = pl.off_lse + up(parts * sizeof(float));
+  pl.bytes = pl.off_o + up(parts * pool->cfg.head_dim * sizeof(float));
+  // the decode launch keeps the plain plan's workgroups: the extra slots are
+  // filled by the prefix launch
   return pl;
 }
 
@@ -344,13 +417,16 @@ static oscar_status check_tables(const int32_t* bf16_pt, int32_t bf16_stride, in
   return ok();
 }
 
-oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
-                                    const int32_t* seq_lens, const int32_t* bf16_page_table,
-                                    int32_t bf16_pt_stride, int32_t bf16_num_pages,
-                                    const int32_t* int2_page_table, int32_t int2_pt_stride,
-                                    int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
-                                    const float* r_k, const float* r_v, void* out, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Decode with optional prefix groups (num_groups = 0: plain decode, one launch).
+oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
+                         const int32_t* seq_lens, const int32_t* bf16_page_table, int32_t bf16_pt_stride,
+                         int32_t bf16_num_pages, const int32_t* int2_page_table, int32_t int2_pt_stride,
+                         int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool, const float* r_k,
+                         const float* r_v, void* out, const oscar_prefix_group* groups, int32_t num_groups,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!pool) return fail(OSCAR_ERR_INVALID, "pool must be non-null");
   if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID, "negative batch or max_seq_len");
   if (batch == 0) return ok();
@@ -363,7 +439,9 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
   oscar_status st = check_tables(bf16_page_table, bf16_pt_stride, bf16_num_pages, int2_page_table, int2_pt_stride,
                                  int2_num_pages, true);
   if (st != OSCAR_OK) return st;
-  const Plan pl = make_plan(pool, batch, max_seq_len, false);
+  CascPlan cp;
+  if ((st = plan_cascade(pool, batch, int2_pt_stride, groups, num_groups, &cp)) != OSCAR_OK) return st;
+  const Plan pl = cascade_plan(pool, batch, max_seq_len, cp);
   if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes)
     return fail(OSCAR_ERR_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes", pl.bytes);
@@ -395,10 +473,65 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
   p.max_chunks = pl.max_chunks;
   p.pages_per_chunk = pl.pages_per_chunk;
   p.units_per_head = pl.units;
+  p.slots_per_head = pl.slots;
   p.sm_log2 = pool->sm_scale * 1.4426950408889634f;
+  p.n_casc = cp.n;
+  for (int i = 0; i < cp.n; ++i) p.casc[i] = cp.units[i];
+  // prefix partials first (same stream): the decode launch's merge reads them
+  if (cp.grid > 0) {
+    if (!oscar::launch_decode_prefix(p, c.head_dim, pool->n_groups, pool->gqa, cp.grid, (hipStream_t)stream))
+      return fail(OSCAR_ERR_UNSUPPORTED, "no prefix decode kernel for this shape");
+    if ((st = check_hip("prefix decode launch")) != OSCAR_OK) return st;
+  }
   if (!oscar::launch_decode(p, c.head_dim, pool->n_groups, pool->gqa, false, pl.grid, (hipStream_t)stream))
     return fail(OSCAR_ERR_UNSUPPORTED, "no decode kernel for this shape");
   return check_hip("decode launch");
+}
+}  // namespace
+
+extern "C" {
+
+oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
+                                    const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                    int32_t bf16_pt_stride, int32_t bf16_num_pages,
+                                    const int32_t* int2_page_table, int32_t int2_pt_stride,
+                                    int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
+                                    const float* r_k, const float* r_v, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return decode_impl(pool, batch, max_seq_len, q, seq_lens, bf16_page_table, bf16_pt_stride, bf16_num_pages,
+                     int2_page_table, int2_pt_stride, int2_num_pages, bf16_pool, int2_pool, r_k, r_v, out, nullptr, 0,
+                     workspace, workspace_bytes, stream);
+}
+
+oscar_status oscar_decode_cascade_workspace_bytes(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
+                                                  int32_t int2_pt_stride, const oscar_prefix_group* groups,
+                                                  int32_t num_groups, size_t* bytes) {
+  if (!pool || !bytes) return fail(OSCAR_ERR_INVALID, "pool and bytes must be non-null");
+  if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID, "negative batch or max_seq_len");
+  if (batch == 0) {
+    *bytes = 0;
+    return ok();
+  }
+  CascPlan cp;
+  oscar_status st = plan_cascade(pool, batch, int2_pt_stride, groups, num_groups, &cp);
+  if (st != OSCAR_OK) return st;
+  const Plan pl = cascade_plan(pool, batch, max_seq_len, cp);
+  if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
+  *bytes = pl.bytes;
+  return ok();
+}
+
+oscar_status oscar_decode_attention_cascade(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
+                                            const void* q, const int32_t* seq_lens,
+                                            const int32_t* bf16_page_table, int32_t bf16_pt_stride,
+                                            int32_t bf16_num_pages, const int32_t* int2_page_table,
+                                            int32_t int2_pt_stride, int32_t int2_num_pages, const void* bf16_pool,
+                                            const void* int2_pool, const float* r_k, const float* r_v, void* out,
+                                            const oscar_prefix_group* groups, int32_t num_groups, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  return decode_impl(pool, batch, max_seq_len, q, seq_lens, bf16_page_table, bf16_pt_stride, bf16_num_pages,
+                     int2_page_table, int2_pt_stride, int2_num_pages, bf16_pool, int2_pool, r_k, r_v, out, groups,
+                     num_groups, workspace, workspace_bytes, stream);
 }
 
 oscar_status oscar_bf16_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
@@ -440,6 +573,7 @@ oscar_status oscar_bf16_decode_attention(const oscar_pool* pool, int32_t batch, 
   p.max_chunks = pl.max_chunks;
   p.pages_per_chunk = pl.pages_per_chunk;
   p.units_per_head = pl.units;
+  p.slots_per_head = pl.slots;
   p.sm_log2 = pool->sm_scale * 1.4426950408889634f;
   if (!oscar::launch_decode(p, c.head_dim, pool->n_groups, pool->gqa, true, pl.grid, (hipStream_t)stream))
     return fail(OSCAR_ERR_UNSUPPORTED, "no decode kernel for this shape");

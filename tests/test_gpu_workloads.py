@@ -146,7 +146,19 @@ def test_mixed_prefix_gqa8_full_size_sampled(gpu_lib):
     gpu_lib.oscar_decode_attention(pool, inp.q.contiguous(), lens, max(wl.seq_lens), dev["bf16_pt"], dev["int2_pt"],
                                    dev["bf16_pool"], dev["int2_pool"], r_k, out, ws)
     torch.cuda.synchronize()
+    # the same step through the prefix-shared decode: the 4,092 shared pages
+    # attended once per pair of sequences
+    groups = [(0, wl.shared_prefix_seqs, (wl.shared_prefix_tokens - wl.sink) // 16)]
+    nbytes = gpu_lib.cascade_workspace_bytes(pool, wl.batch, max(wl.seq_lens), dev["int2_pt"].shape[1], groups)
+    cws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out_c = torch.full(inp.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    log(f"cascade decode with groups {groups}")
+    gpu_lib.oscar_decode_attention_cascade(pool, inp.q.contiguous(), lens, max(wl.seq_lens), dev["bf16_pt"],
+                                           dev["int2_pt"], dev["bf16_pool"], dev["int2_pool"], r_k, out_c, cws,
+                                           groups)
+    torch.cuda.synchronize()
     seqs_idx, kv_heads = list(range(8)), [5]
     log(f"oracle write + decode of all 8 sequences, KV head {kv_heads}")
     ref, qh = _oracle(wl, inp, seqs_idx, kv_heads, dev)
     check_decode(out[seqs_idx][:, qh], ref, what="mixed prefix GQA8 (sampled)")
+    check_decode(out_c[seqs_idx][:, qh], ref, what="mixed prefix GQA8, cascade (sampled)")

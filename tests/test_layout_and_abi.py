@@ -217,3 +217,31 @@ def test_calibration_validation_fails_before_launch():
     assert lib.oscar_dequantize(p.handle, 0, None, 0, None, None, None, None, None, None) == oscar.OSCAR_OK
     assert lib.oscar_attention_error(8, 4, 64, 128, 0.0, F, F, F, None, F, 64 * 128, 128, F, None) == \
         oscar.OSCAR_ERR_INVALID
+
+
+def test_cascade_validation_fails_before_launch():
+    import long_context_decode_oscar_amd as oscar
+    lib = oscar.load()
+    p = oscar.OscarPool(_cfg(num_q_heads=64))  # GQA 8: two sequences per prefix unit
+    F = 1 << 20
+    n = ctypes.c_size_t()
+
+    def ws_bytes(groups, batch=8, stride=8192):
+        arr, ng = oscar._groups(groups)
+        ptr = ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None
+        return lib.oscar_decode_cascade_workspace_bytes(p.handle, batch, 131072, stride, ptr, ng, ctypes.byref(n))
+    assert ws_bytes([]) == oscar.OSCAR_OK
+    plain = n.value
+    assert ws_bytes([(0, 4, 4092)]) == oscar.OSCAR_OK and n.value > plain  # prefix partial slots
+    assert ws_bytes([(0, 4, 0)]) == oscar.OSCAR_OK and n.value == plain    # nothing shared
+    assert ws_bytes([(2, 2, 10), (0, 2, 10)]) == oscar.OSCAR_ERR_INVALID   # not ordered
+    assert ws_bytes([(0, 3, 10), (2, 2, 10)]) == oscar.OSCAR_ERR_INVALID   # overlapping
+    assert ws_bytes([(6, 3, 10)]) == oscar.OSCAR_ERR_INVALID               # past the batch
+    assert ws_bytes([(0, 2, 9000)]) == oscar.OSCAR_ERR_INVALID             # beyond the table
+    assert ws_bytes([(0, 66, 10)], batch=66) == oscar.OSCAR_ERR_UNSUPPORTED  # 33 units of 2
+    arr, ng = oscar._groups([(0, 4, 100)])
+    assert lib.oscar_decode_attention_cascade(p.handle, 8, 131072, F, F, F, 8, 4, F, 8192, 4, F, F, F, None, F,
+                                              ctypes.cast(arr, ctypes.c_void_p), ng, F, 16, None) == \
+        oscar.OSCAR_ERR_WORKSPACE
+    assert lib.oscar_decode_attention_cascade(p.handle, 8, 131072, F, F, F, 8, 4, F, 8192, 4, F, F, F, None, F,
+                                              None, 2, F, 1 << 30, None) == oscar.OSCAR_ERR_INVALID
