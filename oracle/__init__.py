@@ -21,7 +21,9 @@ What it computes, and where the pages say so:
     eigenbases, R = U H P_br, clip thresholds) and the synthetic error chain
     that compares rotations by logit error, score KL and output MSE
     (``calibration``; MarkTechPost article, "What OSCAR Does Differently";
-    ModelScope/CSDN page, motivation section, Figure 1).
+    ModelScope/CSDN page, motivation section, Figure 1);
+  * the four-level Lloyd-Max codebook variant of the history quantizer
+    (``codebook``; ModelScope/CSDN page, closing section).
 
 Floating point: fp64 except where the method's encoding fixes an fp32 or bf16
 rounding (the quantizer's scale, zero and code decisions), which are done in
@@ -39,4 +41,5 @@ from .pool import LogicalPool, SeqPool  # noqa: F401
 from .attention import decode_attention, bf16_decode_attention, attention_one_head  # noqa: F401
 from .merge import merge_partials  # noqa: F401
 from . import calibration  # noqa: F401
+from . import codebook  # noqa: F401
 from .calibration import calibrate  # noqa: F401

@@ -7,7 +7,8 @@ by online softmax).  The oracle does not split anything: it builds the full
 key and value sequence and takes one softmax over it.
 
   R1  history: k^ = [s_K (q_K - z_K)] R_K^T and v^ = s_V (q_V - z_V)
-      (absorbed V; otherwise times R_V^T), all fp64.
+      (absorbed V; otherwise times R_V^T), all fp64; with a four-level
+      codebook L the code value q is replaced by L[q].
   R2  logits l_t = sm * (q . k_t) with sm = 1/sqrt(D) unless given; sink and
       recent keys are the stored bf16 values, unrotated.
   R3  p = softmax(l) over the concatenation sink | history | recent, with max
@@ -20,6 +21,7 @@ import math
 
 import numpy as np
 
+from . import codebook
 from .quant import dequantize
 
 
@@ -37,10 +39,17 @@ def attention_one_head(keys, values, q, sm):
     return (e @ values) / tot, m + math.log(tot)
 
 
+def _dequant(codes, s, z, g, levels):
+    if levels is None:
+        return dequantize(codes, s, z, g)
+    return codebook.dequantize(codes, s, z, g, levels)
+
+
 def _history_kv(seq, kv, r_k, r_v):
-    k_hat = dequantize(seq.kc[:, kv], seq.ks[:, kv], seq.kz[:, kv], seq.g)
+    lk, lv = getattr(seq, "levels_k", None), getattr(seq, "levels_v", None)
+    k_hat = _dequant(seq.kc[:, kv], seq.ks[:, kv], seq.kz[:, kv], seq.g, lk)
     k_hat = k_hat @ np.asarray(r_k[kv], np.float32).astype(np.float64).T
-    v_hat = dequantize(seq.vc[:, kv], seq.vs[:, kv], seq.vz[:, kv], seq.g)
+    v_hat = _dequant(seq.vc[:, kv], seq.vs[:, kv], seq.vz[:, kv], seq.g, lv)
     if not seq.v_absorbed:
         v_hat = v_hat @ np.asarray(r_v[kv], np.float32).astype(np.float64).T
     return k_hat, v_hat

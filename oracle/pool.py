@@ -19,20 +19,24 @@ Readings where the pages are silent:
     rotation, otherwise it is rotated by R_V at demotion.
 
 The oracle holds logical arrays, not pages: dense bf16 K/V per position and
-per-token history codes, scales and zeros.
+per-token history codes, scales and zeros.  With ``levels_k`` / ``levels_v``
+(four-level codebooks, ``codebook``) the history is quantized with the
+codebook quantizer instead of the uniform one.
 """
 
 import numpy as np
 
+from . import codebook
 from .quant import quantize_tokens
 
 
 class SeqPool:
     def __init__(self, num_kv_heads, head_dim, group_size, sink=64, recent=256,
-                 v_absorbed=True):
+                 v_absorbed=True, levels_k=None, levels_v=None):
         self.hkv, self.d, self.g = num_kv_heads, head_dim, group_size
         self.ng = head_dim // group_size
         self.sink, self.recent, self.v_absorbed = sink, recent, v_absorbed
+        self.levels_k, self.levels_v = levels_k, levels_v
         self.L = 0
         self.k = np.zeros((0, self.hkv, self.d), np.float32)
         self.v = np.zeros((0, self.hkv, self.d), np.float32)
@@ -60,10 +64,14 @@ class SeqPool:
     def _quantize(self, pos, r_k, tau_k, r_v, tau_v):
         """Quantize tokens at positions ``pos`` (all KV heads)."""
         outs = {n: [] for n in ("kc", "ks", "kz", "vc", "vs", "vz")}
+        def quant(x, r, tau, levels):
+            if levels is None:
+                return quantize_tokens(x, r, tau, self.g)
+            return codebook.quantize_tokens(x, r, tau, self.g, levels)
         for h in range(self.hkv):
-            kc, ks, kz = quantize_tokens(self.k[pos, h], r_k[h], tau_k[h], self.g)
+            kc, ks, kz = quant(self.k[pos, h], r_k[h], tau_k[h], self.levels_k)
             rv = None if self.v_absorbed else r_v[h]
-            vc, vs, vz = quantize_tokens(self.v[pos, h], rv, tau_v[h], self.g)
+            vc, vs, vz = quant(self.v[pos, h], rv, tau_v[h], self.levels_v)
             for n, a in zip(outs, (kc, ks, kz, vc, vs, vz)):
                 outs[n].append(a)
         return {n: np.stack(a, axis=1) for n, a in outs.items()}

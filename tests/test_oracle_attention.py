@@ -106,6 +106,34 @@ def test_on_grid_history_is_lossless():
     assert np.allclose(lse, ref_lse, rtol=1e-13)
 
 
+def test_on_codebook_history_is_lossless():
+    """The same with a four-level codebook: values s (L[q] - z) quantize
+    exactly with the codebook quantizer, so the decode equals all-BF16 decode
+    on them."""
+    rng = np.random.default_rng(14)
+    d, hkv, L = 64, 2, 640
+    lk = np.array([0.0, 1.125, 1.875, 3.0])
+    lv = np.array([0.0, 0.90625, 2.03125, 3.0])
+    s = np.float32(0.5)
+    z = rng.choice(np.array([-1.5, 0.0, 1.5, 2.0], np.float32), size=(L, hkv))
+    codes = rng.integers(0, 4, size=(L, hkv, d))
+    codes[:, :, 0], codes[:, :, 1] = 0, 3
+    k = (s * (lk[codes] - z[:, :, None])).astype(np.float32)
+    codes_v = rng.integers(0, 4, size=(L, hkv, d))
+    codes_v[:, :, 5], codes_v[:, :, 9] = 0, 3
+    v = (s * (lv[codes_v] - z[:, :, None])).astype(np.float32)
+    assert np.array_equal(round_bf16(k), k) and np.array_equal(round_bf16(v), v)
+    eye = np.stack([np.eye(d, dtype=np.float32)] * hkv)
+    inf = np.full(hkv, np.inf, np.float32)
+    seq = SeqPool(hkv, d, 64, levels_k=lk, levels_v=lv).prefill(k, v, eye, inf, inf)
+    assert np.array_equal(seq.kc, codes[64:L - 256]) and np.array_equal(seq.vc, codes_v[64:L - 256])
+    q = _bf16(rng, 1, 4, d)
+    out, lse = decode_attention([seq], q, eye)
+    ref, ref_lse = bf16_decode_attention([k], [v], q, [L])
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-14)
+    assert np.allclose(lse, ref_lse, rtol=1e-13)
+
+
 def test_logit_error_identity_weights_by_query_covariance():
     """||Q K^T - Q K^^T||_F^2 = tr((K - K^) Q^T Q (K - K^)^T) (MarkTechPost
     article, "What OSCAR Does Differently"), with K^ the oracle's dequantized,
