@@ -87,7 +87,19 @@ typedef enum {
  * num_q_heads / num_kv_heads in {2, 4, 8}; page_size 16; sink_tokens a
  * multiple of 16 (64 by default, MarkTechPost article, "The Serving System");
  * recent_tokens >= 1 (256 by default, same section); v_absorbed 1 or 0
- * (see the value basis above). */
+ * (see the value basis above).
+ *
+ * Codebook (ModelScope/CSDN page, closing section: the rotation combined with
+ * a Lloyd-Max codebook).  codebook = 0: the history levels are 0, 1, 2, 3 in
+ * code units (dequantized value scale * (code - zero)), codes by
+ * round-to-nearest-even and clamp.  codebook = 1: the levels are
+ * levels_k[code] (keys) and levels_v[code] (values), each with
+ * 0 = L[0] < L[1] < L[2] < L[3] = 3 and L[1], L[2] multiples of 1/32 (else
+ * OSCAR_ERR_INVALID); the dequantized value is scale * (L[code] - zero), and
+ * the code of t = c/scale + zero is the number of midpoints
+ * (L[k] + L[k+1]) / 2 strictly below t.  Scale and zero are the same as with
+ * codebook = 0, so the pool layout is unchanged.  oscar_calib_codebook fits
+ * the levels. */
 typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -98,6 +110,9 @@ typedef struct {
   int32_t recent_tokens;
   int32_t v_absorbed;
   float sm_scale; /* softmax scale; 0 selects 1/sqrt(head_dim) */
+  int32_t codebook;
+  float levels_k[4];
+  float levels_v[4];
 } oscar_config;
 
 /* Byte sizes of the pool layout described above, filled by oscar_pool_create. */
@@ -312,6 +327,21 @@ oscar_status oscar_calib_clip_workspace_bytes(int32_t heads, int32_t rows, int32
 oscar_status oscar_calib_clip(int32_t heads, int32_t rows, int32_t head_dim, const float* x, int64_t head_stride,
                               int64_t row_stride, const float* r, double quantile, float* tau, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* Codebook fit (the levels of oscar_config.codebook = 1; ModelScope/CSDN
+ * page, closing section): for x laid out as for oscar_calib_gram, rotated by
+ * r (NULL: none) and clipped to +-tau[h] (device fp32 [heads]), every value's
+ * normalized position t = c/scale + zero (scale and zero per group of
+ * group_size channels of a row, exactly as the write path forms them); then
+ * Lloyd-Max with the end levels fixed at 0 and 3: 100 steps from the uniform
+ * levels, each moving L[1], L[2] to the mean of the values in their cells
+ * [midpoint below, midpoint above), sums in fp64; finally L[1], L[2] rounded
+ * to the nearest multiple of 1/32 (half to even).  levels: device fp32 [4].
+ * One codebook for all heads (a layer's keys, or its values). */
+oscar_status oscar_calib_codebook_workspace_bytes(int32_t heads, int32_t rows, int32_t head_dim, size_t* bytes);
+oscar_status oscar_calib_codebook(int32_t heads, int32_t rows, int32_t head_dim, int32_t group_size, const float* x,
+                                  int64_t head_stride, int64_t row_stride, const float* r, const float* tau,
+                                  float* levels, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The whole calibration of one layer: C_Q = gram(q)/(g N), R_K = U_Q H P_br,
  * C_S from the causal attention outputs, R_V = U_S H P_br, tau_K and tau_V

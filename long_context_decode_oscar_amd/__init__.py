@@ -29,6 +29,7 @@ EXPORTED = (
     "oscar_calib_clip_workspace_bytes", "oscar_calib_clip", "oscar_calib_workspace_bytes", "oscar_calibrate",
     "oscar_dequantize", "oscar_attention_error",
     "oscar_decode_cascade_workspace_bytes", "oscar_decode_attention_cascade",
+    "oscar_calib_codebook_workspace_bytes", "oscar_calib_codebook",
 )
 
 
@@ -43,6 +44,7 @@ class CConfig(ctypes.Structure):
         ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("group_size", ctypes.c_int32), ("page_size", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
         ("recent_tokens", ctypes.c_int32), ("v_absorbed", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+        ("codebook", ctypes.c_int32), ("levels_k", ctypes.c_float * 4), ("levels_v", ctypes.c_float * 4),
     ]
 
 
@@ -95,6 +97,8 @@ def load(path: str = LIB_PATH):
     lib.oscar_attention_error.argtypes = [I, I, I, I, F, P, P, P, P, P, L, L, P, P]
     lib.oscar_decode_cascade_workspace_bytes.argtypes = [P, I, I, I, P, I, ctypes.POINTER(S)]
     lib.oscar_decode_attention_cascade.argtypes = [P, I, I, P, P, P, I, I, P, I, I, P, P, P, P, P, P, I, P, S, P]
+    lib.oscar_calib_codebook_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(S)]
+    lib.oscar_calib_codebook.argtypes = [I, I, I, I, P, L, L, P, P, P, P, S, P]
     lib.oscar_status_string.argtypes = [ctypes.c_int]
     lib.oscar_status_string.restype = ctypes.c_char_p
     lib.oscar_last_error.argtypes = []
@@ -143,6 +147,9 @@ class PoolConfig:
     recent_tokens: int = 256
     v_absorbed: int = 1
     sm_scale: float = 0.0
+    codebook: int = 0
+    levels_k: tuple = (0.0, 1.0, 2.0, 3.0)
+    levels_v: tuple = (0.0, 1.0, 2.0, 3.0)
 
 
 class OscarPool:
@@ -152,7 +159,9 @@ class OscarPool:
         lib = load()
         self.cfg = cfg
         self._c = CConfig(cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.group_size, cfg.page_size,
-                          cfg.sink_tokens, cfg.recent_tokens, cfg.v_absorbed, cfg.sm_scale)
+                          cfg.sink_tokens, cfg.recent_tokens, cfg.v_absorbed, cfg.sm_scale, cfg.codebook,
+                          (ctypes.c_float * 4)(*[float(x) for x in cfg.levels_k]),
+                          (ctypes.c_float * 4)(*[float(x) for x in cfg.levels_v]))
         h = ctypes.c_void_p()
         lay = CLayout()
         _check(lib.oscar_pool_create(ctypes.byref(self._c), ctypes.byref(h), ctypes.byref(lay)), "oscar_pool_create")
@@ -380,6 +389,23 @@ def oscar_calib_clip(x, r, quantile: float, tau, workspace=None, stream=None):
                                    workspace.numel(), _stream(stream)),
            "oscar_calib_clip")
     return tau
+
+
+def oscar_calib_codebook(x, r, tau, group_size: int, levels=None, workspace=None, stream=None):
+    """Fixed-end Lloyd-Max codebook of x [heads, rows, D] rotated by r (or
+    None) and clipped to tau [heads]; returns levels, a device fp32 [4]."""
+    import torch
+    heads, rows, d = x.shape
+    px, hs, rs = _rows_view(x, "x")
+    if levels is None:
+        levels = torch.empty(4, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = _ws(_size_out("oscar_calib_codebook_workspace_bytes", heads, rows, d), x.device)
+    _check(load().oscar_calib_codebook(heads, rows, d, int(group_size), px, hs, rs, _ptr(r, "r", torch.float32),
+                                       _ptr(tau, "tau", torch.float32), _ptr(levels, "levels", torch.float32),
+                                       _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)),
+           "oscar_calib_codebook")
+    return levels
 
 
 def oscar_calibrate(q, k, v, clip_quantile: float = 0.995, sm_scale: float = 0.0, workspace=None, stream=None):

@@ -15,7 +15,10 @@
 //   clip        tau = a quantile of |x R| (linear interpolation between order
 //               statistics), the order statistics found by radix selection
 //               over the fp32 bit patterns of |x R|;
-//   dequantize  INT2 pool pages back to dense vectors, s (code - z) R^T;
+//   codebook    the normalized values t = c/s + z of the calibration set (the
+//               write path's arithmetic) and fixed-end Lloyd-Max on them;
+//   dequantize  INT2 pool pages back to dense vectors, s (L[code] - z) R^T
+//               (L the pool's levels, 0..3 unless it uses a codebook);
 //   error       the causal attention of the reference and of the quantized
 //               keys/values side by side: per query row the score KL, the
 //               summed squared logit error and the output error.
@@ -679,6 +682,159 @@ __global__ void __launch_bounds__(256) k_select_scan(const ClipParams p, int pas
 }
 
 // ---------------------------------------------------------------------------
+// codebook calibration: normalized values, then fixed-end Lloyd-Max
+// ---------------------------------------------------------------------------
+// k_normalize: grid (row blocks, heads), 4 waves, R in LDS.  Each wave forms
+// 16 rows of y = x R (as k_rotate_abs), clips them to +-tau, and per group of
+// G channels of a row computes the write path's bf16 scale and zero and
+// t = fl32(fl32(c / s) + z) for every value (IEEE divisions, as the write
+// path's reference arithmetic).
+__device__ __forceinline__ float row16_min(float x) {
+  x = fminf(x, dpp_row_ror<8>(x));
+  x = fminf(x, dpp_row_ror<4>(x));
+  x = fminf(x, dpp_row_ror<2>(x));
+  return fminf(x, dpp_row_ror<1>(x));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_row_ror<8>(x));
+  x = fmaxf(x, dpp_row_ror<4>(x));
+  x = fmaxf(x, dpp_row_ror<2>(x));
+  return fmaxf(x, dpp_row_ror<1>(x));
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) k_normalize(const CodebookParams p) {
+  constexpr int NT = D / 16;
+  __shared__ float rs[D * D];
+  const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, sub = lane >> 4;
+  const bool rot = p.r != nullptr;
+  if (rot) {
+    const float* r = p.r + (size_t)h * D * D;
+    for (int e = tid; e < D * D; e += 256) rs[e] = r[e];
+  }
+  __syncthreads();
+  const auto x = rsrc(p.x + (size_t)h * p.head_stride, (uint32_t)((size_t)p.rows * p.row_stride * 4));
+  const float tau = p.tau[h];
+  const int tiles_per_group = p.group_size / 16;
+  float* tout = p.t + (size_t)h * p.rows * D;
+  const int nblk = (p.rows + 15) / 16;
+  for (int blk = blockIdx.x * 4 + wave; blk < nblk; blk += gridDim.x * 4) {
+    const int row0 = blk * 16;
+    v4f acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (rot) {
+      for (int s = 0; s < D / 4; ++s) {
+        const float a = ld1(x, ((uint32_t)(row0 + col) * (uint32_t)p.row_stride + 4 * s + sub) * 4u);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma4(a, rs[(4 * s + sub) * D + 16 * t + col], acc[t]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[t][r] = ld1(x, ((uint32_t)(row0 + 4 * sub + r) * (uint32_t)p.row_stride + 16 * t + col) * 4u);
+    }
+    // lane holds y[row0 + 4 sub + r][16 t + col]
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][r] = fminf(fmaxf(acc[t][r], -tau), tau);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 4 * sub + r;
+      for (int g = 0; g < D / p.group_size; ++g) {
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (t / tiles_per_group == g) {
+            mn = fminf(mn, acc[t][r]);
+            mx = fmaxf(mx, acc[t][r]);
+          }
+        mn = row16_min(mn);
+        mx = row16_max(mx);
+        const float dl = mx - mn;
+        float s = bf16_to_f32(f32_to_bf16(dl / 3.0f));
+        if (dl == 0.f || s == 0.f) s = 1.f;
+        const float z = bf16_to_f32(f32_to_bf16(-mn / s));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (t / tiles_per_group == g && row < p.rows)
+            tout[(size_t)row * D + 16 * t + col] = __fadd_rn(acc[t][r] / s, z);
+      }
+    }
+  }
+}
+
+// One Lloyd step, part 1: workgroup w sums (in fp64) the values of its
+// chunk that fall in the cells [b0, b1) and [b1, b2) of the current levels.
+__global__ void __launch_bounds__(256) k_lloyd_partial(const CodebookParams p) {
+  __shared__ double red[4][256];
+  const int tid = threadIdx.x;
+  const double l1 = p.state[1], l2 = p.state[2];
+  const double b0 = 0.5 * l1, b1 = 0.5 * (l1 + l2), b2 = 0.5 * (l2 + 3.0);
+  const size_t n = (size_t)p.heads * p.rows * p.dim;
+  const size_t chunk = (n + gridDim.x - 1) / gridDim.x;
+  const size_t beg = chunk * blockIdx.x, end = min(n, beg + chunk);
+  double s1 = 0.0, c1 = 0.0, s2 = 0.0, c2 = 0.0;
+  for (size_t i = beg + tid; i < end; i += 256) {
+    const double t = (double)p.t[i];
+    if (t >= b0 && t < b1) {
+      s1 += t;
+      c1 += 1.0;
+    } else if (t >= b1 && t < b2) {
+      s2 += t;
+      c2 += 1.0;
+    }
+  }
+  red[0][tid] = s1;
+  red[1][tid] = c1;
+  red[2][tid] = s2;
+  red[3][tid] = c2;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) red[k][tid] += red[k][tid + off];
+    __syncthreads();
+  }
+  if (tid < 4) p.partial[(size_t)blockIdx.x * 4 + tid] = red[tid][0];
+}
+
+// part 2: sum the chunks in order and move each interior level to its cell's
+// mean (an empty cell keeps its level); after the last step round the
+// interior levels to the 1/32 grid and write the codebook.
+__global__ void __launch_bounds__(64) k_lloyd_update(const CodebookParams p, int chunks, int last) {
+  if (threadIdx.x != 0) return;
+  double s1 = 0.0, c1 = 0.0, s2 = 0.0, c2 = 0.0;
+  for (int w = 0; w < chunks; ++w) {
+    s1 += p.partial[(size_t)w * 4 + 0];
+    c1 += p.partial[(size_t)w * 4 + 1];
+    s2 += p.partial[(size_t)w * 4 + 2];
+    c2 += p.partial[(size_t)w * 4 + 3];
+  }
+  if (c1 > 0.0) p.state[1] = s1 / c1;
+  if (c2 > 0.0) p.state[2] = s2 / c2;
+  if (last) {
+    p.levels[0] = 0.f;
+    p.levels[1] = (float)(rint(p.state[1] * 32.0) / 32.0);
+    p.levels[2] = (float)(rint(p.state[2] * 32.0) / 32.0);
+    p.levels[3] = 3.f;
+  }
+}
+
+__global__ void k_lloyd_init(const CodebookParams p) {
+  if (threadIdx.x == 0) {
+    p.state[0] = 0.0;
+    p.state[1] = 1.0;
+    p.state[2] = 2.0;
+    p.state[3] = 3.0;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dequantize INT2 pages back to dense vectors in the model basis
 // ---------------------------------------------------------------------------
 // Grid (page chunks, KV heads), 4 waves.  R^T sits in LDS transposed so that
@@ -719,7 +875,8 @@ __global__ void __launch_bounds__(256) k_dequantize(const DequantParams p) {
       const uint8_t* szp = blk + 8 * D + q * 32 * NG + (p.which ? 16 * NG : 0) + (tok % 4) * NG * 4 + g * 4;
       const uint32_t sz = *(const uint32_t*)szp;
       const float s = bf16_lo(sz), z = bf16_hi(sz);
-      yh[tok][c] = ok ? s * ((float)code - z) : 0.f;
+      const float lvl = code == 0 ? p.levels[0] : code == 1 ? p.levels[1] : code == 2 ? p.levels[2] : p.levels[3];
+      yh[tok][c] = ok ? s * (lvl - z) : 0.f;
     }
     __syncthreads();
     for (int e = tid; e < 16 * D; e += 256) {
@@ -800,6 +957,23 @@ bool launch_clip(const ClipParams& p, hipStream_t stream) {
   for (int pass = 0; pass < 4; ++pass) {
     k_select_hist<<<dim3(p.chunks, p.heads), 256, 0, stream>>>(p, pass);
     k_select_scan<<<p.heads, 256, 0, stream>>>(p, pass, p.chunks);
+  }
+  return true;
+}
+
+bool launch_codebook(const CodebookParams& p, int iterations, hipStream_t stream) {
+  const int nblk = (p.rows + 15) / 16;
+  const int gx = std::max(1, std::min((nblk + 3) / 4, std::max(1, 256 / p.heads)));
+  if (p.dim == 128)
+    k_normalize<128><<<dim3(gx, p.heads), 256, 0, stream>>>(p);
+  else if (p.dim == 64)
+    k_normalize<64><<<dim3(gx, p.heads), 256, 0, stream>>>(p);
+  else
+    return false;
+  k_lloyd_init<<<1, 64, 0, stream>>>(p);
+  for (int it = 0; it < iterations; ++it) {
+    k_lloyd_partial<<<p.chunks, 256, 0, stream>>>(p);
+    k_lloyd_update<<<1, 64, 0, stream>>>(p, p.chunks, it == iterations - 1);
   }
   return true;
 }

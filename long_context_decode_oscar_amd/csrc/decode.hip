@@ -307,6 +307,20 @@ __device__ __forceinline__ void i2_fetch(I2Tile<D, NG, GQA>& t, const uint8_t* _
   t.nvalid = nv;
 }
 
+// The 2-bit K codes of a record word as int8 operands: code c of channel
+// 4b + k sits in byte 4k + b of component k; with a codebook each byte
+// becomes 32 L[c] by one byte permute.
+template <bool LUT>
+__device__ __forceinline__ v4i k_operand(uint32_t x, uint32_t lut_k) {
+  v4i a = {(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
+           (int)((x >> 6) & 0x03030303u)};
+  if constexpr (LUT) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = (int)__builtin_amdgcn_perm(lut_k, lut_k, (uint32_t)a[k]);
+  }
+  return a;
+}
+
 template <int NG>
 struct I2Scores {
   v4i a[NG], b[NG];  // integer dots with the two int8 terms of q', per group
@@ -315,9 +329,9 @@ struct I2Scores {
 // Scores of one tile on the int8 matrix cores (block-diagonal B operands:
 // slot s's page meets only the columns of slot s).  The operands are
 // loop-invariant and held in VGPRs.
-template <int D, int NG, int GQA>
+template <int D, int NG, int GQA, bool LUT>
 __device__ __forceinline__ I2Scores<NG> i2_scores(const I2Tile<D, NG, GQA>& t,
-                                                  const v4i (&bq)[DC<D, NG, GQA>::SLOTS][2][D / 64]) {
+                                                  const v4i (&bq)[DC<D, NG, GQA>::SLOTS][2][D / 64], uint32_t lut_k) {
   using C = DC<D, NG, GQA>;
   I2Scores<NG> r;
 #pragma unroll
@@ -326,9 +340,7 @@ __device__ __forceinline__ I2Scores<NG> i2_scores(const I2Tile<D, NG, GQA>& t,
   for (int s = 0; s < C::SLOTS; ++s) {
 #pragma unroll
     for (int w = 0; w < C::KW; ++w) {
-      const uint32_t x = t.kw[s][w];
-      const v4i a = {(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
-                     (int)((x >> 6) & 0x03030303u)};
+      const v4i a = k_operand<LUT>(t.kw[s][w], lut_k);
       const int g = (NG == 1) ? 0 : w;
       r.a[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq[s][0][w], r.a[g], 0, 0, 0);
       r.b[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq[s][1][w], r.b[g], 0, 0, 0);
@@ -355,18 +367,34 @@ constexpr uint32_t kMaskLo = 0x00C000C0u, kExpLo = 0x4C004C00u;  // tokens i = 0
 constexpr uint32_t kMaskHi = 0x03000300u, kExpHi = 0x44004400u;  // tokens i = 2,3: 4 + code
 constexpr float kBiasLo = 16.f, kBiasHi = 4.f;
 
-template <int D, int NG, int W0>
+// With a codebook every operand is 16 + L[code] (bias 16 for all tokens):
+// the fp16 pattern 0x4C00 | 64 L[code], built by one byte permute per
+// operand word from the shifted codes (selector 4 picks the 0x4C byte).
+constexpr uint32_t kLutHigh = 0x4C4C4C4Cu, kLutSel = 0x04000400u;
+template <int BB, int I>
+__device__ __forceinline__ uint32_t lut_operand(uint32_t x, uint32_t lut_v) {
+  const uint32_t sel = ((x >> (4 * BB + 2 * I)) & 0x00030003u) | kLutSel;
+  return __builtin_amdgcn_perm(kLutHigh, lut_v, sel);
+}
+
+template <int D, int NG, int W0, bool LUT>
 __device__ __forceinline__ void pv_block_pair(Acc<D, NG>& st, uint32_t x0, uint32_t x1, const v4i (&bw)[NG],
-                                              uint32_t exp_lo, uint32_t exp_hi) {
+                                              uint32_t exp_lo, uint32_t exp_hi, uint32_t lut_v) {
   constexpr int G = D / NG;
   // the four channel blocks of this word pair, two pages per MFMA (k = 32)
   auto one = [&](auto bbc) {
     constexpr int BB = decltype(bbc)::value;
     constexpr int cblk = 4 * W0 + BB;
     constexpr int g = (cblk * 16) / G;
-    const uint32_t y0 = v_shift<BB>(x0), y1 = v_shift<BB>(x1);
-    const v4i a = {(int)((y0 & kMaskLo) | exp_lo), (int)((y0 & kMaskHi) | exp_hi), (int)((y1 & kMaskLo) | exp_lo),
-                   (int)((y1 & kMaskHi) | exp_hi)};
+    v4i a;
+    if constexpr (LUT) {
+      a = v4i{(int)lut_operand<BB, 0>(x0, lut_v), (int)lut_operand<BB, 1>(x0, lut_v),
+              (int)lut_operand<BB, 0>(x1, lut_v), (int)lut_operand<BB, 1>(x1, lut_v)};
+    } else {
+      const uint32_t y0 = v_shift<BB>(x0), y1 = v_shift<BB>(x1);
+      a = v4i{(int)((y0 & kMaskLo) | exp_lo), (int)((y0 & kMaskHi) | exp_hi), (int)((y1 & kMaskLo) | exp_lo),
+              (int)((y1 & kMaskHi) | exp_hi)};
+    }
     st.o[cblk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, bw[g]),
                                                         st.o[cblk], 0, 0, 0);
   };
@@ -384,7 +412,7 @@ template <int D, int NG, int GQA>
 struct I2Weights {
   v4i bw[DC<D, NG, GQA>::SLOTS / 2][NG];  // block-diagonal B operands of the P.V MFMAs
 };
-template <int D, int NG, int GQA>
+template <int D, int NG, int GQA, bool LUT>
 __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, GQA>& t, const I2Scores<NG>& S,
                                                            Acc<D, NG>& st, float kappa, const float (&sig)[NG],
                                                            int my_slot) {
@@ -396,7 +424,8 @@ __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, 
     float acc = 0.f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const float sint = (float)(S.a[g][i] * 256 + S.b[g][i]);
+      // with a codebook the integer dot holds 32 L[code]
+      const float sint = (float)(S.a[g][i] * 256 + S.b[g][i]) * (LUT ? 1.f / 32.f : 1.f);
       const uint32_t sz = t.sc[i * NG + g];
       acc += bf16_lo(sz) * (sint - bf16_hi(sz) * sig[g]);
     }
@@ -417,7 +446,7 @@ __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, 
     for (int i = 0; i < 4; ++i) {
       const uint32_t sz = t.sc[4 * NG + i * NG + g];
       w[i] = pr[i] * bf16_lo(sz);
-      zb[i] = bf16_hi(sz) + (i < 2 ? kBiasLo : kBiasHi);
+      zb[i] = bf16_hi(sz) + (LUT || i < 2 ? kBiasLo : kBiasHi);
     }
     const h2 w01 = __builtin_convertvector(f2{w[0], w[1]}, h2);
     const h2 w23 = __builtin_convertvector(f2{w[2], w[3]}, h2);
@@ -433,15 +462,15 @@ __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, 
 }
 
 // P.V of one INT2 tile on the fp16 matrix cores, two pages per MFMA.
-template <int D, int NG, int GQA>
+template <int D, int NG, int GQA, bool LUT>
 __device__ __forceinline__ void i2_pv(const I2Tile<D, NG, GQA>& t, const I2Weights<D, NG, GQA>& W, Acc<D, NG>& st,
-                                      uint32_t exp_lo, uint32_t exp_hi) {
+                                      uint32_t exp_lo, uint32_t exp_hi, uint32_t lut_v) {
   using C = DC<D, NG, GQA>;
 #pragma unroll
   for (int pp = 0; pp < C::SLOTS / 2; ++pp) {
-    pv_block_pair<D, NG, 0>(st, t.vw[2 * pp][0], t.vw[2 * pp + 1][0], W.bw[pp], exp_lo, exp_hi);
+    pv_block_pair<D, NG, 0, LUT>(st, t.vw[2 * pp][0], t.vw[2 * pp + 1][0], W.bw[pp], exp_lo, exp_hi, lut_v);
     if constexpr (C::KW > 1)
-      pv_block_pair<D, NG, 1>(st, t.vw[2 * pp][1], t.vw[2 * pp + 1][1], W.bw[pp], exp_lo, exp_hi);
+      pv_block_pair<D, NG, 1, LUT>(st, t.vw[2 * pp][1], t.vw[2 * pp + 1][1], W.bw[pp], exp_lo, exp_hi, lut_v);
   }
 }
 
@@ -591,7 +620,7 @@ __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, in
 }
 
 // ------------------------------------------------------------- kernel ----
-template <int D, int NG, int GQA, bool BF16_ONLY>
+template <int D, int NG, int GQA, bool BF16_ONLY, bool LUT>
 __global__ void __launch_bounds__(kThreads)
     k_decode(const DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ bf16_pt_all,
              const int32_t* __restrict__ int2_pt_all, const uint8_t* __restrict__ bf16_pool,
@@ -832,7 +861,8 @@ __global__ void __launch_bounds__(kThreads)
     Acc<D, NG> st;
     st.init();
     if (nt_w > 0) {
-      I2Scores<NG> S = i2_scores<D, NG, GQA>(ring[0], bqr);
+      const uint32_t lut_k = p.lut_k, lut_v = p.lut_v;
+      I2Scores<NG> S = i2_scores<D, NG, GQA, LUT>(ring[0], bqr, lut_k);
       int i = 0;
       while (true) {
 #pragma unroll
@@ -841,9 +871,9 @@ __global__ void __launch_bounds__(kThreads)
           fetch(ring[(r + R - 1) % R], i + R - 1);
           // softmax of tile i first: the wait for tile i+1's data comes
           // after it, next to the MFMAs that need that data
-          const I2Weights<D, NG, GQA> W = i2_softmax<D, NG, GQA>(ring[r], S, st, kappa, sig, my_slot);
-          S = i2_scores<D, NG, GQA>(ring[(r + 1) % R], bqr);
-          i2_pv<D, NG, GQA>(ring[r], W, st, exp_lo, exp_hi);
+          const I2Weights<D, NG, GQA> W = i2_softmax<D, NG, GQA, LUT>(ring[r], S, st, kappa, sig, my_slot);
+          S = i2_scores<D, NG, GQA, LUT>(ring[(r + 1) % R], bqr, lut_k);
+          i2_pv<D, NG, GQA, LUT>(ring[r], W, st, exp_lo, exp_hi, lut_v);
           // slots r and r+1 hold arrived data (the loads of r+2 .. r+R-1 may
           // still be in flight and are left alone)
           ring[r].pin();
@@ -1127,7 +1157,7 @@ __device__ __forceinline__ void pt_fetch(PTile<D, NG>& t, const uint8_t* __restr
 // Softmax of one prefix tile (both pages, every column): logits with tokens
 // past the column's member history masked, online max and sum, and the dense
 // fp16 P.V B operands.
-template <int D, int NG>
+template <int D, int NG, bool LUT>
 __device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores<NG> (&S)[2], Acc<D, NG>& st,
                                            float kappa, const float (&sig)[NG], int lp0, int hist_len, int lane,
                                            v4i (&bw)[NG]) {
@@ -1140,7 +1170,7 @@ __device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores
       float acc = 0.f;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float sint = (float)(S[s].a[g][i] * 256 + S[s].b[g][i]);
+        const float sint = (float)(S[s].a[g][i] * 256 + S[s].b[g][i]) * (LUT ? 1.f / 32.f : 1.f);
         const uint32_t sz = t.sc[s][i * NG + g];
         acc += bf16_lo(sz) * (sint - bf16_hi(sz) * sig[g]);
       }
@@ -1165,7 +1195,7 @@ __device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores
       for (int i = 0; i < 4; ++i) {
         const uint32_t sz = t.sc[s][4 * NG + i * NG + g];
         w[i] = pr[s][i] * bf16_lo(sz);
-        zb[i] = bf16_hi(sz) + (i < 2 ? kBiasLo : kBiasHi);
+        zb[i] = bf16_hi(sz) + (LUT || i < 2 ? kBiasLo : kBiasHi);
       }
       const h2 w01 = __builtin_convertvector(f2{w[0], w[1]}, h2);
       const h2 w23 = __builtin_convertvector(f2{w[2], w[3]}, h2);
@@ -1178,7 +1208,7 @@ __device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores
   }
 }
 
-template <int D, int NG, int GQA>
+template <int D, int NG, int GQA, bool LUT>
 __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p) {
   constexpr int KW = D / 64, G = D / NG, BLK2 = 8 * D + 128 * NG;
   constexpr int MEMBERS = 16 / GQA;  // member sequences per unit (columns = members x heads)
@@ -1350,6 +1380,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
     for (int w = 0; w < KW; ++w) bqr[t][w] = sm.bq[t][w][lane];
   __syncthreads();  // the union's qpart is reused for the partials below
 
+  const uint32_t lut_k = p.lut_k, lut_v = p.lut_v;
   auto scores = [&](const PTile<D, NG>& t, I2Scores<NG> (&S)[2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -1357,9 +1388,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
       for (int g = 0; g < NG; ++g) S[s].a[g] = S[s].b[g] = v4i{0, 0, 0, 0};
 #pragma unroll
       for (int w = 0; w < KW; ++w) {
-        const uint32_t x = t.kw[s][w];
-        const v4i a = {(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
-                       (int)((x >> 6) & 0x03030303u)};
+        const v4i a = k_operand<LUT>(t.kw[s][w], lut_k);
         const int g = (NG == 1) ? 0 : w;
         S[s].a[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[0][w], S[s].a[g], 0, 0, 0);
         S[s].b[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[1][w], S[s].b[g], 0, 0, 0);
@@ -1379,10 +1408,11 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
         if (i >= nt_w) break;
         fetch(ring[(r + R - 1) % R], i + R - 1);
         v4i bw[NG];
-        pt_softmax<D, NG>(ring[r], S, st, kappa, sig, first + (wave + i * kWaves) * 2, my_hist, lane, bw);
+        pt_softmax<D, NG, LUT>(ring[r], S, st, kappa, sig, first + (wave + i * kWaves) * 2, my_hist, lane, bw);
         scores(ring[(r + 1) % R], S);
-        pv_block_pair<D, NG, 0>(st, ring[r].vw[0][0], ring[r].vw[1][0], bw, exp_lo, exp_hi);
-        if constexpr (KW > 1) pv_block_pair<D, NG, 1>(st, ring[r].vw[0][1], ring[r].vw[1][1], bw, exp_lo, exp_hi);
+        pv_block_pair<D, NG, 0, LUT>(st, ring[r].vw[0][0], ring[r].vw[1][0], bw, exp_lo, exp_hi, lut_v);
+        if constexpr (KW > 1)
+          pv_block_pair<D, NG, 1, LUT>(st, ring[r].vw[0][1], ring[r].vw[1][1], bw, exp_lo, exp_hi, lut_v);
         ring[r].pin();
         ring[(r + 1) % R].pin();
         ++i;
@@ -1440,7 +1470,10 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
 
 template <int D, int NG, int GQA>
 bool launch_prefix_t(const DecodeParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA>), dim3(grid), dim3(kThreads), 0, stream, p);
+  if (p.lut)
+    hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return true;
 }
 
@@ -1473,11 +1506,14 @@ __global__ void __launch_bounds__(256) k_merge(const MergeParams p) {
 template <int D, int NG, int GQA>
 bool launch_decode_t(const DecodeParams& p, bool bf16_only, int grid, hipStream_t stream) {
   if (bf16_only)
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, true>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens, p.bf16_pt,
-                       p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, true, false>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens,
+                       p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+  else if (p.lut)
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, false, true>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens,
+                       p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
   else
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, false>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens, p.bf16_pt,
-                       p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, false, false>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens,
+                       p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
   return true;
 }
 

@@ -49,6 +49,9 @@ struct DecodeParams {
   int32_t units_per_head;    // workgroups per (sequence, KV head): n_bf16_units + max_chunks
   int32_t slots_per_head;    // partial slots per (sequence, KV head): units_per_head + max prefix chunks
   float sm_log2;             // softmax scale * log2(e)
+  int32_t lut;               // 1: four-level codebook
+  uint32_t lut_k;            // byte c: 32 L_K[c] (int8 score operand of code c)
+  uint32_t lut_v;            // byte c: 64 L_V[c] (mantissa of the fp16 operand 16 + L_V[c])
   int32_t n_casc;            // prefix-shared units (0: plain decode)
   CascUnit casc[kMaxCascUnits];
 };
@@ -90,6 +93,8 @@ struct WriteParams {
   const float* tau_k;        // [Hkv]
   const float* tau_v;
   int32_t batch, num_kv_heads, sink, recent;
+  int32_t lut;               // 1: four-level codebook, codes by the thresholds below
+  float thr_k[3], thr_v[3];  // midpoints of consecutive levels
 };
 bool launch_append_demote(const WriteParams& p, int head_dim, int n_groups, hipStream_t stream);
 bool launch_quantize_pack(const WriteParams& p, int head_dim, int n_groups, hipStream_t stream);
@@ -155,6 +160,22 @@ struct ClipParams {
 };
 bool launch_clip(const ClipParams& p, hipStream_t stream);
 
+// Four-level codebook fit: normalized values of x R (clipped to tau, per
+// group of group_size channels) into t, then Lloyd iterations.
+struct CodebookParams {
+  const float* x;                   // row r of head h at x + h*head_stride + r*row_stride
+  int64_t head_stride, row_stride;
+  int32_t heads, rows, dim, group_size;
+  const float* r;                   // [heads][D][D] or null
+  const float* tau;                 // [heads] device
+  float* t;                         // [heads][rows][D] workspace
+  double* partial;                  // [chunks][4] workspace
+  double* state;                    // [4] workspace: current levels
+  float* levels;                    // [4] result
+  int32_t chunks;
+};
+bool launch_codebook(const CodebookParams& p, int iterations, hipStream_t stream);
+
 struct DequantParams {
   const int32_t* page_ids;          // [ceil(num_tokens / 16)]
   const uint8_t* int2_pool;
@@ -162,6 +183,7 @@ struct DequantParams {
   float* out;                       // [num_tokens][Hkv][D]
   int32_t num_tokens, int2_num_pages, num_kv_heads;
   int32_t which;                    // 0: keys, 1: values
+  float levels[4];                  // code -> level in code units (0, 1, 2, 3 when uniform)
 };
 bool launch_dequantize(const DequantParams& p, int dim, int n_groups, hipStream_t stream);
 

@@ -138,6 +138,32 @@ Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
   return pl;
 }
 
+// ---- codebook ----
+bool levels_ok(const float* l) {
+  if (!(l[0] == 0.f && l[3] == 3.f && l[0] < l[1] && l[1] < l[2] && l[2] < l[3])) return false;
+  for (int k = 1; k < 3; ++k)
+    if (l[k] * 32.f != rintf(l[k] * 32.f)) return false;
+  return true;
+}
+// byte c = scale * L[c] (exact integers for the valid levels)
+uint32_t lut_word(const float* l, float scale) {
+  uint32_t w = 0;
+  for (int c = 0; c < 4; ++c) w |= ((uint32_t)lrintf(l[c] * scale) & 0xFFu) << (8 * c);
+  return w;
+}
+void set_codebook(const oscar_pool* pool, oscar::DecodeParams& p) {
+  p.lut = pool->cfg.codebook;
+  p.lut_k = pool->cfg.codebook ? lut_word(pool->cfg.levels_k, 32.f) : 0u;
+  p.lut_v = pool->cfg.codebook ? lut_word(pool->cfg.levels_v, 64.f) : 0u;
+}
+void set_codebook(const oscar_pool* pool, oscar::WriteParams& p) {
+  p.lut = pool->cfg.codebook;
+  for (int k = 0; k < 3; ++k) {
+    p.thr_k[k] = 0.5f * (pool->cfg.levels_k[k] + pool->cfg.levels_k[k + 1]);
+    p.thr_v[k] = 0.5f * (pool->cfg.levels_v[k] + pool->cfg.levels_v[k + 1]);
+  }
+}
+
 // ---- prefix-shared (cascade) planning ----
 struct CascPlan {
   int n = 0;              // units
@@ -326,6 +352,19 @@ oscar_status run_rotation(int heads, int d, const float* cov, int mix, float* r,
   return check_hip("eigen/rotation launch");
 }
 
+constexpr int kLloydChunks = 128, kLloydIterations = 100;
+struct CodebookWs {
+  size_t t, partial, state, bytes;
+};
+CodebookWs codebook_ws(int heads, int rows, int d) {
+  CodebookWs w;
+  w.t = 0;
+  w.partial = up256((size_t)heads * rows * d * 4);
+  w.state = w.partial + up256((size_t)kLloydChunks * 4 * sizeof(double));
+  w.bytes = w.state + 256;
+  return w;
+}
+
 struct CalibWs {
   size_t part, o, cq, cs, clip, bytes;
 };
@@ -377,6 +416,9 @@ oscar_status oscar_pool_create(const oscar_config* cfg, oscar_pool** out, oscar_
   if (c.group_size != 64 && c.group_size != 128) return fail(OSCAR_ERR_UNSUPPORTED, "group_size must be 64 or 128");
   if (gqa != 2 && gqa != 4 && gqa != 8) return fail(OSCAR_ERR_UNSUPPORTED, "num_q_heads/num_kv_heads must be 2, 4 or 8");
   if (c.v_absorbed != 0 && c.v_absorbed != 1) return fail(OSCAR_ERR_INVALID, "v_absorbed must be 0 or 1");
+  if (c.codebook != 0 && c.codebook != 1) return fail(OSCAR_ERR_INVALID, "codebook must be 0 or 1");
+  if (c.codebook && (!levels_ok(c.levels_k) || !levels_ok(c.levels_v)))
+    return fail(OSCAR_ERR_INVALID, "codebook levels must be 0 < L1 < L2 < 3 (ends 0 and 3), multiples of 1/32");
   oscar_pool* p = new (std::nothrow) oscar_pool;
   if (!p) return fail(OSCAR_ERR_INVALID, "out of host memory");
   p->cfg = c;
@@ -475,6 +517,7 @@ oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_
   p.units_per_head = pl.units;
   p.slots_per_head = pl.slots;
   p.sm_log2 = pool->sm_scale * 1.4426950408889634f;
+  set_codebook(pool, p);
   p.n_casc = cp.n;
   for (int i = 0; i < cp.n; ++i) p.casc[i] = cp.units[i];
   // prefix partials first (same stream): the decode launch's merge reads them
@@ -631,6 +674,7 @@ oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const vo
   p.num_kv_heads = c.num_kv_heads;
   p.sink = c.sink_tokens;
   p.recent = c.recent_tokens;
+  set_codebook(pool, p);
   if (!oscar::launch_append_demote(p, c.head_dim, pool->n_groups, (hipStream_t)stream))
     return fail(OSCAR_ERR_UNSUPPORTED, "no append/demote kernel for this shape");
   return check_hip("append/demote launch");
@@ -672,6 +716,7 @@ oscar_status oscar_quantize_pack(const oscar_pool* pool, int32_t num_tokens, con
   p.num_kv_heads = c.num_kv_heads;
   p.sink = c.sink_tokens;
   p.recent = c.recent_tokens;
+  set_codebook(pool, p);
   if (!oscar::launch_quantize_pack(p, c.head_dim, pool->n_groups, (hipStream_t)stream))
     return fail(OSCAR_ERR_UNSUPPORTED, "no quantize/pack kernel for this shape");
   return check_hip("quantize/pack launch");
@@ -771,6 +816,44 @@ oscar_status oscar_calib_clip(int32_t heads, int32_t rows, int32_t head_dim, con
                   (hipStream_t)stream);
 }
 
+oscar_status oscar_calib_codebook_workspace_bytes(int32_t heads, int32_t rows, int32_t head_dim, size_t* bytes) {
+  if (!bytes || heads <= 0 || rows <= 0) return fail(OSCAR_ERR_INVALID, "bytes must be non-null, heads and rows positive");
+  if (!supported_dim(head_dim)) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  *bytes = codebook_ws(heads, rows, head_dim).bytes;
+  return ok();
+}
+
+oscar_status oscar_calib_codebook(int32_t heads, int32_t rows, int32_t head_dim, int32_t group_size, const float* x,
+                                  int64_t head_stride, int64_t row_stride, const float* r, const float* tau,
+                                  float* levels, void* workspace, size_t workspace_bytes, void* stream) {
+  oscar_status st = check_rows("codebook", x, heads, rows, head_dim, head_stride, row_stride);
+  if (st != OSCAR_OK) return st;
+  if (group_size != 64 && group_size != 128) return fail(OSCAR_ERR_UNSUPPORTED, "group_size must be 64 or 128");
+  if (head_dim % group_size) return fail(OSCAR_ERR_INVALID, "group_size must divide head_dim");
+  if (!tau || !levels) return fail(OSCAR_ERR_INVALID, "tau and levels must be non-null");
+  const CodebookWs w = codebook_ws(heads, rows, head_dim);
+  if (!workspace || workspace_bytes < w.bytes || ((uintptr_t)workspace & 255u))
+    return fail(OSCAR_ERR_WORKSPACE, "codebook fit needs %zu bytes of 256-byte aligned workspace", w.bytes);
+  oscar::CodebookParams p{};
+  p.x = x;
+  p.head_stride = head_stride;
+  p.row_stride = row_stride;
+  p.heads = heads;
+  p.rows = rows;
+  p.dim = head_dim;
+  p.group_size = group_size;
+  p.r = r;
+  p.tau = tau;
+  p.t = (float*)((char*)workspace + w.t);
+  p.partial = (double*)((char*)workspace + w.partial);
+  p.state = (double*)((char*)workspace + w.state);
+  p.levels = levels;
+  p.chunks = kLloydChunks;
+  if (!oscar::launch_codebook(p, kLloydIterations, (hipStream_t)stream))
+    return fail(OSCAR_ERR_UNSUPPORTED, "no codebook kernel for this shape");
+  return check_hip("codebook launch");
+}
+
 oscar_status oscar_calib_workspace_bytes(int32_t kv_heads, int32_t gqa, int32_t tokens, int32_t head_dim,
                                          size_t* bytes) {
   if (!bytes || kv_heads <= 0 || gqa <= 0 || tokens <= 0)
@@ -835,6 +918,8 @@ oscar_status oscar_dequantize(const oscar_pool* pool, int32_t num_tokens, const 
     p.which = which;
     p.r = which ? r_v : r_k;
     p.out = which ? v_out : k_out;
+    for (int k = 0; k < 4; ++k)
+      p.levels[k] = c.codebook ? (which ? c.levels_v[k] : c.levels_k[k]) : (float)k;
     if (!oscar::launch_dequantize(p, c.head_dim, pool->n_groups, (hipStream_t)stream))
       return fail(OSCAR_ERR_UNSUPPORTED, "no dequantize kernel for this shape");
   }

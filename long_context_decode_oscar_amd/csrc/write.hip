@@ -48,8 +48,19 @@ __device__ __forceinline__ void scale_zero(float mn, float mx, uint32_t& s_bits,
   z_bits = f32_to_bf16(-mn / s);
   z = bf16_to_f32(z_bits);
 }
-__device__ __forceinline__ uint32_t quant_code(float c, float s, float z) {
+// Four-level codebook: the code of t = c/s + z is the number of thresholds
+// (midpoints of consecutive levels, exact in fp32) strictly below t; off:
+// the uniform levels 0..3 with round-to-nearest-even and clamp.
+struct Thr {
+  float b0, b1, b2;
+  bool on;
+};
+__device__ __forceinline__ uint32_t thr_code(float t, const Thr& th) {
+  return (uint32_t)(t > th.b0) + (uint32_t)(t > th.b1) + (uint32_t)(t > th.b2);
+}
+__device__ __forceinline__ uint32_t quant_code(float c, float s, float z, const Thr& th) {
   const float t = __fadd_rn(c / s, z);
+  if (th.on) return thr_code(t, th);
   return (uint32_t)fminf(fmaxf(rintf(t), 0.f), 3.f);
 }
 
@@ -178,7 +189,9 @@ __global__ void __launch_bounds__(256) k_append_demote(const WriteParams p) {
     uint32_t sb, zb;
     float s, z;
     scale_zero(mn, mx, sb, zb, s, z);
-    codes[which][c] = (uint8_t)quant_code(x, s, z);
+    const Thr th = which == 0 ? Thr{p.thr_k[0], p.thr_k[1], p.thr_k[2], p.lut != 0}
+                              : Thr{p.thr_v[0], p.thr_v[1], p.thr_v[2], p.lut != 0};
+    codes[which][c] = (uint8_t)quant_code(x, s, z, th);
     if (c % G == 0) sz[which][g] = sb | (zb << 16);
   }
   __syncthreads();
@@ -312,12 +325,27 @@ __device__ __forceinline__ void scale_zero_recip(float mn, float mx, uint32_t& s
 // 2^-9 |z| <= 0.251 of -min/s; so the clamp to [0, 3] never acts.  Other
 // groups take the IEEE division, round and clamp.
 template <int N>
-__device__ __forceinline__ uint32_t group_codes(const float (&x)[N], float mn, float mx, uint32_t (&words)[N / 4]) {
+__device__ __forceinline__ uint32_t group_codes(const float (&x)[N], float mn, float mx, uint32_t (&words)[N / 4],
+                                                const Thr& th) {
   uint32_t sb, zb;
   float s, z, y;
   scale_zero_recip(mn, mx, sb, zb, s, z, y);
   const bool fast = s >= 0x1p-70f && fmaxf(fabsf(mn), fabsf(mx)) <= 0x1p56f && fabsf(z) <= 128.f;
-  if (fast) {
+  if (th.on) {
+    // codebook: the same t as below (exact quotient, then + z), compared
+    // with the thresholds
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xq = x[4 * q + e];
+        const float t = __fadd_rn(fast ? div_bf16(xq, s, y) : xq / s, z);
+        word |= thr_code(t, th) << (8 * e);
+      }
+      words[q] = word;
+    }
+  } else if (fast) {
 #pragma unroll
     for (int q = 0; q < N / 4; ++q) {
       uint32_t word = 0;
@@ -427,7 +455,7 @@ __device__ __forceinline__ void rotate_page(const uint4 (&xb)[D / 32], const uin
 // group scale words are returned in sz.
 template <int D, int NG, bool CHANNEL_ORDER>
 __device__ __forceinline__ void quant_rotated(const float (&y)[D / 16][4], float tau, uint32_t (&words)[D / 64][4],
-                                              uint32_t (&sz)[NG]) {
+                                              uint32_t (&sz)[NG], const Thr& th) {
   constexpr int KW = D / 64, WPG = KW / NG;  // record words per group
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -442,7 +470,7 @@ __device__ __forceinline__ void quant_rotated(const float (&y)[D / 16][4], float
       mx = fmaxf(mx, x[u]);
     }
     uint32_t ww[WPG * 4];
-    sz[g] = group_codes<WPG * 16>(x, col4_min(mn), col4_max(mx), ww);
+    sz[g] = group_codes<WPG * 16>(x, col4_min(mn), col4_max(mx), ww, th);
 #pragma unroll
     for (int u = 0; u < WPG * 4; ++u) words[g * WPG + u / 4][u % 4] = ww[u];
   }
@@ -458,6 +486,8 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const
   const int j = lane >> 4, r = lane & 15, t = lane >> 2, qq = lane & 3;
   const int tok0 = page * kPage;
   uint8_t(*vcode)[D] = sm.vcode[wave];
+  const Thr th_k{p.thr_k[0], p.thr_k[1], p.thr_k[2], p.lut != 0};
+  const Thr th_v{p.thr_v[0], p.thr_v[1], p.thr_v[2], p.lut != 0};
   // the page's INT2 block through a buffer descriptor: stores without a
   // physical page (num_records 0) or from lanes with nothing to store (offset
   // past the block) are dropped, so no store sits behind a branch
@@ -474,7 +504,7 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const
     rotate_page<D>(pg.ka, sm.rb, lane, y);
     const bool tok_ok = pg.id >= 0 && tok0 + r < p.num_tokens;
     uint32_t words[KW][4], sz[NG];
-    quant_rotated<D, NG, false>(y, tau_k, words, sz);
+    quant_rotated<D, NG, false>(y, tau_k, words, sz, th_k);
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
       // byte q of word i holds code m = 4q + i at bits 8q; shifted by 2i
@@ -494,7 +524,7 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const
     rotate_page<D>(pg.va, sm.rbv, lane, y);
     const bool tok_ok = pg.id >= 0 && tok0 + r < p.num_tokens;
     uint32_t words[KW][4], sz[NG];
-    quant_rotated<D, NG, true>(y, tau_v, words, sz);
+    quant_rotated<D, NG, true>(y, tau_v, words, sz, th_v);
 #pragma unroll
     for (int g = 0; g < NG; ++g)
       __builtin_amdgcn_raw_buffer_store_b32(
@@ -533,7 +563,7 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const
 #pragma unroll
       for (int u = 0; u < 32; ++u) xx[u] = x[u / 16][u % 16];
       uint32_t ww[8];
-      const uint32_t sz = group_codes<32>(xx, fminf(mn[0], mn[1]), fmaxf(mx[0], mx[1]), ww);
+      const uint32_t sz = group_codes<32>(xx, fminf(mn[0], mn[1]), fmaxf(mx[0], mx[1]), ww, th_v);
 #pragma unroll
       for (int u = 0; u < 8; ++u) words[u / 4][u % 4] = ww[u];
       __builtin_amdgcn_raw_buffer_store_b32(tok_ok ? sz : 0u, out,
@@ -544,7 +574,7 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const
       static_assert(NG == KW, "V groups are 64 channels wide here");
 #pragma unroll
       for (int w = 0; w < KW; ++w) {
-        const uint32_t sz = group_codes<16>(x[w], mn[w], mx[w], words[w]);
+        const uint32_t sz = group_codes<16>(x[w], mn[w], mx[w], words[w], th_v);
         __builtin_amdgcn_raw_buffer_store_b32(
             tok_ok ? sz : 0u, out, qq == 0 ? sc0 + 4 * ((t / 4) * 8 * NG + 4 * NG + (t % 4) * NG + w) : kDrop, 0, 0);
       }

@@ -51,9 +51,10 @@ def draw_inputs(wl, calib=None, **kw):
     return synthetic.draw_inputs(wl, calibration(wl) if calib is None else calib, **kw)
 
 
-def make_seqs(wl, inputs, r_k=None, tau_k=None, tau_v=None, r_v=None):
+def make_seqs(wl, inputs, r_k=None, tau_k=None, tau_v=None, r_v=None, levels=None):
     """Oracle pool state for every sequence of an Inputs draw.  With r_v the
-    pool does not absorb V: the history stores V R_V."""
+    pool does not absorb V: the history stores V R_V.  levels = (levels_k,
+    levels_v): the four-level codebook quantizer."""
     c = inputs.calib
     r_k = c.r_k if r_k is None else r_k
     tau_k = c.tau_k if tau_k is None else tau_k
@@ -62,16 +63,23 @@ def make_seqs(wl, inputs, r_k=None, tau_k=None, tau_v=None, r_v=None):
     for b, L in enumerate(wl.seq_lens):
         k = inputs.k[b][:L].float().numpy()
         v = inputs.v[b][:L].float().numpy()
+        lk, lv = (None, None) if levels is None else levels
         s = oracle.SeqPool(wl.num_kv_heads, wl.head_dim, wl.group_size, wl.sink, wl.recent,
-                           v_absorbed=r_v is None)
+                           v_absorbed=r_v is None, levels_k=lk, levels_v=lv)
         seqs.append(s.prefill(k, v, r_k, tau_k, tau_v, r_v))
     return seqs
 
 
-def pool_config(wl, v_absorbed=True):
+def pool_config(wl, v_absorbed=True, levels=None):
+    """Pool configuration of a workload; ``levels`` = (levels_k, levels_v)
+    selects the four-level codebook."""
     import long_context_decode_oscar_amd as oscar
+    if levels is None:
+        return oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16, wl.sink,
+                                wl.recent, 1 if v_absorbed else 0, 0.0)
     return oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16, wl.sink, wl.recent,
-                            1 if v_absorbed else 0, 0.0)
+                            1 if v_absorbed else 0, 0.0, 1, tuple(float(x) for x in levels[0]),
+                            tuple(float(x) for x in levels[1]))
 
 
 def to_dev(x, dtype=None):
@@ -115,11 +123,15 @@ def _bf16_neighbors_ok(got, ref, pre, slack):
     return abs(float(pre) - mid) <= slack
 
 
-def check_write(gpu, x, r, tau, gs, what, rot_err_rel=4e-5):
+def check_write(gpu, x, r, tau, gs, what, rot_err_rel=4e-5, levels=None):
     """gpu = (codes [N, D], s [N, NG], z [N, NG]) read back from the pool;
-    x [N, D] bf16 inputs; r rotation (None for pre-rotated input)."""
+    x [N, D] bf16 inputs; r rotation (None for pre-rotated input); levels: a
+    four-level codebook (None: the uniform levels)."""
     codes_g, s_g, z_g = gpu
     codes_o, s_o, z_o, y_o, c_o = oracle.quantize_tokens(x, r, tau, gs, return_intermediate=True)
+    if levels is not None:
+        # scale and zero are the uniform quantizer's; the codes the codebook's
+        codes_o = oracle.codebook.quantize_tokens(x, r, tau, gs, levels)[0]
     n, d = codes_o.shape
     ng = d // gs
     if r is None:
@@ -149,13 +161,18 @@ def check_write(gpu, x, r, tau, gs, what, rot_err_rel=4e-5):
     sgb = np.repeat(s_g, gs, axis=1)
     zgb = np.repeat(z_g, gs, axis=1)
     t = ((c_o / sgb).astype(np.float32) + zgb).astype(np.float32)
-    ref = np.clip(np.rint(t), 0, 3).astype(np.int64)
+    if levels is None:
+        ref = np.clip(np.rint(t), 0, 3).astype(np.int64)
+        mids = np.array([0.5, 1.5, 2.5])
+    else:
+        ref = oracle.codebook.encode(t, levels).astype(np.int64)
+        mids = oracle.codebook.thresholds(levels)
     got = codes_g.astype(np.int64)
     flips = np.argwhere(ref != got)
     for i, c in flips:
         assert abs(int(ref[i, c]) - int(got[i, c])) == 1, f"{what}: code jump at token {i} ch {c}"
         k = min(ref[i, c], got[i, c])
-        boundary = float(sgb[i, c]) * (k + 0.5 - float(zgb[i, c]))
+        boundary = float(sgb[i, c]) * (mids[k] - float(zgb[i, c]))
         assert abs(float(c_o[i, c]) - boundary) <= FLIP_TOL * float(sgb[i, c]), \
             f"{what}: flip at token {i} ch {c}: c={c_o[i, c]} boundary={boundary} s={sgb[i, c]}"
     log(f"{what}: {n} tokens, {sz_mism} scale/zero one-step differences, {len(flips)} allowed code flips")

@@ -114,7 +114,14 @@ def test_pool_create_validation_and_layout():
         (dict(page_size=32, sink_tokens=64), oscar.OSCAR_ERR_UNSUPPORTED),
         (dict(num_q_heads=8), oscar.OSCAR_ERR_UNSUPPORTED),
         (dict(v_absorbed=2), oscar.OSCAR_ERR_INVALID),
+        (dict(codebook=2), oscar.OSCAR_ERR_INVALID),
+        (dict(codebook=1, levels_k=(0, 1.01, 2, 3)), oscar.OSCAR_ERR_INVALID),   # not on the 1/32 grid
+        (dict(codebook=1, levels_v=(0, 2, 1, 3)), oscar.OSCAR_ERR_INVALID),      # not increasing
+        (dict(codebook=1, levels_k=(0.5, 1, 2, 3)), oscar.OSCAR_ERR_INVALID),    # ends must be 0 and 3
     ]
+    assert oscar.OscarPool(_cfg(codebook=1, levels_k=(0, 1.125, 1.875, 3), levels_v=(0, 0.03125, 2.96875, 3)))
+    # without the codebook flag the levels are ignored
+    assert oscar.OscarPool(_cfg(codebook=0, levels_k=(0, 2, 1, 3)))
     for kw, status in cases:
         with pytest.raises(oscar.OscarError) as e:
             oscar.OscarPool(_cfg(**kw))
@@ -217,6 +224,14 @@ def test_calibration_validation_fails_before_launch():
     assert lib.oscar_dequantize(p.handle, 0, None, 0, None, None, None, None, None, None) == oscar.OSCAR_OK
     assert lib.oscar_attention_error(8, 4, 64, 128, 0.0, F, F, F, None, F, 64 * 128, 128, F, None) == \
         oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_calib_codebook_workspace_bytes(8, 2048, 128, ctypes.byref(n)) == oscar.OSCAR_OK
+    assert n.value >= 8 * 2048 * 128 * 4
+    assert lib.oscar_calib_codebook(8, 64, 128, 96, F, 64 * 128, 128, None, F, F, F, 1 << 30, None) == \
+        oscar.OSCAR_ERR_UNSUPPORTED  # group size
+    assert lib.oscar_calib_codebook(8, 64, 128, 128, F, 64 * 128, 128, None, None, F, F, 1 << 30, None) == \
+        oscar.OSCAR_ERR_INVALID  # tau
+    assert lib.oscar_calib_codebook(8, 64, 128, 128, F, 64 * 128, 128, None, F, F, F, 64, None) == \
+        oscar.OSCAR_ERR_WORKSPACE
 
 
 def test_cascade_validation_fails_before_launch():
