@@ -62,6 +62,29 @@ def gpu_calibration(oscar, wl):
     return _CALIB_CACHE[key]
 
 
+_CODEBOOK_CACHE = {}
+
+
+def gpu_codebook(oscar, wl):
+    """Four-level codebooks (keys, values) of a workload's layer from
+    oscar_calib_codebook on the calibration draw, with the rotations and
+    thresholds of gpu_calibration."""
+    import torch
+    from synthetic import draw_calibration
+    key = (wl.num_kv_heads, wl.gqa, wl.head_dim, wl.group_size, wl.seed)
+    if key not in _CODEBOOK_CACHE:
+        c = gpu_calibration(oscar, wl)
+        draws = draw_calibration(wl.num_kv_heads, wl.gqa, wl.head_dim, wl.seed)
+        out = []
+        for name, r, tau in (("k", c.r_k, c.tau_k), ("v", c.r_v, c.tau_v)):
+            x = torch.from_numpy(np.stack([getattr(d, name) for d in draws])).cuda()
+            lv = oscar.oscar_calib_codebook(x, torch.from_numpy(r).cuda(), torch.from_numpy(tau).cuda(),
+                                            wl.group_size)
+            out.append(tuple(float(a) for a in lv.cpu().numpy()))
+        _CODEBOOK_CACHE[key] = tuple(out)
+    return _CODEBOOK_CACHE[key]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -71,6 +94,7 @@ def parse():
     ap.add_argument("--cold-bytes", type=float, default=2 * 2**30)
     ap.add_argument("--repeats", type=int, default=5)
     ap.add_argument("--no-bf16", action="store_true", help="skip the BF16-only comparator")
+    ap.add_argument("--no-codebook", action="store_true", help="skip the four-level codebook variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run N eager decode steps over the cold pool copies, then one plain copy of "
@@ -550,9 +574,16 @@ def bench_calibration(oscar, steps=10, warmup=2, repeats=5, profile_launches=0):
     oscar.oscar_calib_clip(v, had, 0.995, tau_h["v"])
     inf = torch.full((hkv,), float("inf"), dtype=torch.float32, device="cuda")
     variants = {"oscar": (res["r_k"], res["r_v"], res["tau_k"], res["tau_v"]),
+                "oscar_lloyd_max": (res["r_k"], res["r_v"], res["tau_k"], res["tau_v"]),
                 "hadamard_only": (had, had, tau_h["k"], tau_h["v"]),
                 "none": (eye, eye, inf, inf)}
     pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, hkv, d, wl.group_size, 16, wl.sink, wl.recent, 0, 0.0))
+    # the layer's codebooks, fitted on the same draw with the calibrated
+    # rotations and thresholds
+    lv_k = oscar.oscar_calib_codebook(k, res["r_k"], res["tau_k"], wl.group_size).cpu().numpy()
+    lv_v = oscar.oscar_calib_codebook(v, res["r_v"], res["tau_v"], wl.group_size).cpu().numpy()
+    lm_pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, hkv, d, wl.group_size, 16, wl.sink, wl.recent, 0, 0.0,
+                                               1, tuple(map(float, lv_k)), tuple(map(float, lv_v))))
     npg = (n + 15) // 16
     ids = torch.arange(npg, dtype=torch.int32, device="cuda")
     int2 = torch.zeros(npg, pool.int2_page_bytes, dtype=torch.uint8, device="cuda")
@@ -565,9 +596,11 @@ def bench_calibration(oscar, steps=10, warmup=2, repeats=5, profile_launches=0):
     pairs = hkv * g * n * (n + 1) / 2
     chain = {}
     for name, (rk, rv, tk, tv) in variants.items():
-        def run(i, rk=rk, rv=rv, tk=tk, tv=tv):
-            oscar.oscar_quantize_pack(pool, k_tok, v_tok, ids, int2, rk, tk, tv, r_v=rv)
-            oscar.oscar_dequantize(pool, n, ids, int2, rk, rv, kh, vh)
+        pl = lm_pool if name == "oscar_lloyd_max" else pool
+
+        def run(i, rk=rk, rv=rv, tk=tk, tv=tv, pl=pl):
+            oscar.oscar_quantize_pack(pl, k_tok, v_tok, ids, int2, rk, tk, tv, r_v=rv)
+            oscar.oscar_dequantize(pl, n, ids, int2, rk, rv, kh, vh)
             oscar.oscar_attention_error(q, k_ref, v_ref, kh.transpose(0, 1), vh.transpose(0, 1), stats)
         run(0)
         torch.cuda.synchronize()
@@ -587,6 +620,7 @@ def bench_calibration(oscar, steps=10, warmup=2, repeats=5, profile_launches=0):
                                                                                       FP32_MFMA_PEAK_TFLOPS, 2),
                                 "kernel": "k_calib_attention (fp32 MFMA causal attention)"},
             "error_chain": chain, "us_per_error_chain": round(ms_chain * 1e3, 1),
+            "codebooks": {"levels_k": [float(x) for x in lv_k], "levels_v": [float(x) for x in lv_v]},
             "error_chain_note": "quantize_pack -> dequantize -> attention_error on the calibration draw itself; "
                                 "logit_mse per causal pair, score_kl per query row, out_rel_mse = "
                                 "sum ||o - o^||^2 / sum ||o||^2"}
@@ -694,6 +728,21 @@ def main():
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_for(wl.name),
                      "kernel": "k_decode (INT2 split-K + BF16 sink/recent + LSE merge, one launch per step)"},
     }
+    if not args.no_codebook:
+        # the same step over pools written with the layer's Lloyd-Max codebook
+        levels = gpu_codebook(oscar, wl)
+        lpool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
+                                                 wl.sink, wl.recent, 1, 0.0, 1, levels[0], levels[1]))
+        lcopies, _ = build_pools(oscar, lpool, wl, inp, n_copies, seed=wl.seed + 3)
+        ldec = Decoder(oscar, lpool, wl, q, lens, lcopies, r_k, out, ws)
+        ms_lm, ms_lm_min = time_steps(ldec, args.steps, args.warmup, args.repeats, use_graph=True)
+        log(f"INT2 decode with the codebook (graph, cold): {ms_lm * 1e3:.2f} us/step, levels {levels}")
+        result["codebook_variant"] = {"levels_k": levels[0], "levels_v": levels[1],
+                                      "ms_per_step": round(ms_lm, 6), "ms_min": round(ms_lm_min, 6),
+                                      "GBps": round(kv["total"] / (ms_lm * 1e-3) / 1e9, 2),
+                                      "slowdown_vs_uniform": round(ms_lm / ms, 3)}
+        del ldec, lcopies
+        torch.cuda.empty_cache()
     if not args.no_bf16:
         n16 = max(1, math.ceil(args.cold_bytes / kv["bf16_only_total"]))
         bcopies, _ = build_pools(oscar, pool, wl, inp, n16, bf16_only=True, seed=wl.seed + 1)

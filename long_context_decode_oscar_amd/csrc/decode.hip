@@ -620,7 +620,7 @@ __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, in
 }
 
 // ------------------------------------------------------------- kernel ----
-template <int D, int NG, int GQA, bool BF16_ONLY, bool LUT>
+template <int D, int NG, int GQA, bool BF16_ONLY, bool LUT, bool CASC>
 __global__ void __launch_bounds__(kThreads)
     k_decode(const DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ bf16_pt_all,
              const int32_t* __restrict__ int2_pt_all, const uint8_t* __restrict__ bf16_pool,
@@ -646,7 +646,7 @@ __global__ void __launch_bounds__(kThreads)
   // prefix-shared unit of this sequence: its first S_u history pages and the
   // unit's prefix partials come from the prefix launch
   int S_u = 0, cch = 0;
-  if (!BF16_ONLY) {
+  if constexpr (CASC) {
     for (int i = 0; i < p.n_casc; ++i)
       if (b >= p.casc[i].first && b < p.casc[i].first + p.casc[i].count) {
         S_u = p.casc[i].shared_pages;
@@ -1503,17 +1503,28 @@ __global__ void __launch_bounds__(256) k_merge(const MergeParams p) {
   for (int q = 0; q < PER; ++q) p.out[(size_t)row * D + lane * PER + q] = (uint16_t)f32_to_bf16(acc[q] * inv);
 }
 
+// the INT2 decode, with the prefix-unit bookkeeping compiled in only when
+// the call has prefix units (CASC) and the codebook operands only for a
+// codebook pool (LUT)
+template <int D, int NG, int GQA, bool CASC>
+void launch_int2_t(const DecodeParams& p, int grid, hipStream_t stream) {
+  if (p.lut)
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, false, true, CASC>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+  else
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, false, false, CASC>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+}
+
 template <int D, int NG, int GQA>
 bool launch_decode_t(const DecodeParams& p, bool bf16_only, int grid, hipStream_t stream) {
   if (bf16_only)
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, true, false>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens,
-                       p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
-  else if (p.lut)
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, false, true>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens,
-                       p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, true, false, false>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+  else if (p.n_casc > 0)
+    launch_int2_t<D, NG, GQA, true>(p, grid, stream);
   else
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, false, false>), dim3(grid), dim3(kThreads), 0, stream, p, p.seq_lens,
-                       p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+    launch_int2_t<D, NG, GQA, false>(p, grid, stream);
   return true;
 }
 
