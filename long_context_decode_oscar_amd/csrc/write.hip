@@ -324,14 +324,14 @@ __device__ __forceinline__ void scale_zero_recip(float mn, float mx, uint32_t& s
 // 3(1 + 2^-8) because s is within 2^-9 of (max - min)/3, and z is within
 // 2^-9 |z| <= 0.251 of -min/s; so the clamp to [0, 3] never acts.  Other
 // groups take the IEEE division, round and clamp.
-template <int N>
+template <int N, bool LUT>
 __device__ __forceinline__ uint32_t group_codes(const float (&x)[N], float mn, float mx, uint32_t (&words)[N / 4],
                                                 const Thr& th) {
   uint32_t sb, zb;
   float s, z, y;
   scale_zero_recip(mn, mx, sb, zb, s, z, y);
   const bool fast = s >= 0x1p-70f && fmaxf(fabsf(mn), fabsf(mx)) <= 0x1p56f && fabsf(z) <= 128.f;
-  if (th.on) {
+  if constexpr (LUT) {
     // codebook: the same t as below (exact quotient, then + z), compared
     // with the thresholds
 #pragma unroll
@@ -345,7 +345,8 @@ __device__ __forceinline__ uint32_t group_codes(const float (&x)[N], float mn, f
       }
       words[q] = word;
     }
-  } else if (fast) {
+  } else {
+  if (fast) {
 #pragma unroll
     for (int q = 0; q < N / 4; ++q) {
       uint32_t word = 0;
@@ -362,6 +363,7 @@ __device__ __forceinline__ uint32_t group_codes(const float (&x)[N], float mn, f
       for (int e = 0; e < 4; ++e) word = code_into(word, x[4 * q + e] / s, z, e);
       words[q] = word;
     }
+  }
   }
   return sb | (zb << 16);
 }
@@ -453,7 +455,7 @@ __device__ __forceinline__ void rotate_page(const uint4 (&xb)[D / 32], const uin
 // words[w][i] holds, in byte q, the code of channel w*64 + j*16 + 4q + i;
 // true: words[w][q] holds, in byte i, that same code (channel order).  The
 // group scale words are returned in sz.
-template <int D, int NG, bool CHANNEL_ORDER>
+template <int D, int NG, bool CHANNEL_ORDER, bool LUT>
 __device__ __forceinline__ void quant_rotated(const float (&y)[D / 16][4], float tau, uint32_t (&words)[D / 64][4],
                                               uint32_t (&sz)[NG], const Thr& th) {
   constexpr int KW = D / 64, WPG = KW / NG;  // record words per group
@@ -470,13 +472,13 @@ __device__ __forceinline__ void quant_rotated(const float (&y)[D / 16][4], float
       mx = fmaxf(mx, x[u]);
     }
     uint32_t ww[WPG * 4];
-    sz[g] = group_codes<WPG * 16>(x, col4_min(mn), col4_max(mx), ww, th);
+    sz[g] = group_codes<WPG * 16, LUT>(x, col4_min(mn), col4_max(mx), ww, th);
 #pragma unroll
     for (int u = 0; u < WPG * 4; ++u) words[g * WPG + u / 4][u % 4] = ww[u];
   }
 }
 
-template <int D, int NG, bool VROT>
+template <int D, int NG, bool VROT, bool LUT>
 __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const WriteParams& p,
                                           BulkSmem<D, NG, VROT>& sm, int kvh, int page, int wave, int lane,
                                           float tau_k, float tau_v) {
@@ -504,7 +506,7 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const
     rotate_page<D>(pg.ka, sm.rb, lane, y);
     const bool tok_ok = pg.id >= 0 && tok0 + r < p.num_tokens;
     uint32_t words[KW][4], sz[NG];
-    quant_rotated<D, NG, false>(y, tau_k, words, sz, th_k);
+    quant_rotated<D, NG, false, LUT>(y, tau_k, words, sz, th_k);
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
       // byte q of word i holds code m = 4q + i at bits 8q; shifted by 2i
@@ -524,7 +526,7 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const
     rotate_page<D>(pg.va, sm.rbv, lane, y);
     const bool tok_ok = pg.id >= 0 && tok0 + r < p.num_tokens;
     uint32_t words[KW][4], sz[NG];
-    quant_rotated<D, NG, true>(y, tau_v, words, sz, th_v);
+    quant_rotated<D, NG, true, LUT>(y, tau_v, words, sz, th_v);
 #pragma unroll
     for (int g = 0; g < NG; ++g)
       __builtin_amdgcn_raw_buffer_store_b32(
@@ -563,7 +565,7 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const
 #pragma unroll
       for (int u = 0; u < 32; ++u) xx[u] = x[u / 16][u % 16];
       uint32_t ww[8];
-      const uint32_t sz = group_codes<32>(xx, fminf(mn[0], mn[1]), fmaxf(mx[0], mx[1]), ww, th_v);
+      const uint32_t sz = group_codes<32, LUT>(xx, fminf(mn[0], mn[1]), fmaxf(mx[0], mx[1]), ww, th_v);
 #pragma unroll
       for (int u = 0; u < 8; ++u) words[u / 4][u % 4] = ww[u];
       __builtin_amdgcn_raw_buffer_store_b32(tok_ok ? sz : 0u, out,
@@ -574,7 +576,7 @@ __device__ __forceinline__ void bulk_page(const BulkPage<D, NG, VROT>& pg, const
       static_assert(NG == KW, "V groups are 64 channels wide here");
 #pragma unroll
       for (int w = 0; w < KW; ++w) {
-        const uint32_t sz = group_codes<16>(x[w], mn[w], mx[w], words[w], th_v);
+        const uint32_t sz = group_codes<16, LUT>(x[w], mn[w], mx[w], words[w], th_v);
         __builtin_amdgcn_raw_buffer_store_b32(
             tok_ok ? sz : 0u, out, qq == 0 ? sc0 + 4 * ((t / 4) * 8 * NG + 4 * NG + (t % 4) * NG + w) : kDrop, 0, 0);
       }
@@ -635,7 +637,7 @@ __device__ __forceinline__ void split_rotation(const float* __restrict__ r, uint
   }
 }
 
-template <int D, int NG, bool VROT>
+template <int D, int NG, bool VROT, bool LUT>
 __global__ void __launch_bounds__(64 * qp_waves<VROT>()) k_quantize_pack(const WriteParams p) {
   constexpr int W = qp_waves<VROT>(), THREADS = 64 * W;
   __shared__ BulkSmem<D, NG, VROT> sm;
@@ -666,10 +668,10 @@ __global__ void __launch_bounds__(64 * qp_waves<VROT>()) k_quantize_pack(const W
   BulkPage<D, NG, VROT> nxt;
   for (int k = 0; k < my_n; k += 2) {
     bulk_load<D, NG, VROT>(nxt, p, kvh, first + (k + 1) * W, id_of(k + 1), lane);
-    bulk_page<D, NG, VROT>(cur, p, sm, kvh, first + k * W, wave, lane, tau_k, tau_v);
+    bulk_page<D, NG, VROT, LUT>(cur, p, sm, kvh, first + k * W, wave, lane, tau_k, tau_v);
     if (k + 1 >= my_n) break;
     bulk_load<D, NG, VROT>(cur, p, kvh, first + (k + 2) * W, id_of(k + 2), lane);
-    bulk_page<D, NG, VROT>(nxt, p, sm, kvh, first + (k + 1) * W, wave, lane, tau_k, tau_v);
+    bulk_page<D, NG, VROT, LUT>(nxt, p, sm, kvh, first + (k + 1) * W, wave, lane, tau_k, tau_v);
   }
 }
 
@@ -708,7 +710,10 @@ void launch_qp_v(const WriteParams& p, hipStream_t s) {
   q.pages_per_block = std::min(std::max(p.pages_per_block, 1), 64 * W);  // <= 64 pages per wave
   const int gx = (npages + q.pages_per_block - 1) / q.pages_per_block;
   if (gx == 0) return;
-  hipLaunchKernelGGL((k_quantize_pack<D, NG, VROT>), dim3(gx, p.num_kv_heads), dim3(64 * W), 0, s, q);
+  if (p.lut)
+    hipLaunchKernelGGL((k_quantize_pack<D, NG, VROT, true>), dim3(gx, p.num_kv_heads), dim3(64 * W), 0, s, q);
+  else
+    hipLaunchKernelGGL((k_quantize_pack<D, NG, VROT, false>), dim3(gx, p.num_kv_heads), dim3(64 * W), 0, s, q);
 }
 template <int D, int NG>
 void launch_qp(const WriteParams& p, hipStream_t s) {
