@@ -132,8 +132,18 @@ __device__ __forceinline__ int row_sum_i(int x) {
   x += dpp_row_ror_i<2>(x);
   return x + dpp_row_ror_i<1>(x);
 }
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_row_ror<8>(x);
+  x += dpp_row_ror<4>(x);
+  x += dpp_row_ror<2>(x);
+  return x + dpp_row_ror<1>(x);
+}
 // every lane receives the reduction over the wave
 __device__ __forceinline__ float wave_max(float x) { return xor32_max(xor16_max(row_max(x))); }
+// lane 0's reduction order, the same value in every lane
+__device__ __forceinline__ float wave_sum(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(xor32_add(xor16_add(row_sum(x))))));
+}
 __device__ __forceinline__ int wave_sum_i(int x) { return xor32_add(xor16_add(row_sum_i(x))); }
 // over one 32-lane half
 __device__ __forceinline__ int half_sum_i(int x) { return xor16_add(row_sum_i(x)); }
@@ -982,38 +992,42 @@ __global__ void __launch_bounds__(kThreads)
   if (!sm.last) return;
   const size_t p0 = head_base * US * GQA;
   // Folds partials u0 .. u1-1 of head h, channel c into (M, S, A): the log2
-  // max, the sum of weights and the weighted sum of normalized outputs, in
-  // batches of 32 (one memory round trip per batch; indices past the range
-  // re-read its last partial, in bounds and without branches, with weight 0).
-  auto fold = [&](int h, int c, int u0, int u1, float& M, float& S, float& A) {
-    const float* lsrc = p.part_lse + p0 + h;        // partial u at lsrc[u * GQA]
-    const float* osrc = p.part_o + (p0 + h) * D + c;  // partial u at osrc[u * GQA * D]
+  // max, the sum of weights and the weighted sum of normalized outputs.  h
+  // is the same in all 64 lanes of a wave (a wave covers 64 channels of one
+  // head), so the head's lse values are read once per wave, 64 partials at a
+  // time (lane k holds partial ub + k), and max, weights and sum come from
+  // wave reductions; each weight reaches every lane by readlane.  Partial
+  // rows are read through a buffer descriptor with the partial's offset in
+  // the scalar operand.  Lanes past the range carry weight 0 and re-read the
+  // last partial, in bounds.
+  auto fold = [&](int h_lane, int c, int u0, int u1, float& M, float& S, float& A) {
+    const int h = __builtin_amdgcn_readfirstlane(h_lane);
+    const float* lsrc = p.part_lse + p0 + h;  // partial u at lsrc[u * GQA]
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.part_o + (p0 + h) * D), (short)0, (US * GQA - h) * D * 4, kBufferFlags);
     M = -INFINITY;
     S = 0.f;
     A = 0.f;
-    for (int ub = u0; ub < u1; ub += 32) {
-      float e[32], v[32];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const int uu = min(ub + k, u1 - 1);
-        e[k] = lsrc[(size_t)uu * GQA];
-        v[k] = osrc[(size_t)uu * GQA * D];
-      }
-#pragma unroll
-      for (int k = 0; k < 32; ++k)
-        if (ub + k >= u1) e[k] = -INFINITY;
-      float mb = M;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) mb = fmaxf(mb, e[k]);
+    for (int ub = u0; ub < u1; ub += 64) {
+      const int uu = ub + lane;
+      const float e = uu < u1 ? lsrc[(size_t)uu * GQA] : -INFINITY;
+      const float mb = fmaxf(M, wave_max(e));
       if (mb > -INFINITY) {
         const float f = __builtin_amdgcn_exp2f(M - mb);  // 0 while M = -inf
-        S *= f;
+        const float w = __builtin_amdgcn_exp2f(e - mb);  // 0 past the range
+        S = S * f + wave_sum(w);
         A *= f;
+        const int n = min(64, u1 - ub);
+        for (int kb = 0; kb < n; kb += 16) {
+          float o[16];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-          const float w = __builtin_amdgcn_exp2f(e[k] - mb);
-          S += w;
-          A = fmaf(w, v[k], A);
+          for (int k = 0; k < 16; ++k) {
+            const int ui = min(ub + kb + k, u1 - 1);
+            o[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ors, c * 4, ui * GQA * D * 4, 0));
+          }
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            A = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), kb + k)), o[k], A);
         }
         M = mb;
       }
