@@ -1004,12 +1004,13 @@ __global__ void __launch_bounds__(kThreads)
   // Folds partials u0 .. u1-1 of head h, channel c into (M, S, A): the log2
   // max, the sum of weights and the weighted sum of normalized outputs.  h
   // is the same in all 64 lanes of a wave (a wave covers 64 channels of one
-  // head), so the head's lse values are read once per wave, 64 partials at a
-  // time (lane k holds partial ub + k), and max, weights and sum come from
-  // wave reductions; each weight reaches every lane by readlane.  Partial
+  // head).  Per batch of 32 partials the lane's 32 partial values and the
+  // head's 32 lse values (lane k holds partial ub + k) are requested
+  // together, one memory round trip; max, weights and sum then come from
+  // wave reductions and each weight reaches every lane by readlane.  Partial
   // rows are read through a buffer descriptor with the partial's offset in
-  // the scalar operand.  Lanes past the range carry weight 0 and re-read the
-  // last partial, in bounds.
+  // the scalar operand.  Entries past the range carry weight 0 and re-read
+  // the last partial, in bounds.
   auto fold = [&](int h_lane, int c, int u0, int u1, float& M, float& S, float& A) {
     const int h = __builtin_amdgcn_readfirstlane(h_lane);
     const float* lsrc = p.part_lse + p0 + h;  // partial u at lsrc[u * GQA]
@@ -1018,27 +1019,24 @@ __global__ void __launch_bounds__(kThreads)
     M = -INFINITY;
     S = 0.f;
     A = 0.f;
-    for (int ub = u0; ub < u1; ub += 64) {
+    for (int ub = u0; ub < u1; ub += 32) {
+      float o[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const int ui = min(ub + k, u1 - 1);
+        o[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ors, c * 4, ui * GQA * D * 4, 0));
+      }
       const int uu = ub + lane;
-      const float e = uu < u1 ? lsrc[(size_t)uu * GQA] : -INFINITY;
+      const float e = (lane < 32 && uu < u1) ? lsrc[(size_t)uu * GQA] : -INFINITY;
       const float mb = fmaxf(M, wave_max(e));
       if (mb > -INFINITY) {
         const float f = __builtin_amdgcn_exp2f(M - mb);  // 0 while M = -inf
         const float w = __builtin_amdgcn_exp2f(e - mb);  // 0 past the range
         S = S * f + wave_sum(w);
         A *= f;
-        const int n = min(64, u1 - ub);
-        for (int kb = 0; kb < n; kb += 16) {
-          float o[16];
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const int ui = min(ub + kb + k, u1 - 1);
-            o[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ors, c * 4, ui * GQA * D * 4, 0));
-          }
-#pragma unroll
-          for (int k = 0; k < 16; ++k)
-            A = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), kb + k)), o[k], A);
-        }
+        for (int k = 0; k < 32; ++k)
+          A = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k)), o[k], A);
         M = mb;
       }
     }
