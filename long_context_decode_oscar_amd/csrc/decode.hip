@@ -1428,9 +1428,12 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (i >= nt_w) break;
+        // raised priority over the fetch and the softmax, as in k_decode
+        __builtin_amdgcn_s_setprio(2);
         fetch(ring[(r + R - 1) % R], i + R - 1);
         v4i bw[NG];
         pt_softmax<D, NG, LUT>(ring[r], S, st, kappa, sig, first + (wave + i * kWaves) * 2, my_hist, lane, bw);
+        __builtin_amdgcn_s_setprio(0);
         scores(ring[(r + 1) % R], S);
         pv_block_pair<D, NG, 0, LUT>(st, ring[r].vw[0][0], ring[r].vw[1][0], bw, exp_lo, exp_hi, lut_v);
         if constexpr (KW > 1)
