@@ -177,7 +177,8 @@ oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const vo
  * oscar_append_demote).
  * q: bf16 [batch][Hq][D] (model basis); seq_lens: int32 [batch] device, L_b
  * counting the current token, at most max_seq_len (longer lengths are
- * clamped to max_seq_len and to what the page tables can address); out:
+ * clamped to max_seq_len and to what the page tables can address; lengths
+ * of 0 or less select no token and give zero output rows); out:
  * bf16 [batch][Hq][D].
  * workspace: oscar_decode_workspace_bytes(pool, batch, max_seq_len, 0) bytes,
  * 256-byte aligned, zero-filled before first use. */

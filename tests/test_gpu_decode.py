@@ -57,6 +57,28 @@ def test_decode_matches_oracle(gpu_lib, name):
     check_decode(out, ref, what=name)
 
 
+def test_decode_empty_sequences_give_zero_rows(gpu_lib):
+    """Lengths of 0 (and negative ones, clamped to 0) select no token: those
+    rows of the output are exactly zero, and the other sequences of the batch
+    are unaffected."""
+    wl = make_workload(QWEN, num_q_heads=8, num_kv_heads=2, batch=4, seq_lens=(700, 2000, 333, 1500), seed=12)
+    inp = draw_inputs(wl)
+    seqs = make_seqs(wl, inp)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    pool = gpu_lib.OscarPool(pool_config(wl))
+    dev = upload(pools)
+    lens = torch.tensor([0, 2000, -5, 1500], dtype=torch.int32, device="cuda")
+    out = torch.full(inp.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = pool.alloc_workspace(wl.batch, 2000)
+    log("decode launch: lengths (0, 2000, -5, 1500)")
+    gpu_lib.oscar_decode_attention(pool, inp.q.cuda(), lens, 2000, dev["bf16_pt"], dev["int2_pt"], dev["bf16_pool"],
+                                   dev["int2_pool"], to_dev(inp.calib.r_k), out, ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[0].float()) == 0 and torch.count_nonzero(out[2].float()) == 0
+    ref, _ = oracle.decode_attention([seqs[1], seqs[3]], inp.q[[1, 3]].float().numpy(), inp.calib.r_k)
+    check_decode(out[[1, 3]], ref, what="non-empty sequences of a batch with empty ones")
+
+
 @pytest.mark.parametrize("name", ["d64-gqa2-boundary-lengths", "d128-gqa4-ragged", "d128-g64-gqa8"])
 def test_decode_values_not_absorbed(gpu_lib, name):
     """v_absorbed = 0: the BF16 segments hold V, the history V R_V; decode

@@ -125,6 +125,53 @@ def test_quantize_pack_full_size_sampled(gpu_lib):
                     f"bulk V head {h} (64 sampled pages)")
 
 
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).bfloat16().float().numpy()
+
+
+def _degenerate_rows(n, d, gs, rng):
+    """Token rows whose groups hit every special case of the quantizer's
+    scale/zero rule (W4-W6): constant groups (d = 0, so s = 1, including a
+    zero point far from the code range), spreads so small that the scale is
+    below 2^-70, values beyond 2^56, zero points beyond 128 in magnitude, and
+    a group with one outlier; the rest are plain Gaussian groups."""
+    patterns = [
+        lambda: np.zeros(gs),
+        lambda: np.full(gs, 1.5),
+        lambda: np.full(gs, -200.0),
+        lambda: rng.uniform(1e-30, 3e-30, gs) * rng.choice([-1.0, 1.0]),
+        lambda: rng.uniform(-1e20, 1e20, gs),
+        lambda: 1000.0 + 8.0 * rng.integers(0, 3, gs),
+        lambda: np.r_[np.full(gs - 1, 7.0), 7.0 + 1.0 / 32],
+        lambda: rng.standard_normal(gs),
+    ]
+    x = np.empty((n, d), np.float32)
+    for i in range(n):
+        for g in range(d // gs):
+            x[i, g * gs:(g + 1) * gs] = patterns[(i + 3 * g) % len(patterns)]()
+    return _bf16(x)
+
+
+@pytest.mark.parametrize("name", list(WL))
+def test_quantize_pack_degenerate_groups(gpu_lib, name):
+    """Pre-rotated input (R_K = I, V absorbed) whose groups take the bulk
+    kernel off its reciprocal fast path: codes, scales and zeros must still
+    be bit-exact against the oracle.  Clipping is disabled (tau = 1e30)."""
+    wl = WL[name]
+    rng = np.random.default_rng(wl.seed + 50)
+    t = 45  # two full pages and a ragged third
+    k = np.stack([_degenerate_rows(t, wl.head_dim, wl.group_size, rng) for _ in range(wl.num_kv_heads)], axis=1)
+    v = np.stack([_degenerate_rows(t, wl.head_dim, wl.group_size, rng) for _ in range(wl.num_kv_heads)], axis=1)
+    tau = np.full(wl.num_kv_heads, 1e30, np.float32)
+    r_k = _identity(wl.num_kv_heads, wl.head_dim)
+    kc, ks, kz, vc, vs, vz = _bulk(gpu_lib, wl, k, v, r_k, tau, tau, seed=wl.seed + 51)
+    for h in range(wl.num_kv_heads):
+        check_write((kc[:, h], ks[:, h], kz[:, h]), k[:, h], None, tau[h], wl.group_size,
+                    f"{name} K head {h} degenerate groups")
+        check_write((vc[:, h], vs[:, h], vz[:, h]), v[:, h], None, tau[h], wl.group_size,
+                    f"{name} V head {h} degenerate groups")
+
+
 @pytest.mark.parametrize("rotated", [False, True, "values too"])
 @pytest.mark.parametrize("name", ["d128-g128", "d64-g64", "d128-g64"])
 def test_append_demote_steps_then_decode(gpu_lib, name, rotated):
@@ -191,3 +238,45 @@ def test_append_demote_steps_then_decode(gpu_lib, name, rotated):
     torch.cuda.synchronize()
     ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), r_k, r_v)
     check_decode(out, ref, what=f"{name} decode after demotion rotated={rotated}")
+
+
+@pytest.mark.parametrize("name", list(WL))
+def test_append_demote_degenerate_groups(gpu_lib, name):
+    """Decode-time demotion of tokens whose groups take every special case of
+    the scale/zero rule (see _degenerate_rows): with R_K = I, V absorbed and
+    no clipping, the codes, scales and zeros the GPU writes for the demoted
+    tokens are bit-exact against the oracle."""
+    wl = make_workload(WL[name], batch=1, seq_lens=(370,), seed=WL[name].seed + 200)
+    rng = np.random.default_rng(wl.seed)
+    steps, l0 = 40, 330  # the appends demote positions 74 .. 113
+    n = l0 + steps
+    k = np.stack([_degenerate_rows(n, wl.head_dim, wl.group_size, rng) for _ in range(wl.num_kv_heads)], axis=1)
+    v = np.stack([_degenerate_rows(n, wl.head_dim, wl.group_size, rng) for _ in range(wl.num_kv_heads)], axis=1)
+    tau = np.full(wl.num_kv_heads, 1e30, np.float32)
+    r_k = _identity(wl.num_kv_heads, wl.head_dim)
+    seq = oracle.SeqPool(wl.num_kv_heads, wl.head_dim, wl.group_size, wl.sink, wl.recent).prefill(
+        k[:l0], v[:l0], r_k, tau, tau)
+    cap = [(n - 320 + 15) // 16 + 1]
+    pools = pool_io.build_pools([seq], wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=6,
+                                int2_capacity=cap, extra_bf16_pages={0: list(range((n + 15) // 16))}, garbage=False)
+    dev = upload(pools)
+    pool = gpu_lib.OscarPool(pool_config(wl))
+    rk, tk = to_dev(r_k), to_dev(tau)
+    for st in range(steps):
+        lens = torch.tensor([l0 + st], dtype=torch.int32, device="cuda")
+        kn = to_dev(k[l0 + st][None], torch.bfloat16)
+        vn = to_dev(v[l0 + st][None], torch.bfloat16)
+        gpu_lib.oscar_append_demote(pool, kn, vn, lens, dev["bf16_pt"], dev["int2_pt"], dev["bf16_pool"],
+                                    dev["int2_pool"], rk, tk, tk)
+        seq.append_demote(k[l0 + st], v[l0 + st], r_k, tau, tau)
+    torch.cuda.synchronize()
+    kc, ks, kz, vc, vs, vz = pool_io.read_history(dev["int2_pool"].cpu().numpy(), pools["int2_pt"][0], seq.n_hist,
+                                                  wl.num_kv_heads, wl.head_dim, wl.n_groups)
+    new = np.arange(l0 - 320, seq.n_hist)  # history slots written by the GPU
+    assert len(new) == steps
+    for h in range(wl.num_kv_heads):
+        pos = wl.sink + new
+        check_write((kc[new, h], ks[new, h], kz[new, h]), k[pos, h], None, tau[h], wl.group_size,
+                    f"{name} demoted degenerate K head {h}")
+        check_write((vc[new, h], vs[new, h], vz[new, h]), v[pos, h], None, tau[h], wl.group_size,
+                    f"{name} demoted degenerate V head {h}")
