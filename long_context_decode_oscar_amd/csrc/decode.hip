@@ -881,11 +881,12 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           if (i >= nt_w) break;
-          // The fetch and the softmax run at a raised wave priority, the
-          // matrix-core phases (scores, P.V) at the base one: of the two
-          // waves on a SIMD, the one in its short VALU chain issues first
-          // while the other one's MFMAs keep the matrix core busy (measured
-          // 0.3 us faster per 100K-token step than a flat priority).
+          // Wave priority by phase: the fetch and the softmax (a short VALU
+          // chain) at 2, the P.V operands and MFMAs at 1, the score MFMAs
+          // at 0.  Of the two waves on a SIMD, the one in the VALU-heavy
+          // phase issues first while the other one's MFMAs keep the matrix
+          // core busy (measured 0.5 us faster per 100K-token step than a
+          // flat priority).
           __builtin_amdgcn_s_setprio(2);
           fetch(ring[(r + R - 1) % R], i + R - 1);
           // softmax of tile i first: the wait for tile i+1's data comes
@@ -893,6 +894,7 @@ __global__ void __launch_bounds__(kThreads)
           const I2Weights<D, NG, GQA> W = i2_softmax<D, NG, GQA, LUT>(ring[r], S, st, kappa, sig, my_slot);
           __builtin_amdgcn_s_setprio(0);
           S = i2_scores<D, NG, GQA, LUT>(ring[(r + 1) % R], bqr, lut_k);
+          __builtin_amdgcn_s_setprio(1);
           i2_pv<D, NG, GQA, LUT>(ring[r], W, st, exp_lo, exp_hi, lut_v);
           // slots r and r+1 hold arrived data (the loads of r+2 .. r+R-1 may
           // still be in flight and are left alone)
@@ -902,6 +904,7 @@ __global__ void __launch_bounds__(kThreads)
         }
         if (i >= nt_w) break;
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     wave_finish<D, NG, GQA, true>(st, sm, wave, lane);
   } else {
@@ -1428,13 +1431,14 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (i >= nt_w) break;
-        // raised priority over the fetch and the softmax, as in k_decode
+        // wave priority by phase, as in k_decode
         __builtin_amdgcn_s_setprio(2);
         fetch(ring[(r + R - 1) % R], i + R - 1);
         v4i bw[NG];
         pt_softmax<D, NG, LUT>(ring[r], S, st, kappa, sig, first + (wave + i * kWaves) * 2, my_hist, lane, bw);
         __builtin_amdgcn_s_setprio(0);
         scores(ring[(r + 1) % R], S);
+        __builtin_amdgcn_s_setprio(1);
         pv_block_pair<D, NG, 0, LUT>(st, ring[r].vw[0][0], ring[r].vw[1][0], bw, exp_lo, exp_hi, lut_v);
         if constexpr (KW > 1)
           pv_block_pair<D, NG, 1, LUT>(st, ring[r].vw[0][1], ring[r].vw[1][1], bw, exp_lo, exp_hi, lut_v);
@@ -1444,6 +1448,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
       }
       if (i >= nt_w) break;
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   // ---- wave epilogue: one (o, lse) per column (no two columns share a head)
   st.l = col_sum(st.l);
