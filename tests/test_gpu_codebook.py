@@ -78,6 +78,30 @@ def test_quantize_pack_codebook(gpu_lib, name, lv, rotated):
                     wl.group_size, f"{name} {lv} V head {h}", levels=levels[1])
 
 
+@pytest.mark.parametrize("lv", list(LEVELS))
+@pytest.mark.parametrize("name", list(WL))
+def test_quantize_pack_codebook_degenerate_groups(gpu_lib, name, lv):
+    """The codebook encoding on groups that leave the reciprocal fast path
+    (constant groups, scales below 2^-70, values near 1e20, zero points of
+    several hundred): pre-rotated input, no clipping, bit-exact codes,
+    scales and zeros."""
+    from test_gpu_write import _degenerate_rows
+    wl = WL[name]
+    levels = LEVELS[lv]
+    rng = np.random.default_rng(wl.seed + 60)
+    t = 45
+    k = np.stack([_degenerate_rows(t, wl.head_dim, wl.group_size, rng) for _ in range(wl.num_kv_heads)], axis=1)
+    v = np.stack([_degenerate_rows(t, wl.head_dim, wl.group_size, rng) for _ in range(wl.num_kv_heads)], axis=1)
+    tau = np.full(wl.num_kv_heads, 1e30, np.float32)
+    kc, ks, kz, vc, vs, vz = _bulk(gpu_lib, wl, k, v, _identity(wl.num_kv_heads, wl.head_dim), tau, tau, levels,
+                                   seed=wl.seed + 61)
+    for h in range(wl.num_kv_heads):
+        check_write((kc[:, h], ks[:, h], kz[:, h]), k[:, h], None, tau[h], wl.group_size,
+                    f"{name} {lv} K head {h} degenerate groups", levels=levels[0])
+        check_write((vc[:, h], vs[:, h], vz[:, h]), v[:, h], None, tau[h], wl.group_size,
+                    f"{name} {lv} V head {h} degenerate groups", levels=levels[1])
+
+
 @pytest.mark.parametrize("name", ["d128-g128", "d64-g64"])
 @pytest.mark.parametrize("rotated", [False, True])
 def test_append_demote_codebook(gpu_lib, name, rotated):
