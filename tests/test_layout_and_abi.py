@@ -141,6 +141,23 @@ def test_workspace_bytes_grows_with_batch_and_length():
     assert p.workspace_bytes(1, 100_000, bf16_only=True) > 0
 
 
+def test_decode_plan_chunk_limit():
+    """The split-K planner gives one (sequence, KV head) at most 1024 INT2
+    chunks of at most 512 pages: a history of exactly 1024 x 512 pages fits,
+    one page more is rejected as unsupported before any launch."""
+    import ctypes
+    import long_context_decode_oscar_amd as oscar
+    lib = oscar.load()
+    p = oscar.OscarPool(_cfg())
+    n = ctypes.c_size_t()
+    at_limit = 64 + 256 + 1024 * 512 * 16  # sink + recent + history tokens
+    assert lib.oscar_decode_workspace_bytes(p.handle, 1, at_limit, 0, ctypes.byref(n)) == oscar.OSCAR_OK
+    assert n.value > 0
+    assert lib.oscar_decode_workspace_bytes(p.handle, 1, at_limit + 16, 0, ctypes.byref(n)) == \
+        oscar.OSCAR_ERR_UNSUPPORTED
+    assert b"split-K chunks" in lib.oscar_last_error()
+
+
 def test_decode_validation_fails_before_launch():
     import long_context_decode_oscar_amd as oscar
     lib = oscar.load()
