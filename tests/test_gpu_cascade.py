@@ -154,3 +154,31 @@ def test_cascade_repeated_calls_deterministic(gpu_lib):
                                                groups)
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), out1.view(torch.int16))
+
+
+def test_cascade_group_with_empty_member(gpu_lib):
+    """A prefix group whose member has length 0 this step: its rows are
+    exactly zero, and the other members still match the oracle."""
+    wl, groups = CASES["d128-gqa4"]
+    inp = _prefix_inputs(wl, groups)
+    seqs = make_seqs(wl, inp)
+    pools = _share_tables(pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent,
+                                              seed=wl.seed), seqs, groups)
+    pool = gpu_lib.OscarPool(pool_config(wl))
+    dev = upload(pools)
+    lens_h = [s.L for s in seqs]
+    empty = groups[0][0] + 1  # second member of the group
+    lens_h[empty] = 0
+    lens = torch.tensor(lens_h, dtype=torch.int32, device="cuda")
+    max_len = max(lens_h)
+    out = torch.full(inp.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    nbytes = gpu_lib.cascade_workspace_bytes(pool, len(seqs), max_len, dev["int2_pt"].shape[1], groups)
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    log(f"cascade decode with an empty member {empty}: lengths {lens_h}")
+    gpu_lib.oscar_decode_attention_cascade(pool, inp.q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"],
+                                           dev["bf16_pool"], dev["int2_pool"], to_dev(inp.calib.r_k), out, ws, groups)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[empty].float()) == 0
+    keep = [b for b in range(len(seqs)) if b != empty]
+    ref, _ = oracle.decode_attention([seqs[b] for b in keep], inp.q[keep].float().numpy(), inp.calib.r_k)
+    check_decode(out[keep], ref, what="cascade, group with an empty member")
