@@ -37,7 +37,7 @@ from .numerics import round_bf16, f32  # noqa: F401
 from .quant import (  # noqa: F401
     quantize_token, quantize_tokens, dequantize, pack_codes, unpack_codes,
 )
-from .pool import LogicalPool, SeqPool  # noqa: F401
+from .pool import SeqPool  # noqa: F401
 from .attention import decode_attention, bf16_decode_attention, attention_one_head  # noqa: F401
 from .merge import merge_partials  # noqa: F401
 from . import calibration  # noqa: F401

@@ -109,16 +109,3 @@ class SeqPool:
             return d
         return None
 
-
-class LogicalPool:
-    """A batch of sequences sharing one configuration."""
-
-    def __init__(self, num_kv_heads, head_dim, group_size, sink=64, recent=256,
-                 v_absorbed=True):
-        self.args = (num_kv_heads, head_dim, group_size, sink, recent, v_absorbed)
-        self.seqs = []
-
-    def add_sequence(self, k, v, r_k, tau_k, tau_v, r_v=None):
-        s = SeqPool(*self.args).prefill(k, v, r_k, tau_k, tau_v, r_v)
-        self.seqs.append(s)
-        return s

@@ -316,3 +316,79 @@ def test_error_chain_rotations_beat_no_rotation(calib):
     for name in ("hadamard", "oscar"):
         assert res[name]["logit_mse"] < 0.5 * res["none"]["logit_mse"], res
         assert res[name]["kl"] < 0.5 * res["none"]["kl"], res
+
+
+def test_summarize_hand_computed():
+    """Hand-worked summary of two query heads' rows at N = 3 (ModelScope/CSDN
+    page, motivation section, Figure 1: score KL and output error).  Causal
+    pairs per head are 1 + 2 + 3 = 6, so 12 in all; the KL is averaged over
+    the 6 query rows; the output error is one ratio of sums.  The literals
+    below were worked out by hand: 12 / 12 pairs, 1.8 / 6 rows, 8 / 80."""
+    kl = [[0.0, 0.3, 0.6], [0.0, 0.9, 0.0]]
+    lse2 = [[0.5, 1.0, 4.5], [0.0, 3.0, 3.0]]
+    ose = [[1.0, 2.0, 3.0], [0.0, 0.0, 2.0]]
+    osq = [[10.0, 10.0, 10.0], [10.0, 10.0, 30.0]]
+    s = cal.summarize(np.array([kl, lse2, ose, osq]))
+    # n^2 normalization would give 2/3, a per-row mean 2.0
+    assert s["logit_mse"] == pytest.approx(1.0, rel=1e-15)
+    # a summed KL would give 1.8
+    assert s["kl"] == pytest.approx(0.3, rel=1e-15)
+    # the mean of per-row ratios would give 1/9
+    assert s["out_rel_mse"] == pytest.approx(0.1, rel=1e-15)
+    # the leading axes are only a stack: one head alone has 6 pairs, 3 rows
+    s0 = cal.summarize(np.array([kl[0], lse2[0], ose[0], osq[0]]))
+    assert s0["logit_mse"] == pytest.approx(1.0, rel=1e-15)
+    assert s0["kl"] == pytest.approx(0.3, rel=1e-15)
+    assert s0["out_rel_mse"] == pytest.approx(0.2, rel=1e-15)
+
+
+def _grid_keys(rng, n, d, g):
+    """Keys already on a 4-level grid in every group: lossless without
+    rotation or clipping (s = 0.5, z = 1)."""
+    lev = rng.integers(0, 4, size=(n, d)).astype(np.float64)
+    for j in range(0, d, g):
+        lev[:, j], lev[:, j + 1] = 0, 3
+    return 0.5 * (lev - 1)
+
+
+def test_error_chain_routes_key_and_value_parameters():
+    """error_chain must quantize the keys with (r_k, tau_k) and the values
+    with (r_v, tau_v).  Keys on the grid with no rotation and no clip are
+    lossless, so the logit error and the KL are exactly zero while the
+    values, rotated and clipped, carry an output error; swapping the
+    rotations or the thresholds would make the keys lossy.  The output error
+    is checked against pure-Python loops fed the value round trip (E1)."""
+    rng = np.random.default_rng(11)
+    n, d, g = 9, 8, 4
+    k = _grid_keys(rng, n, d, g)
+    v = rng.standard_normal((n, d))
+    r_v, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    r_v = r_v.astype(np.float32)
+    tau_v = np.float32(0.6)  # clips the rotated values, and would clip the keys (|k| up to 1)
+    q = rng.standard_normal((2, n, d))
+    rows, summ = cal.error_chain(q, k, v, None, r_v, np.inf, tau_v, g, sm=0.5)
+    assert summ["logit_mse"] == 0.0 and summ["kl"] == 0.0
+    assert summ["out_rel_mse"] > 1e-3
+    vh = cal.quantize_roundtrip(v, r_v, tau_v, g)
+    for h in range(2):
+        bk, bl, bo = _error_rows_loops(q[h].tolist(), k.tolist(), v.tolist(), k.tolist(), vh.tolist(), 0.5)
+        assert np.allclose(rows[2, h], bo, rtol=1e-12, atol=1e-15)
+        assert np.all(rows[0, h] == 0) and np.all(rows[1, h] == 0)
+    # the swapped routes are lossy on the keys
+    for rk, tk in ((r_v, np.inf), (None, tau_v)):
+        _, bad = cal.error_chain(q, k, v, rk, None, tk, np.inf, g, sm=0.5)
+        assert bad["logit_mse"] > 1e-4
+
+    # reversed roles: lossless values, rotated and clipped keys
+    vg = _grid_keys(rng, n, d, g)
+    r_k, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    r_k = r_k.astype(np.float32)
+    tau_k = np.float32(0.7)
+    rows, summ = cal.error_chain(q, k, vg, r_k, None, tau_k, np.inf, g, sm=0.5)
+    kh = cal.quantize_roundtrip(k, r_k, tau_k, g)
+    for h in range(2):
+        bk, bl, bo = _error_rows_loops(q[h].tolist(), k.tolist(), vg.tolist(), kh.tolist(), vg.tolist(), 0.5)
+        assert np.allclose(rows[0, h], bk, rtol=1e-10, atol=1e-14)
+        assert np.allclose(rows[1, h], bl, rtol=1e-12, atol=1e-14)
+        assert np.allclose(rows[2, h], bo, rtol=1e-10, atol=1e-14)
+    assert summ["logit_mse"] > 1e-4
