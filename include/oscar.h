@@ -181,7 +181,17 @@ oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const vo
  * of 0 or less select no token and give zero output rows); out:
  * bf16 [batch][Hq][D].
  * workspace: oscar_decode_workspace_bytes(pool, batch, max_seq_len, 0) bytes,
- * 256-byte aligned, zero-filled before first use. */
+ * 256-byte aligned, zero-filled before first use.
+ * Value range: the history's P.V runs on fp16 matrix cores with weights
+ * p * s_V * 2^-E, where E follows the largest value group scale s_V seen by
+ * the softmax state (clamped to [-96, 96]); every s_V in [2^-96, 2^96] keeps
+ * the weights inside fp16's normal range, whatever tau_V was (+inf included).
+ * Larger scales are outside the supported range (the weights overflow).
+ * Query precision: q' = q R_K enters the int8 matrix cores as
+ * sq (a + b/256) (~16 significant bits relative to max|q'|), and as
+ * sq (a + b/256 + c/65536) for a workgroup whose heads include a q' with one
+ * channel above 8x its rms (group_size = head_dim; with two scale groups per
+ * head the two-term split is kept). */
 oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
                                     const int32_t* seq_lens, const int32_t* bf16_page_table,
                                     int32_t bf16_pt_stride, int32_t bf16_num_pages,

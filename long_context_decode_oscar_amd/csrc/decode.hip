@@ -80,9 +80,12 @@ struct Smem {
     float part[kWaves][GQA][D + 1];  // per-wave partials, [D] = lse (log2)
     float qpart[kWaves][GQA][D];     // prologue: per-wave partial sums of q R_K
   } u;
-  v4i bq[SLOTS][2][D / 64][64];      // int8 q' B operands per lane (shared by the waves)
+  v4i bq[SLOTS][3][D / 64][64];      // int8 q' B operands per lane (terms a, b, c; shared by the waves)
   float kap[GQA];                    // logit factor sm * log2(e) * sq / 256 per query head
+  float kap3[GQA];                   // the same with the third term: sm * log2(e) * sq / 65536
   int sig[GQA * 2];                  // sum(256 a + b) per head and group
+  int sig3[GQA * 2];                 // sum(65536 a + 256 b + c) per head and group
+  int dom[GQA];                      // 1: the head's q' has a dominant channel (three terms)
   int last;
 };
 
@@ -177,16 +180,31 @@ __device__ __forceinline__ v8bf as_v8bf(uint4 x) {
   return __builtin_bit_cast(v8bf, x);
 }
 // online-softmax state of one wave: accumulators O^T[channel][column]
+//
+// The weights are p = 2^(logit - ref) with ref = m + E.  m is the lazy
+// running max of the logits (log2 units).  E (INT2 units only; 0 for BF16)
+// is an integer exponent that follows the largest value scale s_V seen, so
+// that the fp16 P.V weights w = p s_V stay inside fp16's normal range for
+// any scale in [2^kEmin, 2^kEmax]: p <= 2^kLazy and s_V <= 2^(E + kSlack)
+// give w <= 2^(kLazy + kSlack).  Numerator and denominator carry the same
+// factor 2^-E, so the normalized output needs no correction and the
+// partial's log2 normalizer is ref + log2(l).
+constexpr float kSlack = 4.f;   // log2 slack of a value scale above 2^E before E is raised
+constexpr float kEmin = -96.f, kEmax = 96.f;
 template <int D, int NG>
 struct Acc {
   v4f o[D / 16];
   float m, l;
+  float E, ref, slim;  // value-scale exponent, exp2 reference m + E, 2^(E + kSlack)
   float Z[NG];  // INT2 only: sum over tokens of weight * (operand bias + zero)
-  __device__ void init() {
+  __device__ void init(bool int2) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
     m = kNegBig;
     l = 0.f;
+    E = int2 ? kEmin : 0.f;
+    ref = m + E;
+    slim = int2 ? __builtin_amdgcn_ldexpf(1.f, (int)(kEmin + kSlack)) : INFINITY;
 #pragma unroll
     for (int g = 0; g < NG; ++g) Z[g] = 0.f;
   }
@@ -197,19 +215,34 @@ struct Acc {
 #pragma unroll
     for (int g = 0; g < NG; ++g) Z[g] *= f;
   }
-  // lazy running max: raise m only when some logit exceeds it by kLazy
-  __device__ __forceinline__ void update_max(const float lg[4], const float lg2[4]) {
+  // new reference from the (already reduced) logit max mn and value-scale
+  // max sm of the columns that share this state
+  __device__ __forceinline__ void raise(float mn, float sm) {
+    const float En = sm > slim ? fminf((float)(__builtin_amdgcn_frexp_expf(sm) - 1), kEmax) : E;
+    const float rn = mn + En;
+    scale(__builtin_amdgcn_exp2f(ref - rn));
+    m = mn;
+    E = En;
+    ref = rn;
+    slim = __builtin_amdgcn_ldexpf(1.f, (int)(En + kSlack));
+  }
+  // INT2 prefix tiles (two pages, every column its own state): lazy raise
+  // when a logit exceeds m by kLazy or a value scale exceeds slim
+  __device__ __forceinline__ void update_ref(const float lg[4], const float lg2[4], float smax) {
     const float lmax = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
                              fmaxf(fmaxf(lg2[0], lg2[1]), fmaxf(lg2[2], lg2[3])));
-    if (__any(lmax > m + kLazy)) {
-      const float mn = fmaxf(m, col_max(lmax));
-      scale(__builtin_amdgcn_exp2f(m - mn));
-      m = mn;
-    }
+    if (__any(lmax > m + kLazy || smax > slim)) raise(fmaxf(m, col_max(lmax)), col_max(smax));
   }
-  // the columns n, n + SHARE, n + 2 SHARE, ... of a 16-lane row (the pages
-  // of one query head) keep one running max, so that their states merge
-  // without rescaling
+  // INT2 tiles of k_decode: the columns n, n + SHARE, n + 2 SHARE, ... of a
+  // 16-lane row (the pages of one query head) keep one state reference, so
+  // that their states merge without rescaling
+  template <int SHARE>
+  __device__ __forceinline__ void update_ref(const float lg[4], float smax) {
+    const float lmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    if (__any(lmax > m + kLazy || smax > slim))
+      raise(slot_max<SHARE>(fmaxf(m, col_max(lmax))), slot_max<SHARE>(col_max(smax)));
+  }
+  // BF16 tiles (E = 0): the logit max alone
   template <int SHARE>
   __device__ __forceinline__ void update_max(const float lg[4]) {
     const float lmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
@@ -217,9 +250,55 @@ struct Acc {
       const float mn = slot_max<SHARE>(fmaxf(m, col_max(lmax)));
       scale(__builtin_amdgcn_exp2f(m - mn));
       m = mn;
+      ref = mn;
     }
   }
 };
+
+// ------------------------------------------------------ q' int8 split ----
+// q' of one query head, lane holding channels CPL*lane + e, split as
+// q' ~ sq (a + b/256 + c/65536) with int8 a, b, c (sq = max|q'| / 127), so
+// that its dot with the int8 key codes is exact on the matrix cores.  Two
+// terms carry ~16 significant bits relative to max|q'|, which leaves the
+// other channels enough bits unless one channel dominates; `dom` (the same
+// in every lane) is set when max|q'| exceeds kDominant times the rms over the
+// channels, and the kernels then add the third term.
+constexpr float kDominant = 8.f;
+
+// An LDS read that the compiler re-issues where it stands (a volatile access
+// through an LDS pointer): loop-invariant operands read this way are not
+// hoisted into registers for the whole loop.
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+__device__ __forceinline__ v4i lds_read_fresh(const v4i* p) {
+  return *(volatile const lds_v4i*)(const lds_v4i*)p;
+}
+template <int CPL>
+__device__ __forceinline__ float split_query(const float (&x)[CPL], int (&a)[CPL], int (&b)[CPL], int (&c)[CPL],
+                                             bool& dom) {
+  float amax = 0.f, ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    amax = fmaxf(amax, fabsf(x[e]));
+    ss = fmaf(x[e], x[e], ss);
+  }
+  amax = wave_max(amax);
+  ss = wave_sum(ss);
+  dom = amax * amax > kDominant * kDominant * ss * (1.f / (64 * CPL));
+  const float sq = amax > 0.f ? amax / 127.f : 1.f;
+  const float inv_sq = 1.f / sq;
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    const float y = x[e] * inv_sq;
+    const float af = fminf(fmaxf(rintf(y), -127.f), 127.f);
+    const float r1 = (y - af) * 256.f;  // exact: af is the integer nearest y
+    const float bf = fminf(fmaxf(rintf(r1), -127.f), 127.f);
+    const float cf = fminf(fmaxf(rintf((r1 - bf) * 256.f), -127.f), 127.f);
+    a[e] = (int)af;
+    b[e] = (int)bf;
+    c[e] = (int)cf;
+  }
+  return sq;
+}
 
 // ------------------------------------------------------------- INT2 tile --
 template <int D, int NG, int GQA>
@@ -337,30 +416,15 @@ __device__ __forceinline__ v4i k_operand(uint32_t x, uint32_t lut_k) {
 
 template <int NG>
 struct I2Scores {
-  v4i a[NG], b[NG];  // integer dots with the two int8 terms of q', per group
+  v4i a[NG], b[NG], c[NG];  // integer dots with the int8 terms of q', per group (c: three-term mode)
 };
 
-// Scores of one tile on the int8 matrix cores (block-diagonal B operands:
-// slot s's page meets only the columns of slot s).  The operands are
-// loop-invariant and held in VGPRs.
-template <int D, int NG, int GQA, bool LUT>
-__device__ __forceinline__ I2Scores<NG> i2_scores(const I2Tile<D, NG, GQA>& t,
-                                                  const v4i (&bq)[DC<D, NG, GQA>::SLOTS][2][D / 64], uint32_t lut_k) {
-  using C = DC<D, NG, GQA>;
-  I2Scores<NG> r;
-#pragma unroll
-  for (int g = 0; g < NG; ++g) r.a[g] = r.b[g] = v4i{0, 0, 0, 0};
-#pragma unroll
-  for (int s = 0; s < C::SLOTS; ++s) {
-#pragma unroll
-    for (int w = 0; w < C::KW; ++w) {
-      const v4i a = k_operand<LUT>(t.kw[s][w], lut_k);
-      const int g = (NG == 1) ? 0 : w;
-      r.a[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq[s][0][w], r.a[g], 0, 0, 0);
-      r.b[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq[s][1][w], r.b[g], 0, 0, 0);
-    }
-  }
-  return r;
+// the integer dot of a score row as a float: 256 S_a + S_b (exact), or with
+// the third term 65536 S_a + 256 S_b + S_c (rounded once to fp32)
+template <bool T3>
+__device__ __forceinline__ float score_int(int sa, int sb, int sc) {
+  if constexpr (T3) return fmaf((float)sa, 65536.f, fmaf((float)sb, 256.f, (float)sc));
+  return (float)(sa * 256 + sb);
 }
 
 // P.V operands from packed value codes, without per-code shifts.  A value
@@ -426,7 +490,7 @@ template <int D, int NG, int GQA>
 struct I2Weights {
   v4i bw[DC<D, NG, GQA>::SLOTS / 2][NG];  // block-diagonal B operands of the P.V MFMAs
 };
-template <int D, int NG, int GQA, bool LUT>
+template <int D, int NG, int GQA, bool LUT, bool T3>
 __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, GQA>& t, const I2Scores<NG>& S,
                                                            Acc<D, NG>& st, float kappa, const float (&sig)[NG],
                                                            int my_slot) {
@@ -439,16 +503,26 @@ __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, 
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       // with a codebook the integer dot holds 32 L[code]
-      const float sint = (float)(S.a[g][i] * 256 + S.b[g][i]) * (LUT ? 1.f / 32.f : 1.f);
+      const float sint = score_int<T3>(S.a[g][i], S.b[g][i], S.c[g][i]) * (LUT ? 1.f / 32.f : 1.f);
       const uint32_t sz = t.sc[i * NG + g];
       acc += bf16_lo(sz) * (sint - bf16_hi(sz) * sig[g]);
     }
     lg[i] = fmaf(acc, kappa, i < t.nvalid ? 0.f : -INFINITY);
   }
-  st.template update_max<GQA>(lg);
+  // value scales of the lane's tokens (zero for tokens outside the history)
+  float sv[NG][4];
+  float smax = 0.f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[g][i] = bf16_lo(t.sc[4 * NG + i * NG + g]);
+      smax = fmaxf(smax, sv[g][i]);
+    }
+  st.template update_ref<GQA>(lg, smax);
   float pr[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(lg[i] - st.m);
+  for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(lg[i] - st.ref);
   st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   // ---- fp16 weights w = p * s_V per group, and the correction
   //      Z += sum w * (bias + z) with the rounded weights
@@ -459,7 +533,7 @@ __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t sz = t.sc[4 * NG + i * NG + g];
-      w[i] = pr[i] * bf16_lo(sz);
+      w[i] = pr[i] * sv[g][i];
       zb[i] = bf16_hi(sz) + (LUT || i < 2 ? kBiasLo : kBiasHi);
     }
     const h2 w01 = __builtin_convertvector(f2{w[0], w[1]}, h2);
@@ -574,7 +648,7 @@ __device__ __forceinline__ void b16_compute(const B16Tile<D, GQA>& t, Acc<D, 1>&
   st.template update_max<GQA>(lg);
   float pr[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(lg[i] - st.m);
+  for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(lg[i] - st.ref);
   st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
 #pragma unroll
@@ -601,7 +675,7 @@ __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, in
   st.l = col_sum(st.l);
 #pragma unroll
   for (int g = 0; g < NG; ++g) st.Z[g] = col_sum(st.Z[g]);
-  const float mh = st.m;  // shared by the head's columns (update_max<GQA>)
+  const float mh = st.ref;  // shared by the head's columns (update_ref<GQA> / update_max<GQA>)
   st.l = slot_sum<GQA>(st.l);
 #pragma unroll
   for (int g = 0; g < NG; ++g) st.Z[g] = slot_sum<GQA>(st.Z[g]);
@@ -772,7 +846,7 @@ __global__ void __launch_bounds__(kThreads)
     // ---- prologue: q' = q R_K (fp32), per-head int8 split, B operands
     {
       v4i* bqz = &sm.bq[0][0][0][0];
-      for (int x = tid; x < C::SLOTS * 2 * C::KW * 64; x += kThreads) bqz[x] = v4i{0, 0, 0, 0};
+      for (int x = tid; x < C::SLOTS * 3 * C::KW * 64; x += kThreads) bqz[x] = v4i{0, 0, 0, 0};
     }
     float qacc[GQA][4];
 #pragma unroll
@@ -817,20 +891,15 @@ __global__ void __launch_bounds__(kThreads)
         for (int w = 0; w < kWaves; ++w) v += sm.u.qpart[w][h][CPL * lane + e];
         x[e] = v;
       }
-      float amax = 0.f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
-      amax = wave_max(amax);
-      const float sq = amax > 0.f ? amax / 127.f : 1.f;
-      const float inv_sq = 1.f / sq;
-      int sg = 0;
+      int ta[CPL], tb[CPL], tc[CPL];
+      bool dom;
+      const float sq = split_query<CPL>(x, ta, tb, tc, dom);
+      int sg = 0, sg3 = 0;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         const int c = CPL * lane + e;
-        const float y = x[e] * inv_sq;
-        const float a = fminf(fmaxf(rintf(y), -127.f), 127.f);
-        const float bt = fminf(fmaxf(rintf((y - a) * 256.f), -127.f), 127.f);
-        sg += 256 * (int)a + (int)bt;
+        sg += 256 * ta[e] + tb[e];
+        sg3 += 65536 * ta[e] + 256 * tb[e] + tc[e];
         // byte of channel c inside the transposed 16-byte operand of lane
         // group c%64/16 (the unpacked K codes hold channel 4*b + k at byte
         // 4*k + b)
@@ -839,43 +908,95 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int s = 0; s < C::SLOTS; ++s) {
           const int l = 16 * jj + s * GQA + h;
-          ((int8_t*)&sm.bq[s][0][w][l])[byte] = (int8_t)a;
-          ((int8_t*)&sm.bq[s][1][w][l])[byte] = (int8_t)bt;
+          ((int8_t*)&sm.bq[s][0][w][l])[byte] = (int8_t)ta[e];
+          ((int8_t*)&sm.bq[s][1][w][l])[byte] = (int8_t)tb[e];
+          ((int8_t*)&sm.bq[s][2][w][l])[byte] = (int8_t)tc[e];
         }
       }
       if constexpr (NG == 1) {
         sg = wave_sum_i(sg);
-        if (lane == 0) sm.sig[h] = sg;
+        sg3 = wave_sum_i(sg3);
+        if (lane == 0) {
+          sm.sig[h] = sg;
+          sm.sig3[h] = sg3;
+        }
       } else {
         // D = 128, G = 64: lanes 0-31 hold group 0, lanes 32-63 group 1
         sg = half_sum_i(sg);
-        if ((lane & 31) == 0) sm.sig[h * NG + (lane >> 5)] = sg;
+        sg3 = half_sum_i(sg3);
+        if ((lane & 31) == 0) {
+          sm.sig[h * NG + (lane >> 5)] = sg;
+          sm.sig3[h * NG + (lane >> 5)] = sg3;
+        }
       }
-      if (lane == 0) sm.kap[h] = p.sm_log2 * sq * (1.f / 256.f);
+      if (lane == 0) {
+        sm.kap[h] = p.sm_log2 * sq * (1.f / 256.f);
+        sm.kap3[h] = p.sm_log2 * sq * (1.f / 65536.f);
+        sm.dom[h] = dom ? 1 : 0;
+      }
     }
     __syncthreads();
-    const float kappa = sm.kap[chd];
+    // three-term mode for the whole workgroup when any of its heads needs it
+    int any_dom = 0;
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) any_dom |= sm.dom[h];
+    const bool t3 = NG == 1 && __builtin_amdgcn_readfirstlane(any_dom) != 0;
+    const float kappa = t3 ? sm.kap3[chd] : sm.kap[chd];
     float sig[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) sig[g] = (float)sm.sig[chd * NG + g];
+    for (int g = 0; g < NG; ++g) sig[g] = (float)(t3 ? sm.sig3[chd * NG + g] : sm.sig[chd * NG + g]);
     // fp16 exponent patterns of the P.V operands, held in VGPRs so that each
     // operand is one and-or (bitop3) of a shifted code word
     uint32_t exp_lo = kExpLo, exp_hi = kExpHi;
     asm volatile("" : "+v"(exp_lo), "+v"(exp_hi));
 
-    v4i bqr[C::SLOTS][2][C::KW];
-#pragma unroll
-    for (int s = 0; s < C::SLOTS; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int w = 0; w < C::KW; ++w) bqr[s][t][w] = sm.bq[s][t][w][lane];
-
     Acc<D, NG> st;
-    st.init();
-    if (nt_w > 0) {
+    st.init(true);
+    auto run = [&](auto t3c) {
+      constexpr bool T3 = decltype(t3c)::value;
+      // two-term mode: the loop-invariant B operands live in VGPRs
+      v4i bqr[C::SLOTS][2][C::KW];
+      if constexpr (!T3) {
+#pragma unroll
+        for (int s = 0; s < C::SLOTS; ++s)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int w = 0; w < C::KW; ++w) bqr[s][t][w] = sm.bq[s][t][w][lane];
+      }
       const uint32_t lut_k = p.lut_k, lut_v = p.lut_v;
-      I2Scores<NG> S = i2_scores<D, NG, GQA, LUT>(ring[0], bqr, lut_k);
+      // scores of one tile on the int8 matrix cores (block-diagonal B
+      // operands: slot s's page meets only the columns of slot s); the
+      // third term's operands stay in LDS
+      auto scores = [&](const I2Tile<D, NG, GQA>& t) {
+        I2Scores<NG> r;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) r.a[g] = r.b[g] = r.c[g] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < C::SLOTS; ++s) {
+#pragma unroll
+          for (int w = 0; w < C::KW; ++w) {
+            const v4i a = k_operand<LUT>(t.kw[s][w], lut_k);
+            const int g = (NG == 1) ? 0 : w;
+            if constexpr (T3) {
+              // three-term mode (rare): every operand is read from LDS per
+              // tile (volatile reads are not hoisted), so that this loop
+              // needs no registers for them
+              const v4i b0 = lds_read_fresh(&sm.bq[s][0][w][lane]);
+              const v4i b1 = lds_read_fresh(&sm.bq[s][1][w][lane]);
+              const v4i b2 = lds_read_fresh(&sm.bq[s][2][w][lane]);
+              r.a[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b0, r.a[g], 0, 0, 0);
+              r.b[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b1, r.b[g], 0, 0, 0);
+              r.c[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b2, r.c[g], 0, 0, 0);
+            } else {
+              r.a[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[s][0][w], r.a[g], 0, 0, 0);
+              r.b[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[s][1][w], r.b[g], 0, 0, 0);
+            }
+          }
+        }
+        return r;
+      };
+      I2Scores<NG> S = scores(ring[0]);
       int i = 0;
       while (true) {
 #pragma unroll
@@ -891,9 +1012,9 @@ __global__ void __launch_bounds__(kThreads)
           fetch(ring[(r + R - 1) % R], i + R - 1);
           // softmax of tile i first: the wait for tile i+1's data comes
           // after it, next to the MFMAs that need that data
-          const I2Weights<D, NG, GQA> W = i2_softmax<D, NG, GQA, LUT>(ring[r], S, st, kappa, sig, my_slot);
+          const I2Weights<D, NG, GQA> W = i2_softmax<D, NG, GQA, LUT, T3>(ring[r], S, st, kappa, sig, my_slot);
           __builtin_amdgcn_s_setprio(0);
-          S = i2_scores<D, NG, GQA, LUT>(ring[(r + 1) % R], bqr, lut_k);
+          S = scores(ring[(r + 1) % R]);
           __builtin_amdgcn_s_setprio(1);
           i2_pv<D, NG, GQA, LUT>(ring[r], W, st, exp_lo, exp_hi, lut_v);
           // slots r and r+1 hold arrived data (the loads of r+2 .. r+R-1 may
@@ -905,6 +1026,16 @@ __global__ void __launch_bounds__(kThreads)
         if (i >= nt_w) break;
       }
       __builtin_amdgcn_s_setprio(0);
+    };
+    if (nt_w > 0) {
+      // the three-term loop is compiled for one scale group per head only:
+      // with two groups its registers would push the two-term loop into
+      // spills (two groups keep ~16 bits of q' relative to its largest
+      // channel)
+      if (t3)
+        run(std::bool_constant<NG == 1>{});
+      else
+        run(std::false_type{});
     }
     wave_finish<D, NG, GQA, true>(st, sm, wave, lane);
   } else {
@@ -927,7 +1058,7 @@ __global__ void __launch_bounds__(kThreads)
     }
     const int ntiles = (end - first + SB - 1) / SB;
     Acc<D, 1> st;
-    st.init();
+    st.init(false);
     const int32_t* __restrict__ bpt = bf16_pt_all + (size_t)b * p.bf16_pt_stride;
     int tile = wave;
     B16Tile<D, GQA> cur;
@@ -950,6 +1081,9 @@ __global__ void __launch_bounds__(kThreads)
       for (int i = 0; i < D / 16; ++i) st2.o[i] = st.o[i];
       st2.m = st.m;
       st2.l = st.l;
+      st2.E = st.E;
+      st2.ref = st.ref;
+      st2.slim = st.slim;
 #pragma unroll
       for (int g = 0; g < NG; ++g) st2.Z[g] = 0.f;
     }
@@ -1132,9 +1266,10 @@ struct PSmem {
     float part[kWaves][16][D + 1];  // per-wave partials per column, [D] = lse (log2)
     float qpart[kWaves][16][D];     // prologue: per-wave partial sums of q R_K
   } u;
-  v4i bq[2][D / 64][64];            // int8 q' B operands (dense: every column)
-  float kap[16];
-  int sig[16 * NG];
+  v4i bq[3][D / 64][64];            // int8 q' B operands (dense: every column; terms a, b, c)
+  float kap[16], kap3[16];
+  int sig[16 * NG], sig3[16 * NG];
+  int dom[16];
 };
 
 // Loads the tile of logical pages lp0, lp0 + 1 (physical ids from lanes idx0,
@@ -1182,7 +1317,7 @@ __device__ __forceinline__ void pt_fetch(PTile<D, NG>& t, const uint8_t* __restr
 // Softmax of one prefix tile (both pages, every column): logits with tokens
 // past the column's member history masked, online max and sum, and the dense
 // fp16 P.V B operands.
-template <int D, int NG, bool LUT>
+template <int D, int NG, bool LUT, bool T3>
 __device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores<NG> (&S)[2], Acc<D, NG>& st,
                                            float kappa, const float (&sig)[NG], int lp0, int hist_len, int lane,
                                            v4i (&bw)[NG]) {
@@ -1195,19 +1330,24 @@ __device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores
       float acc = 0.f;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float sint = (float)(S[s].a[g][i] * 256 + S[s].b[g][i]) * (LUT ? 1.f / 32.f : 1.f);
+        const float sint = score_int<T3>(S[s].a[g][i], S[s].b[g][i], S[s].c[g][i]) * (LUT ? 1.f / 32.f : 1.f);
         const uint32_t sz = t.sc[s][i * NG + g];
         acc += bf16_lo(sz) * (sint - bf16_hi(sz) * sig[g]);
       }
       const bool ok = (lp0 + s) * kPage + 4 * j + i < hist_len;
       lg[s][i] = fmaf(acc, kappa, ok ? 0.f : -INFINITY);
     }
-  st.update_max(lg[0], lg[1]);
+  float smax = 0.f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int w = 0; w < 4 * NG; ++w) smax = fmaxf(smax, bf16_lo(t.sc[s][4 * NG + w]));
+  st.update_ref(lg[0], lg[1], smax);
   float pr[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[s][i] = __builtin_amdgcn_exp2f(lg[s][i] - st.m);
+    for (int i = 0; i < 4; ++i) pr[s][i] = __builtin_amdgcn_exp2f(lg[s][i] - st.ref);
   st.l += ((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) + ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3]));
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -1362,40 +1502,53 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
       for (int w = 0; w < kWaves; ++w) v += sm.u.qpart[w][col][CPL * lane + e];
       x[e] = v;
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    amax = wave_max(amax);
-    const float sq = amax > 0.f ? amax / 127.f : 1.f;
-    const float inv_sq = 1.f / sq;
-    int sg = 0;
+    int ta[CPL], tb[CPL], tc[CPL];
+    bool dom;
+    const float sq = split_query<CPL>(x, ta, tb, tc, dom);
+    int sg = 0, sg3 = 0;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       const int ch = CPL * lane + e;
-      const float y = x[e] * inv_sq;
-      const float a = fminf(fmaxf(rintf(y), -127.f), 127.f);
-      const float bt = fminf(fmaxf(rintf((y - a) * 256.f), -127.f), 127.f);
-      sg += 256 * (int)a + (int)bt;
+      sg += 256 * ta[e] + tb[e];
+      sg3 += 65536 * ta[e] + 256 * tb[e] + tc[e];
       const int w = ch / 64, jj = (ch % 64) / 16, mm = ch % 16;
       const int byte = 4 * (mm % 4) + mm / 4;
       const int l = 16 * jj + col;
-      ((int8_t*)&sm.bq[0][w][l])[byte] = (int8_t)a;
-      ((int8_t*)&sm.bq[1][w][l])[byte] = (int8_t)bt;
+      ((int8_t*)&sm.bq[0][w][l])[byte] = (int8_t)ta[e];
+      ((int8_t*)&sm.bq[1][w][l])[byte] = (int8_t)tb[e];
+      ((int8_t*)&sm.bq[2][w][l])[byte] = (int8_t)tc[e];
     }
     if constexpr (NG == 1) {
       sg = wave_sum_i(sg);
-      if (lane == 0) sm.sig[col] = sg;
+      sg3 = wave_sum_i(sg3);
+      if (lane == 0) {
+        sm.sig[col] = sg;
+        sm.sig3[col] = sg3;
+      }
     } else {
       sg = half_sum_i(sg);
-      if ((lane & 31) == 0) sm.sig[col * NG + (lane >> 5)] = sg;
+      sg3 = half_sum_i(sg3);
+      if ((lane & 31) == 0) {
+        sm.sig[col * NG + (lane >> 5)] = sg;
+        sm.sig3[col * NG + (lane >> 5)] = sg3;
+      }
     }
-    if (lane == 0) sm.kap[col] = p.sm_log2 * sq * (1.f / 256.f);
+    if (lane == 0) {
+      sm.kap[col] = p.sm_log2 * sq * (1.f / 256.f);
+      sm.kap3[col] = p.sm_log2 * sq * (1.f / 65536.f);
+      sm.dom[col] = dom ? 1 : 0;
+    }
   }
   __syncthreads();
-  const float kappa = sm.kap[n];
+  // three-term mode for the whole workgroup when any column needs it
+  int any_dom = 0;
+#pragma unroll
+  for (int c2 = 0; c2 < 16; ++c2) any_dom |= sm.dom[c2];
+  const bool t3 = NG == 1 && __builtin_amdgcn_readfirstlane(any_dom) != 0;
+  const float kappa = t3 ? sm.kap3[n] : sm.kap[n];
   float sig[NG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) sig[g] = (float)sm.sig[n * NG + g];
+  for (int g = 0; g < NG; ++g) sig[g] = (float)(t3 ? sm.sig3[n * NG + g] : sm.sig[n * NG + g]);
   uint32_t exp_lo = kExpLo, exp_hi = kExpHi;
   asm volatile("" : "+v"(exp_lo), "+v"(exp_hi));
   v4i bqr[2][KW];
@@ -1406,24 +1559,29 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
   __syncthreads();  // the union's qpart is reused for the partials below
 
   const uint32_t lut_k = p.lut_k, lut_v = p.lut_v;
-  auto scores = [&](const PTile<D, NG>& t, I2Scores<NG> (&S)[2]) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int g = 0; g < NG; ++g) S[s].a[g] = S[s].b[g] = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int w = 0; w < KW; ++w) {
-        const v4i a = k_operand<LUT>(t.kw[s][w], lut_k);
-        const int g = (NG == 1) ? 0 : w;
-        S[s].a[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[0][w], S[s].a[g], 0, 0, 0);
-        S[s].b[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[1][w], S[s].b[g], 0, 0, 0);
-      }
-    }
-  };
-
   Acc<D, NG> st;
-  st.init();
-  if (nt_w > 0) {
+  st.init(true);
+  auto run = [&](auto t3c) {
+    constexpr bool T3 = decltype(t3c)::value;
+    // the third term's operands stay in LDS
+    auto scores = [&](const PTile<D, NG>& t, I2Scores<NG> (&S)[2]) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) S[s].a[g] = S[s].b[g] = S[s].c[g] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < KW; ++w) {
+          const v4i a = k_operand<LUT>(t.kw[s][w], lut_k);
+          const int g = (NG == 1) ? 0 : w;
+          S[s].a[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[0][w], S[s].a[g], 0, 0, 0);
+          S[s].b[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bqr[1][w], S[s].b[g], 0, 0, 0);
+          if constexpr (T3) {
+            const v4i b3 = lds_read_fresh(&sm.bq[2][w][lane]);  // not hoisted (registers)
+            S[s].c[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b3, S[s].c[g], 0, 0, 0);
+          }
+        }
+      }
+    };
     I2Scores<NG> S[2];
     scores(ring[0], S);
     int i = 0;
@@ -1435,7 +1593,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
         __builtin_amdgcn_s_setprio(2);
         fetch(ring[(r + R - 1) % R], i + R - 1);
         v4i bw[NG];
-        pt_softmax<D, NG, LUT>(ring[r], S, st, kappa, sig, first + (wave + i * kWaves) * 2, my_hist, lane, bw);
+        pt_softmax<D, NG, LUT, T3>(ring[r], S, st, kappa, sig, first + (wave + i * kWaves) * 2, my_hist, lane, bw);
         __builtin_amdgcn_s_setprio(0);
         scores(ring[(r + 1) % R], S);
         __builtin_amdgcn_s_setprio(1);
@@ -1449,6 +1607,13 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
       if (i >= nt_w) break;
     }
     __builtin_amdgcn_s_setprio(0);
+  };
+  if (nt_w > 0) {
+    // three terms for one scale group per head only, as in k_decode
+    if (t3)
+      run(std::bool_constant<NG == 1>{});
+    else
+      run(std::false_type{});
   }
   // ---- wave epilogue: one (o, lse) per column (no two columns share a head)
   st.l = col_sum(st.l);
@@ -1463,7 +1628,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
         const int g = (cbk * 16) / G;
         sm.u.part[wave][n][cbk * 16 + 4 * j + i] = (st.o[cbk][i] - st.Z[g]) * inv;
       }
-    if (j == 0) sm.u.part[wave][n][D] = st.l > 0.f ? st.m + __log2f(st.l) : -INFINITY;
+    if (j == 0) sm.u.part[wave][n][D] = st.l > 0.f ? st.ref + __log2f(st.l) : -INFINITY;
   }
   __syncthreads();
   // ---- merge the waves and store each column's partial in its member's

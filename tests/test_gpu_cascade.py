@@ -182,3 +182,18 @@ def test_cascade_group_with_empty_member(gpu_lib):
     keep = [b for b in range(len(seqs)) if b != empty]
     ref, _ = oracle.decode_attention([seqs[b] for b in keep], inp.q[keep].float().numpy(), inp.calib.r_k)
     check_decode(out[keep], ref, what="cascade, group with an empty member")
+
+
+@pytest.mark.parametrize("vscale", [1e-6, 500.0])
+def test_cascade_value_range_unclipped(gpu_lib, vscale):
+    """The prefix kernel keeps the same value-scale exponent as the decode
+    kernel: values x1e-6 and x500 with no value clip (tau_V = +inf), GQA 8."""
+    wl, groups = CASES["d128-gqa8"]
+    inp = _prefix_inputs(wl, groups)
+    inp.v = [(v.float() * vscale).to(torch.bfloat16) for v in inp.v]
+    seqs = make_seqs(wl, inp, tau_v=np.full(wl.num_kv_heads, np.inf, np.float32))
+    pools = _share_tables(pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent,
+                                              seed=wl.seed), seqs, groups)
+    out, _ = _run(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k, groups)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
+    check_decode(out, ref, what=f"cascade, values x{vscale:g}, no value clip")

@@ -171,3 +171,68 @@ def test_merge_matches_oracle(gpu_lib, d):
         nrm = np.linalg.norm(ref[i])
         assert np.max(np.abs(got[i] - ref[i])) <= DECODE_TOL * max(nrm, 1e-30) + (0 if nrm > 0 else 0), i
     assert np.all(got[3] == 0) and np.all(got[5] == 0)
+
+
+def _value_scaled(inp, factor):
+    """The draw with every value multiplied by factor(t) (a scalar or an
+    array over token positions), rounded to bf16 like the cache content."""
+    vs = []
+    for v in inp.v:
+        f = torch.as_tensor(factor(v.shape[0]) if callable(factor) else factor, dtype=torch.float32)
+        f = f.reshape(-1, 1, 1) if f.ndim == 1 else f
+        vs.append((v.float() * f).to(torch.bfloat16))
+    inp.v = vs
+    return inp
+
+
+@pytest.mark.parametrize("gqa", [4, 8])
+@pytest.mark.parametrize("vscale", [1e-8, 1e-3, 300.0, 1e12])
+def test_decode_value_range_unclipped(gpu_lib, gqa, vscale):
+    """Values far from N(0, 1) with no value clip (tau_V = +inf): the value
+    scales s_V run from ~1e-8 to ~1e12, so the fp16 P.V weights p * s_V
+    would leave fp16's range without the scale exponent the kernel keeps
+    beside its running max.  Tolerance as everywhere (2e-3 of each head's
+    norm)."""
+    wl = make_workload(QWEN, num_q_heads=2 * gqa, num_kv_heads=2, batch=2, seq_lens=(3000, 777), seed=20 + gqa)
+    log(f"value range case gqa={gqa} scale={vscale}")
+    inp = _value_scaled(draw_inputs(wl), vscale)
+    tau_v = np.full(wl.num_kv_heads, np.inf, np.float32)
+    seqs = make_seqs(wl, inp, tau_v=tau_v)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
+    check_decode(out, ref, what=f"gqa {gqa}, values x{vscale:g}, no value clip")
+
+
+@pytest.mark.parametrize("gqa", [4, 8])
+def test_decode_value_scale_ramp(gpu_lib, gqa):
+    """Value magnitudes growing 2^(t/400) along the sequence (64x over the
+    history), so the scale exponent is raised several times inside a wave's
+    tiles and the accumulated state is rescaled each time."""
+    wl = make_workload(QWEN, num_q_heads=2 * gqa, num_kv_heads=2, batch=1, seq_lens=(2700,), seed=30 + gqa)
+    inp = _value_scaled(draw_inputs(wl), lambda n: 2.0 ** (np.arange(n) / 400.0))
+    tau_v = np.full(wl.num_kv_heads, np.inf, np.float32)
+    seqs = make_seqs(wl, inp, tau_v=tau_v)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
+    check_decode(out, ref, what=f"gqa {gqa}, value scale ramp")
+
+
+@pytest.mark.parametrize("gqa", [4, 8])
+def test_decode_dominant_query_channel(gpu_lib, gqa):
+    """R_K = I and one query channel 50x the others: q' = q, so the int8
+    split of q' is scaled by that one channel and the other channels keep
+    fewer significant bits.  Keys are unrotated and unclipped."""
+    wl = make_workload(QWEN, num_q_heads=2 * gqa, num_kv_heads=2, batch=2, seq_lens=(4000, 900), seed=40 + gqa)
+    inp = draw_inputs(wl)
+    q = inp.q.float()
+    q[:, :, 17] *= 50.0
+    inp.q = q.to(torch.bfloat16)
+    eye = np.broadcast_to(np.eye(wl.head_dim, dtype=np.float32), (wl.num_kv_heads, wl.head_dim, wl.head_dim)).copy()
+    tau_k = np.full(wl.num_kv_heads, np.inf, np.float32)
+    seqs = make_seqs(wl, inp, r_k=eye, tau_k=tau_k)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, eye)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), eye)
+    check_decode(out, ref, what=f"gqa {gqa}, one query channel x50, R_K = I")
