@@ -200,6 +200,26 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
                                     const float* r_k, const float* r_v, void* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* oscar_decode_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and result as oscar_decode_attention,
+ * without the workspace: the decode's partials and tickets live in a
+ * library-owned device array of OSCAR_NOALLOC_SCRATCH_BYTES per GPU, kept
+ * until the process ends.  The call allocates nothing.  A request whose
+ * decode workspace (oscar_decode_workspace_bytes) exceeds that size returns
+ * OSCAR_ERR_UNSUPPORTED and launches nothing.  The first call on a device
+ * also enqueues a clear of the array on `stream`; every call leaves the
+ * array's tickets at zero.  All calls on one GPU share the array, so calls
+ * that overlap in time on one GPU (concurrent streams, threads) race and
+ * give undefined results. */
+#define OSCAR_NOALLOC_SCRATCH_BYTES (8u << 20)
+oscar_status oscar_decode_attention_noalloc(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
+                                            const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                            int32_t bf16_pt_stride, int32_t bf16_num_pages,
+                                            const int32_t* int2_page_table, int32_t int2_pt_stride,
+                                            int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
+                                            const float* r_k, const float* r_v, void* out, void* stream);
+
 /* Prefix-shared ("cascade") decode.  The pages keep the paged pool's prefix
  * sharing intact (MarkTechPost article, "Visual Explainer / How-To", the
  * inference step: the radix cache and prefix reuse work unchanged) and report

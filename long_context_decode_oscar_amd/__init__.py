@@ -29,7 +29,7 @@ EXPORTED = (
     "oscar_calib_clip_workspace_bytes", "oscar_calib_clip", "oscar_calib_workspace_bytes", "oscar_calibrate",
     "oscar_dequantize", "oscar_attention_error",
     "oscar_decode_cascade_workspace_bytes", "oscar_decode_attention_cascade",
-    "oscar_calib_codebook_workspace_bytes", "oscar_calib_codebook",
+    "oscar_calib_codebook_workspace_bytes", "oscar_calib_codebook", "oscar_decode_attention_noalloc",
 )
 
 
@@ -80,6 +80,7 @@ def load(path: str = LIB_PATH):
     lib.oscar_decode_workspace_bytes.argtypes = [P, I, I, I, ctypes.POINTER(S)]
     lib.oscar_append_demote.argtypes = [P, I, P, P, P, P, I, I, P, I, I, P, P, P, P, P, P, P]
     lib.oscar_decode_attention.argtypes = [P, I, I, P, P, P, I, I, P, I, I, P, P, P, P, P, P, S, P]
+    lib.oscar_decode_attention_noalloc.argtypes = [P, I, I, P, P, P, I, I, P, I, I, P, P, P, P, P, P]
     lib.oscar_merge.argtypes = [I, I, P, P, P, P, P]
     lib.oscar_quantize_pack.argtypes = [P, I, P, P, P, I, P, P, P, P, P, P]
     lib.oscar_bf16_decode_attention.argtypes = [P, I, I, P, P, P, I, I, P, P, P, S, P]
@@ -226,6 +227,27 @@ def oscar_decode_attention(pool: OscarPool, q, seq_lens, max_seq_len: int, bf16_
         _ptr(r_k, "r_k", torch.float32), _ptr(r_v, "r_v", torch.float32), _ptr(out, "out", torch.bfloat16),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)),
         "oscar_decode_attention")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # OSCAR_NOALLOC_SCRATCH_BYTES
+
+
+def oscar_decode_attention_noalloc(pool: OscarPool, q, seq_lens, max_seq_len: int, bf16_page_table, int2_page_table,
+                                   bf16_pool, int2_pool, r_k, out, r_v=None, stream=None):
+    """oscar_decode_attention without a workspace: the library's own device
+    scratch holds the partials (calls that overlap on one GPU race)."""
+    import torch
+    _check(load().oscar_decode_attention_noalloc(
+        pool.handle, q.shape[0], int(max_seq_len), _ptr(q, "q", torch.bfloat16), _ptr(seq_lens, "seq_lens", torch.int32),
+        _ptr(bf16_page_table, "bf16_page_table", torch.int32), bf16_page_table.shape[1],
+        _pages(bf16_pool, pool.bf16_page_bytes),
+        _ptr(int2_page_table, "int2_page_table", torch.int32), int2_page_table.shape[1],
+        _pages(int2_pool, pool.int2_page_bytes),
+        _ptr(bf16_pool, "bf16_pool", torch.uint8), _ptr(int2_pool, "int2_pool", torch.uint8),
+        _ptr(r_k, "r_k", torch.float32), _ptr(r_v, "r_v", torch.float32), _ptr(out, "out", torch.bfloat16),
+        _stream(stream)),
+        "oscar_decode_attention_noalloc")
     return out
 
 

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -544,6 +545,75 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
   return decode_impl(pool, batch, max_seq_len, q, seq_lens, bf16_page_table, bf16_pt_stride, bf16_num_pages,
                      int2_page_table, int2_pt_stride, int2_num_pages, bf16_pool, int2_pool, r_k, r_v, out, nullptr, 0,
                      workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- decode without a workspace argument ----
+// The scratch of oscar_decode_attention_noalloc: a fixed array in device
+// memory, one copy per GPU the library runs on, held until the process ends.
+// Host code reaches it only through the per-device address that
+// hipGetSymbolAddress returns (kept in g_scratch_ptr).
+static __device__ __align__(256) uint8_t scratch[OSCAR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void k_zero_words(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's scratch address.  At the first call on a device the
+// address is looked up and the whole array is cleared by a kernel on
+// `stream` (a kernel rather than a memset, so that the clear can also sit in
+// a captured graph); afterwards every decode leaves its counters at zero.
+oscar_status current_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(OSCAR_ERR_HIP, "hipGetDevice failed");
+  if (dev >= kMaxDevices) return fail(OSCAR_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(OSCAR_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    const uint32_t words = OSCAR_NOALLOC_SCRATCH_BYTES / 4;
+    hipLaunchKernelGGL(k_zero_words, dim3(256), dim3(256), 0, stream, (uint32_t*)ptr, words);
+    const oscar_status st = check_hip("scratch clear launch");
+    if (st != OSCAR_OK) return st;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return OSCAR_OK;
+}
+}  // namespace
+
+extern "C" {
+
+oscar_status oscar_decode_attention_noalloc(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
+                                            const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                            int32_t bf16_pt_stride, int32_t bf16_num_pages,
+                                            const int32_t* int2_page_table, int32_t int2_pt_stride,
+                                            int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
+                                            const float* r_k, const float* r_v, void* out, void* stream) {
+  if (!pool) return fail(OSCAR_ERR_INVALID, "pool must be non-null");
+  if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID, "negative batch or max_seq_len");
+  if (batch == 0) return ok();
+  const Plan pl = make_plan(pool, batch, max_seq_len, false);
+  if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
+  if (pl.bytes > OSCAR_NOALLOC_SCRATCH_BYTES)
+    return fail(OSCAR_ERR_UNSUPPORTED,
+                "batch %d at max_seq_len %d needs %zu bytes of decode scratch; the allocation-free decode holds %zu "
+                "(use oscar_decode_attention with a workspace)",
+                batch, max_seq_len, pl.bytes, (size_t)OSCAR_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const oscar_status st = current_scratch((hipStream_t)stream, &ws);
+  if (st != OSCAR_OK) return st;
+  return decode_impl(pool, batch, max_seq_len, q, seq_lens, bf16_page_table, bf16_pt_stride, bf16_num_pages,
+                     int2_page_table, int2_pt_stride, int2_num_pages, bf16_pool, int2_pool, r_k, r_v, out, nullptr, 0,
+                     ws, OSCAR_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 oscar_status oscar_decode_cascade_workspace_bytes(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
