@@ -108,12 +108,17 @@ def parse():
 class Decoder:
     """Pre-marshalled oscar_decode_attention calls, one per pool copy."""
 
-    def __init__(self, oscar, pool, wl, q, lens, copies, r_k, out, ws, bf16_only=False, groups=None):
+    def __init__(self, oscar, pool, wl, q, lens, copies, r_k, out, ws, bf16_only=False, groups=None,
+                 host_lengths=True):
         import torch
         lib = oscar.load()
         self.lib = lib
         self.bf16_only = bf16_only
         self.torch = torch
+        # the sequences' lengths on the host: the length-aware split-K plan
+        # (host_lengths=False: every sequence planned for the longest)
+        self.host_lens = oscar.HostLengths(wl.seq_lens)
+        hptr = self.host_lens.ptr if host_lengths else None
         self.args = []
         for c in copies:
             b16, i2 = c["bf16_pool"], c["int2_pool"]
@@ -122,7 +127,7 @@ class Decoder:
                                   c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], b16.shape[0],
                                   b16.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()))
             else:
-                self.args.append((pool.handle, wl.batch, max(wl.seq_lens), q.data_ptr(), lens.data_ptr(),
+                self.args.append((pool.handle, wl.batch, max(wl.seq_lens), q.data_ptr(), lens.data_ptr(), hptr,
                                   c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], b16.shape[0],
                                   c["int2_pt"].data_ptr(), c["int2_pt"].shape[1], i2.shape[0],
                                   b16.data_ptr(), i2.data_ptr(), r_k.data_ptr(), None,
@@ -287,10 +292,12 @@ def unique_kv_bytes(wl):
     return kv["total"] - dup
 
 
-def bench_decode_workload(oscar, name, steps, warmup, repeats, cold_bytes):
+def bench_decode_workload(oscar, name, steps, warmup, repeats, cold_bytes, profile_launches=0):
     """Decode steps of a batched workload, timed like the headline: HIP-graph
     replay over cold pool copies.  With wl.demote every step also appends one
-    token per sequence and demotes one to the INT2 history."""
+    token per sequence and demotes one to the INT2 history.  profile_launches
+    > 0 only runs that many eager steps (for rocprofv3 counters) and returns
+    None."""
     import torch
     from synthetic import CONFIGS, draw_inputs
     wl = CONFIGS[name]
@@ -316,7 +323,21 @@ def bench_decode_workload(oscar, name, steps, warmup, repeats, cold_bytes):
         step = DemoteDecoder(oscar, pool, wl, q, copies, r_k, tau_k, tau_v, k_new, v_new, lens_pre, lens, out, ws)
     else:
         step = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws)
+    if profile_launches:
+        for i in range(profile_launches):
+            step(i)
+        torch.cuda.synchronize()
+        log(f"profile run: {profile_launches} {name} steps done")
+        return None
     ms, ms_min = time_steps(step, steps, warmup, repeats, use_graph=True)
+    uniform = None
+    if wl.batch > 1 and len(set(wl.seq_lens)) > 1:
+        # the same step with every sequence planned for the longest one
+        ustep = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws, host_lengths=False)
+        ms_u, _ = time_steps(ustep, steps, warmup, repeats, use_graph=True)
+        uniform = {"us_per_step": round(ms_u * 1e3, 3), "host_length_plan_speedup": round(ms_u / ms, 3)}
+        log(f"{name} max-length plan: {ms_u * 1e3:.2f} us/step ({ms_u / ms:.2f}x the host-length plan)")
+        del ustep
     cascade = None
     if wl.shared_prefix_seqs:
         # the same step with the shared prefix pages attended once per group
@@ -356,6 +377,8 @@ def bench_decode_workload(oscar, name, steps, warmup, repeats, cold_bytes):
     if wl.demote:
         res["append_demote"] = "one token appended and one demoted per sequence inside every timed step"
         res["int2_arena_GiB"] = round(wl.int2_arena_bytes / 2**30, 1)
+    if uniform:
+        res["max_length_plan"] = uniform
     if wl.shared_prefix_seqs:
         res["shared_prefix"] = f"{wl.shared_prefix_seqs} sequences share {wl.shared_prefix_tokens} tokens"
         res["logical_GBps"] = round(kv["total"] / (ms * 1e-3) / 1e9, 2)
@@ -652,6 +675,10 @@ def main():
     oscar.load()
     if args.only in ("demote", "mixed"):
         name = "qwen3-8b-b32-l32k-demote" if args.only == "demote" else "qwen3-32b-b8-mixed-prefix"
+        if args.profile_steps:
+            bench_decode_workload(oscar, name, 0, 0, 0, args.cold_bytes, profile_launches=args.profile_steps)
+            copy_probe(args.probe_bytes)
+            return
         print(json.dumps({args.only: bench_decode_workload(oscar, name, max(10, args.steps // 4), args.warmup,
                                                            args.repeats, args.cold_bytes)}), flush=True)
         return

@@ -180,6 +180,15 @@ oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const vo
  * clamped to max_seq_len and to what the page tables can address; lengths
  * of 0 or less select no token and give zero output rows); out:
  * bf16 [batch][Hq][D].
+ * seq_lens_host: NULL, or the same lengths in host memory (int32 [batch]).
+ * With them (and batch <= 128) the split-K plan follows each sequence's own
+ * history: every sequence gets as many chunks as its pages need, and the
+ * chunk size is the smallest that fills whole rounds of workgroups over the
+ * compute units (ModelScope/CSDN page, design section: split INT2 and BF16
+ * kernels merged by online softmax; the chunk count per sequence length).
+ * Without them every sequence is planned for max_seq_len.  The device
+ * lengths must not exceed the host ones (tokens past a sequence's planned
+ * history would not be attended).
  * workspace: oscar_decode_workspace_bytes(pool, batch, max_seq_len, 0) bytes,
  * 256-byte aligned, zero-filled before first use.
  * Value range: the history's P.V runs on fp16 matrix cores with weights
@@ -193,7 +202,7 @@ oscar_status oscar_append_demote(const oscar_pool* pool, int32_t batch, const vo
  * channel above 8x its rms (group_size = head_dim; with two scale groups per
  * head the two-term split is kept). */
 oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
-                                    const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                    const int32_t* seq_lens, const int32_t* seq_lens_host, const int32_t* bf16_page_table,
                                     int32_t bf16_pt_stride, int32_t bf16_num_pages,
                                     const int32_t* int2_page_table, int32_t int2_pt_stride,
                                     int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
@@ -214,7 +223,7 @@ oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32
  * give undefined results. */
 #define OSCAR_NOALLOC_SCRATCH_BYTES (8u << 20)
 oscar_status oscar_decode_attention_noalloc(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
-                                            const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                            const int32_t* seq_lens, const int32_t* seq_lens_host, const int32_t* bf16_page_table,
                                             int32_t bf16_pt_stride, int32_t bf16_num_pages,
                                             const int32_t* int2_page_table, int32_t int2_pt_stride,
                                             int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
@@ -252,7 +261,7 @@ oscar_status oscar_decode_cascade_workspace_bytes(const oscar_pool* pool, int32_
                                                   int32_t int2_pt_stride, const oscar_prefix_group* groups,
                                                   int32_t num_groups, size_t* bytes);
 oscar_status oscar_decode_attention_cascade(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
-                                            const void* q, const int32_t* seq_lens,
+                                            const void* q, const int32_t* seq_lens, const int32_t* seq_lens_host,
                                             const int32_t* bf16_page_table, int32_t bf16_pt_stride,
                                             int32_t bf16_num_pages, const int32_t* int2_page_table,
                                             int32_t int2_pt_stride, int32_t int2_num_pages, const void* bf16_pool,

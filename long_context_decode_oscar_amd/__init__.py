@@ -79,8 +79,8 @@ def load(path: str = LIB_PATH):
     lib.oscar_pool_destroy.restype = None
     lib.oscar_decode_workspace_bytes.argtypes = [P, I, I, I, ctypes.POINTER(S)]
     lib.oscar_append_demote.argtypes = [P, I, P, P, P, P, I, I, P, I, I, P, P, P, P, P, P, P]
-    lib.oscar_decode_attention.argtypes = [P, I, I, P, P, P, I, I, P, I, I, P, P, P, P, P, P, S, P]
-    lib.oscar_decode_attention_noalloc.argtypes = [P, I, I, P, P, P, I, I, P, I, I, P, P, P, P, P, P]
+    lib.oscar_decode_attention.argtypes = [P, I, I, P, P, P, P, I, I, P, I, I, P, P, P, P, P, P, S, P]
+    lib.oscar_decode_attention_noalloc.argtypes = [P, I, I, P, P, P, P, I, I, P, I, I, P, P, P, P, P, P]
     lib.oscar_merge.argtypes = [I, I, P, P, P, P, P]
     lib.oscar_quantize_pack.argtypes = [P, I, P, P, P, I, P, P, P, P, P, P]
     lib.oscar_bf16_decode_attention.argtypes = [P, I, I, P, P, P, I, I, P, P, P, S, P]
@@ -97,7 +97,7 @@ def load(path: str = LIB_PATH):
     lib.oscar_dequantize.argtypes = [P, I, P, I, P, P, P, P, P, P]
     lib.oscar_attention_error.argtypes = [I, I, I, I, F, P, P, P, P, P, L, L, P, P]
     lib.oscar_decode_cascade_workspace_bytes.argtypes = [P, I, I, I, P, I, ctypes.POINTER(S)]
-    lib.oscar_decode_attention_cascade.argtypes = [P, I, I, P, P, P, I, I, P, I, I, P, P, P, P, P, P, I, P, S, P]
+    lib.oscar_decode_attention_cascade.argtypes = [P, I, I, P, P, P, P, I, I, P, I, I, P, P, P, P, P, P, I, P, S, P]
     lib.oscar_calib_codebook_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(S)]
     lib.oscar_calib_codebook.argtypes = [I, I, I, I, P, L, L, P, P, P, P, S, P]
     lib.oscar_status_string.argtypes = [ctypes.c_int]
@@ -197,6 +197,29 @@ def _pages(pool_tensor, page_bytes):
     return pool_tensor.numel() // page_bytes
 
 
+class HostLengths:
+    """Host copy of a batch's lengths for the length-aware split-K plan
+    (seq_lens_host of the decode calls); keeps the int32 array alive."""
+
+    def __init__(self, lengths):
+        vals = [int(x) for x in lengths]
+        self.array = (ctypes.c_int32 * max(len(vals), 1))(*vals)
+        self.count = len(vals)
+
+    @property
+    def ptr(self):
+        return ctypes.cast(self.array, ctypes.c_void_p)
+
+
+def _host_lens(seq_lens_host, batch):
+    if seq_lens_host is None:
+        return None, None
+    h = seq_lens_host if isinstance(seq_lens_host, HostLengths) else HostLengths(seq_lens_host)
+    if h.count != batch:
+        raise ValueError(f"seq_lens_host holds {h.count} lengths for a batch of {batch}")
+    return h, h.ptr
+
+
 def oscar_append_demote(pool: OscarPool, k_new, v_new, seq_lens, bf16_page_table, int2_page_table, bf16_pool,
                         int2_pool, r_k, tau_k, tau_v, r_v=None, stream=None):
     import torch
@@ -215,10 +238,14 @@ def oscar_append_demote(pool: OscarPool, k_new, v_new, seq_lens, bf16_page_table
 
 
 def oscar_decode_attention(pool: OscarPool, q, seq_lens, max_seq_len: int, bf16_page_table, int2_page_table,
-                           bf16_pool, int2_pool, r_k, out, workspace, r_v=None, stream=None):
+                           bf16_pool, int2_pool, r_k, out, workspace, r_v=None, stream=None, seq_lens_host=None):
+    """seq_lens_host: the lengths on the host (a sequence of ints or
+    HostLengths) for the length-aware split-K plan, or None."""
     import torch
+    keep, hptr = _host_lens(seq_lens_host, q.shape[0])
     _check(load().oscar_decode_attention(
         pool.handle, q.shape[0], int(max_seq_len), _ptr(q, "q", torch.bfloat16), _ptr(seq_lens, "seq_lens", torch.int32),
+        hptr,
         _ptr(bf16_page_table, "bf16_page_table", torch.int32), bf16_page_table.shape[1],
         _pages(bf16_pool, pool.bf16_page_bytes),
         _ptr(int2_page_table, "int2_page_table", torch.int32), int2_page_table.shape[1],
@@ -234,12 +261,14 @@ NOALLOC_SCRATCH_BYTES = 8 << 20  # OSCAR_NOALLOC_SCRATCH_BYTES
 
 
 def oscar_decode_attention_noalloc(pool: OscarPool, q, seq_lens, max_seq_len: int, bf16_page_table, int2_page_table,
-                                   bf16_pool, int2_pool, r_k, out, r_v=None, stream=None):
+                                   bf16_pool, int2_pool, r_k, out, r_v=None, stream=None, seq_lens_host=None):
     """oscar_decode_attention without a workspace: the library's own device
     scratch holds the partials (calls that overlap on one GPU race)."""
     import torch
+    keep, hptr = _host_lens(seq_lens_host, q.shape[0])
     _check(load().oscar_decode_attention_noalloc(
         pool.handle, q.shape[0], int(max_seq_len), _ptr(q, "q", torch.bfloat16), _ptr(seq_lens, "seq_lens", torch.int32),
+        hptr,
         _ptr(bf16_page_table, "bf16_page_table", torch.int32), bf16_page_table.shape[1],
         _pages(bf16_pool, pool.bf16_page_bytes),
         _ptr(int2_page_table, "int2_page_table", torch.int32), int2_page_table.shape[1],
@@ -271,13 +300,15 @@ def cascade_workspace_bytes(pool: OscarPool, batch: int, max_seq_len: int, int2_
 
 def oscar_decode_attention_cascade(pool: OscarPool, q, seq_lens, max_seq_len: int, bf16_page_table,
                                    int2_page_table, bf16_pool, int2_pool, r_k, out, workspace, groups, r_v=None,
-                                   stream=None):
+                                   stream=None, seq_lens_host=None):
     """Decode with prefix groups [(first_seq, num_seqs, shared_pages), ...]
     whose INT2 page tables share their first shared_pages history pages."""
     import torch
     arr, ng = _groups(groups)
+    keep, hptr = _host_lens(seq_lens_host, q.shape[0])
     _check(load().oscar_decode_attention_cascade(
         pool.handle, q.shape[0], int(max_seq_len), _ptr(q, "q", torch.bfloat16), _ptr(seq_lens, "seq_lens", torch.int32),
+        hptr,
         _ptr(bf16_page_table, "bf16_page_table", torch.int32), bf16_page_table.shape[1],
         _pages(bf16_pool, pool.bf16_page_bytes),
         _ptr(int2_page_table, "int2_page_table", torch.int32), int2_page_table.shape[1],

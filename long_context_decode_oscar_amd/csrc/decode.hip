@@ -707,11 +707,19 @@ __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, in
 }
 
 // ------------------------------------------------------------- kernel ----
-template <int D, int NG, int GQA, bool BF16_ONLY, bool LUT, bool CASC>
+// The plan argument: the length-aware plan's tables for the PACKED
+// instantiations, an empty placeholder otherwise.
+template <bool PACKED>
+struct PlanArg {};
+template <>
+struct PlanArg<true> : PackedPlanArgs {};
+
+template <int D, int NG, int GQA, bool BF16_ONLY, bool LUT, bool CASC, bool PACKED>
 __global__ void __launch_bounds__(kThreads)
     k_decode(const DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ bf16_pt_all,
              const int32_t* __restrict__ int2_pt_all, const uint8_t* __restrict__ bf16_pool,
-             const uint8_t* __restrict__ int2_pool, const uint16_t* __restrict__ qin, const float* __restrict__ r_k) {
+             const uint8_t* __restrict__ int2_pool, const uint16_t* __restrict__ qin, const float* __restrict__ r_k,
+             const PlanArg<PACKED> pa) {
   using C = DC<D, NG, GQA>;
   __shared__ Smem<D, GQA> sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -720,10 +728,61 @@ __global__ void __launch_bounds__(kThreads)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, j = lane >> 4;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int U = p.units_per_head;
-  const int u = lin % U;
-  const int kvh = (lin / U) % p.num_kv_heads;
-  const int b = lin / (U * p.num_kv_heads);
+  // this workgroup's (sequence, KV head, unit), its head's units U and
+  // partial slots [slot0, slot0 + head_slots)
+  int U, u, kvh, b, head_slots, slot0;
+  if constexpr (!BF16_ONLY && PACKED) {
+    // the first 16 offsets are read with constant indices (one batch of
+    // scalar loads next to the other arguments); longer batches continue
+    // with a binary search over the rest
+    constexpr int kReg = 16;
+    int wo[kReg + 1], so[kReg + 1];
+#pragma unroll
+    for (int i = 0; i <= kReg; ++i) {
+      wo[i] = pa.wg_off[i];
+      so[i] = pa.slot_off[i];
+    }
+    int wb = 0, we = 0, sb = 0, se = 0;
+    b = 0;
+#pragma unroll
+    for (int i = 0; i < kReg; ++i)
+      if (i < p.batch && wo[i] <= lin) {
+        b = i;
+        wb = wo[i];
+        we = wo[i + 1];
+        sb = so[i];
+        se = so[i + 1];
+      }
+    if (p.batch > kReg && lin >= wo[kReg]) {
+      int lo = kReg, hi = p.batch;  // wg_off[lo] <= lin < wg_off[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pa.wg_off[mid] <= lin)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      b = lo;
+      wb = pa.wg_off[b];
+      we = pa.wg_off[b + 1];
+      sb = pa.slot_off[b];
+      se = pa.slot_off[b + 1];
+    }
+    U = (we - wb) / p.num_kv_heads;
+    const int local = lin - wb;
+    kvh = local / U;
+    u = local % U;
+    head_slots = (se - sb) / p.num_kv_heads;
+    slot0 = sb + kvh * head_slots;
+  } else {
+    U = p.units_per_head;
+    u = lin % U;
+    kvh = (lin / U) % p.num_kv_heads;
+    b = lin / (U * p.num_kv_heads);
+    head_slots = p.slots_per_head;
+    slot0 = (b * p.num_kv_heads + kvh) * head_slots;
+  }
+  const int max_chunks = (!BF16_ONLY && PACKED) ? U - p.n_bf16_units : p.max_chunks;
   const int hq = p.num_kv_heads * GQA;
 
   // Loads that do not depend on the sequence length are issued before its
@@ -797,7 +856,7 @@ __global__ void __launch_bounds__(kThreads)
     end = (u == chunks - 1) ? npages : min(first + p.pages_per_chunk, npages);
   } else {
     const int own_pages = max(hist_pages - S_u, 0);
-    const int chunks = min((own_pages + p.pages_per_chunk - 1) / p.pages_per_chunk, p.max_chunks);
+    const int chunks = min((own_pages + p.pages_per_chunk - 1) / p.pages_per_chunk, max_chunks);
     total = p.n_bf16_units + chunks;
     if (u < p.n_bf16_units) {
       const int nlist = n_sp + n_rp;
@@ -1093,8 +1152,7 @@ __global__ void __launch_bounds__(kThreads)
 
   // ---- merge the waves' partials into this workgroup's partial
   const size_t head_base = (size_t)b * p.num_kv_heads + kvh;
-  const int US = p.slots_per_head;
-  const size_t pidx = (head_base * US + u) * GQA;
+  const size_t pidx = ((size_t)slot0 + u) * GQA;
   for (int idx = tid; idx < GQA * D; idx += kThreads) {
     const int h = idx / D, c = idx % D;
     float mx = -INFINITY;
@@ -1137,7 +1195,7 @@ __global__ void __launch_bounds__(kThreads)
   }
   __syncthreads();
   if (!sm.last) return;
-  const size_t p0 = head_base * US * GQA;
+  const size_t p0 = (size_t)slot0 * GQA;
   // Folds partials u0 .. u1-1 of head h, channel c into (M, S, A): the log2
   // max, the sum of weights and the weighted sum of normalized outputs.  h
   // is the same in all 64 lanes of a wave (a wave covers 64 channels of one
@@ -1152,7 +1210,7 @@ __global__ void __launch_bounds__(kThreads)
     const int h = __builtin_amdgcn_readfirstlane(h_lane);
     const float* lsrc = p.part_lse + p0 + h;  // partial u at lsrc[u * GQA]
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.part_o + (p0 + h) * D), (short)0, (US * GQA - h) * D * 4, kBufferFlags);
+        (void*)(p.part_o + (p0 + h) * D), (short)0, (head_slots * GQA - h) * D * 4, kBufferFlags);
     M = -INFINITY;
     S = 0.f;
     A = 0.f;
@@ -1373,8 +1431,8 @@ __device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores
   }
 }
 
-template <int D, int NG, int GQA, bool LUT>
-__global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p) {
+template <int D, int NG, int GQA, bool LUT, bool PACKED>
+__global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p, const PlanArg<PACKED> pa) {
   constexpr int KW = D / 64, G = D / NG, BLK2 = 8 * D + 128 * NG;
   constexpr int MEMBERS = 16 / GQA;  // member sequences per unit (columns = members x heads)
   __shared__ PSmem<D, NG> sm;
@@ -1391,23 +1449,34 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
   const int kvh = rem / cu.chunks, c = rem % cu.chunks;
   const int hq = p.num_kv_heads * GQA;
   const int mcol = n / GQA, hcol = n % GQA;  // this lane's column: member, head
-  const int US = p.slots_per_head;
-
-  // member histories (the same clamps as the decode launch)
-  int hist_len_m[MEMBERS], own_chunks_m[MEMBERS];
+  // member histories (the same clamps as the decode launch) and each
+  // member's first partial slot for this KV head (slot_m) in the decode
+  // launch's layout
+  int hist_len_m[MEMBERS], own_chunks_m[MEMBERS], slot_m[MEMBERS];
   int valid_len = 0, src = cu.first;
 #pragma unroll
   for (int m = 0; m < MEMBERS; ++m) {
     hist_len_m[m] = 0;
     own_chunks_m[m] = 0;
+    slot_m[m] = 0;
     if (m < cu.count) {
+      const int sb = cu.first + m;
+      int mc = p.max_chunks;
+      if constexpr (PACKED) {
+        const int um = (pa.wg_off[sb + 1] - pa.wg_off[sb]) / p.num_kv_heads;
+        const int sm_ = (pa.slot_off[sb + 1] - pa.slot_off[sb]) / p.num_kv_heads;
+        mc = um - p.n_bf16_units;
+        slot_m[m] = pa.slot_off[sb] + kvh * sm_;
+      } else {
+        slot_m[m] = (sb * p.num_kv_heads + kvh) * p.slots_per_head;
+      }
       int L = min(max(p.seq_lens[cu.first + m], 0), p.max_len);
       L = min(L, kPage * p.bf16_pt_stride);
       L = min(L, p.sink + p.recent + kPage * p.int2_pt_stride);
       const int hl = max(p.sink, L - p.recent) - p.sink;
       const int hp = (hl + kPage - 1) / kPage;
       hist_len_m[m] = min(hl, kPage * cu.shared_pages);
-      own_chunks_m[m] = min((max(hp - cu.shared_pages, 0) + p.pages_per_chunk - 1) / p.pages_per_chunk, p.max_chunks);
+      own_chunks_m[m] = min((max(hp - cu.shared_pages, 0) + p.pages_per_chunk - 1) / p.pages_per_chunk, mc);
       if (hist_len_m[m] > valid_len) {
         valid_len = hist_len_m[m];
         src = cu.first + m;
@@ -1652,23 +1721,36 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
       o = so / sw;
       lse = mx + __log2f(sw);
     }
-    int oc = 0;
+    int oc = 0, s0 = 0;
 #pragma unroll
     for (int mm = 0; mm < MEMBERS; ++mm)
-      if (mm == m) oc = own_chunks_m[mm];
-    const size_t head_base = (size_t)(cu.first + m) * p.num_kv_heads + kvh;
-    const size_t pidx = (head_base * US + p.n_bf16_units + oc + c) * GQA + h;
+      if (mm == m) {
+        oc = own_chunks_m[mm];
+        s0 = slot_m[mm];
+      }
+    const size_t pidx = ((size_t)s0 + p.n_bf16_units + oc + c) * GQA + h;
     p.part_o[pidx * D + ch] = o;
     if (ch == 0) p.part_lse[pidx] = lse;
   }
 }
 
 template <int D, int NG, int GQA>
-bool launch_prefix_t(const DecodeParams& p, int grid, hipStream_t stream) {
+bool launch_prefix_t(const DecodeParams& p, const PackedPlanArgs* packed, int grid, hipStream_t stream) {
+  auto go = [&](auto lut) {
+    constexpr bool L = decltype(lut)::value;
+    if (packed) {
+      PlanArg<true> pa;
+      static_cast<PackedPlanArgs&>(pa) = *packed;
+      hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, L, true>), dim3(grid), dim3(kThreads), 0, stream, p, pa);
+    } else {
+      hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, L, false>), dim3(grid), dim3(kThreads), 0, stream, p,
+                         PlanArg<false>{});
+    }
+  };
   if (p.lut)
-    hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    go(std::true_type{});
   else
-    hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    go(std::false_type{});
   return true;
 }
 
@@ -1699,36 +1781,47 @@ __global__ void __launch_bounds__(256) k_merge(const MergeParams p) {
 }
 
 // the INT2 decode, with the prefix-unit bookkeeping compiled in only when
-// the call has prefix units (CASC) and the codebook operands only for a
-// codebook pool (LUT)
+// the call has prefix units (CASC), the codebook operands only for a
+// codebook pool (LUT) and the plan tables only for a length-aware plan
 template <int D, int NG, int GQA, bool CASC>
-void launch_int2_t(const DecodeParams& p, int grid, hipStream_t stream) {
+void launch_int2_t(const DecodeParams& p, const PackedPlanArgs* packed, int grid, hipStream_t stream) {
+  auto go = [&](auto lut) {
+    constexpr bool L = decltype(lut)::value;
+    if (packed) {
+      PlanArg<true> pa;
+      static_cast<PackedPlanArgs&>(pa) = *packed;
+      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, true>), dim3(grid), dim3(kThreads), 0, stream, p,
+                         p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, pa);
+    } else {
+      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, false>), dim3(grid), dim3(kThreads), 0, stream, p,
+                         p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, PlanArg<false>{});
+    }
+  };
   if (p.lut)
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, false, true, CASC>), dim3(grid), dim3(kThreads), 0, stream, p,
-                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+    go(std::true_type{});
   else
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, false, false, CASC>), dim3(grid), dim3(kThreads), 0, stream, p,
-                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+    go(std::false_type{});
 }
 
 template <int D, int NG, int GQA>
-bool launch_decode_t(const DecodeParams& p, bool bf16_only, int grid, hipStream_t stream) {
+bool launch_decode_t(const DecodeParams& p, const PackedPlanArgs* packed, bool bf16_only, int grid,
+                     hipStream_t stream) {
   if (bf16_only)
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, true, false, false>), dim3(grid), dim3(kThreads), 0, stream, p,
-                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k);
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, true, false, false, false>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, PlanArg<false>{});
   else if (p.n_casc > 0)
-    launch_int2_t<D, NG, GQA, true>(p, grid, stream);
+    launch_int2_t<D, NG, GQA, true>(p, packed, grid, stream);
   else
-    launch_int2_t<D, NG, GQA, false>(p, grid, stream);
+    launch_int2_t<D, NG, GQA, false>(p, packed, grid, stream);
   return true;
 }
 
 }  // namespace
 
-bool launch_decode(const DecodeParams& p, int head_dim, int n_groups, int gqa, bool bf16_only, int grid,
-                   hipStream_t stream) {
+bool launch_decode(const DecodeParams& p, const PackedPlanArgs* packed, int head_dim, int n_groups, int gqa,
+                   bool bf16_only, int grid, hipStream_t stream) {
 #define OSCAR_DEC(D, NG, G) \
-  if (head_dim == D && n_groups == NG && gqa == G) return launch_decode_t<D, NG, G>(p, bf16_only, grid, stream);
+  if (head_dim == D && n_groups == NG && gqa == G) return launch_decode_t<D, NG, G>(p, packed, bf16_only, grid, stream);
   OSCAR_DEC(128, 1, 2)
   OSCAR_DEC(128, 1, 4)
   OSCAR_DEC(128, 1, 8)
@@ -1742,10 +1835,11 @@ bool launch_decode(const DecodeParams& p, int head_dim, int n_groups, int gqa, b
   return false;
 }
 
-bool launch_decode_prefix(const DecodeParams& p, int head_dim, int n_groups, int gqa, int grid, hipStream_t stream) {
+bool launch_decode_prefix(const DecodeParams& p, const PackedPlanArgs* packed, int head_dim, int n_groups, int gqa,
+                          int grid, hipStream_t stream) {
   if (grid <= 0) return true;
 #define OSCAR_PRE(D, NG, G) \
-  if (head_dim == D && n_groups == NG && gqa == G) return launch_prefix_t<D, NG, G>(p, grid, stream);
+  if (head_dim == D && n_groups == NG && gqa == G) return launch_prefix_t<D, NG, G>(p, packed, grid, stream);
   OSCAR_PRE(128, 1, 2)
   OSCAR_PRE(128, 1, 4)
   OSCAR_PRE(128, 1, 8)

@@ -25,6 +25,10 @@ struct CascUnit {
   int32_t wg_start;          // first prefix workgroup of the unit
 };
 
+// Length-aware ("packed") split-K plans are passed in the kernel arguments
+// for batches of up to this many sequences.
+constexpr int kMaxPackedSeqs = 128;
+
 struct DecodeParams {
   const uint16_t* q;         // [B][Hq][D] bf16
   const int32_t* seq_lens;   // [B]
@@ -56,11 +60,25 @@ struct DecodeParams {
   CascUnit casc[kMaxCascUnits];
 };
 
+// The length-aware plan's tables, a separate kernel argument of the packed
+// kernel instantiations only (the plain launch keeps its small argument
+// block).  Sequence b owns workgroups [wg_off[b], wg_off[b+1])
+// (num_kv_heads x its units, KV head major) and partial slots
+// [slot_off[b], slot_off[b+1]) (num_kv_heads x its slots: its units, then its
+// prefix chunks).  Without it every (sequence, KV head) has units_per_head
+// workgroups and slots_per_head slots.
+struct PackedPlanArgs {
+  int32_t wg_off[kMaxPackedSeqs + 1];
+  int32_t slot_off[kMaxPackedSeqs + 1];
+};
+
 // Returns false if the (head_dim, n_groups, gqa) combination has no kernel.
-bool launch_decode(const DecodeParams& p, int head_dim, int n_groups, int gqa, bool bf16_only, int grid,
-                   hipStream_t stream);
+// packed: the length-aware plan's tables (null: the uniform plan).
+bool launch_decode(const DecodeParams& p, const PackedPlanArgs* packed, int head_dim, int n_groups, int gqa,
+                   bool bf16_only, int grid, hipStream_t stream);
 // The prefix workgroups of p.casc (grid = sum of Hkv * chunks over units).
-bool launch_decode_prefix(const DecodeParams& p, int head_dim, int n_groups, int gqa, int grid, hipStream_t stream);
+bool launch_decode_prefix(const DecodeParams& p, const PackedPlanArgs* packed, int head_dim, int n_groups, int gqa,
+                          int grid, hipStream_t stream);
 
 struct MergeParams {
   int32_t rows, head_dim;

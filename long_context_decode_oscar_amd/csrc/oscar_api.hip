@@ -237,6 +237,84 @@ Plan cascade_plan(const oscar_pool* pool, int batch, int max_len, const CascPlan
   return pl;
 }
 
+// ---- length-aware ("packed") split-K plan ----
+// With the host-side lengths the planner sizes every sequence's chunks from
+// its own history: one common chunk size ppc (a multiple of the tile, at most
+// 64 * kDecodeWaves pages) is chosen as the smallest that lets all units,
+// BF16 units included, fit in R whole rounds of `target` workgroups, for the
+// smallest R that can hold them.  Sequence b then has n_bf16_units +
+// ceil(own_pages_b / ppc) units per KV head (own pages: its history past a
+// prefix group's shared pages) and those units plus its prefix group's
+// chunks as partial slots.  Returns false (use the uniform plan) for
+// batches above kMaxPackedSeqs.
+struct PackedPlan {
+  int ppc, grid, slots;
+  size_t off_lse, off_o, bytes;
+  int32_t wg_off[oscar::kMaxPackedSeqs + 1];
+  int32_t slot_off[oscar::kMaxPackedSeqs + 1];
+};
+
+bool plan_packed(const oscar_pool* pool, int batch, int max_len, const int32_t* host_lens, int bf16_pt_stride,
+                 int int2_pt_stride, const Plan& base, const CascPlan& cp, PackedPlan* pp) {
+  if (!host_lens || batch <= 0 || batch > oscar::kMaxPackedSeqs) return false;
+  const oscar_config& c = pool->cfg;
+  const int hkv = c.num_kv_heads, slots = slots_for(pool->gqa), nb = base.n_bf16_units;
+  const int target = env_int("OSCAR_TARGET_WGS", num_cus());
+  const int cap = 64 * kDecodeWaves;
+  int own[oscar::kMaxPackedSeqs], cch[oscar::kMaxPackedSeqs];
+  for (int b = 0; b < batch; ++b) {
+    // the kernel's clamps of the length
+    int L = std::min(std::max(host_lens[b], 0), max_len);
+    L = std::min(L, oscar::kPage * bf16_pt_stride);
+    L = std::min(L, c.sink_tokens + c.recent_tokens + oscar::kPage * int2_pt_stride);
+    const int r0 = std::max(c.sink_tokens, L - c.recent_tokens);
+    const int hp = (r0 - c.sink_tokens + oscar::kPage - 1) / oscar::kPage;
+    int shared = 0;
+    cch[b] = 0;
+    for (int i = 0; i < cp.n; ++i)
+      if (b >= cp.units[i].first && b < cp.units[i].first + cp.units[i].count) {
+        shared = cp.units[i].shared_pages;
+        cch[b] = cp.units[i].chunks;
+      }
+    own[b] = std::max(hp - shared, 0);
+  }
+  auto units = [&](int ppc) {
+    long long u = 0;
+    for (int b = 0; b < batch; ++b) u += nb + (own[b] + ppc - 1) / ppc;
+    return u * hkv;
+  };
+  int ppc = -1;
+  for (int r = 1; r <= 64 && ppc < 0; ++r) {
+    const long long budget = (long long)r * target;
+    if (units(cap) > budget) continue;
+    int lo = 1, hi = cap / slots;  // smallest k with units(k * slots) <= budget
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (units(mid * slots) <= budget)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    ppc = lo * slots;
+  }
+  if (ppc < 0) return false;
+  pp->ppc = ppc;
+  pp->wg_off[0] = pp->slot_off[0] = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int ub = nb + (own[b] + ppc - 1) / ppc;
+    pp->wg_off[b + 1] = pp->wg_off[b] + hkv * ub;
+    pp->slot_off[b + 1] = pp->slot_off[b] + hkv * (ub + cch[b]);
+  }
+  pp->grid = pp->wg_off[batch];
+  pp->slots = pp->slot_off[batch];
+  const size_t heads = (size_t)batch * hkv, parts = (size_t)pp->slots * pool->gqa;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  pp->off_lse = up(heads * oscar::kCounterStride * sizeof(uint32_t));
+  pp->off_o = pp->off_lse + up(parts * sizeof(float));
+  pp->bytes = pp->off_o + up(parts * c.head_dim * sizeof(float));
+  return true;
+}
+
 // ---- calibration helpers ----
 constexpr size_t kSpan = (size_t)1 << 31;
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -465,7 +543,8 @@ static oscar_status check_tables(const int32_t* bf16_pt, int32_t bf16_stride, in
 namespace {
 // Decode with optional prefix groups (num_groups = 0: plain decode, one launch).
 oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
-                         const int32_t* seq_lens, const int32_t* bf16_page_table, int32_t bf16_pt_stride,
+                         const int32_t* seq_lens, const int32_t* seq_lens_host, const int32_t* bf16_page_table,
+                         int32_t bf16_pt_stride,
                          int32_t bf16_num_pages, const int32_t* int2_page_table, int32_t int2_pt_stride,
                          int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool, const float* r_k,
                          const float* r_v, void* out, const oscar_prefix_group* groups, int32_t num_groups,
@@ -488,6 +567,12 @@ oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_
   if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes)
     return fail(OSCAR_ERR_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes", pl.bytes);
+  // the length-aware plan when host lengths are given and its partials fit
+  // the workspace (sized for the uniform plan of max_seq_len)
+  PackedPlan pk;
+  const bool packed = plan_packed(pool, batch, max_seq_len, seq_lens_host, bf16_pt_stride, int2_pt_stride, pl, cp,
+                                  &pk) &&
+                      pk.bytes <= workspace_bytes;
   const oscar_config& c = pool->cfg;
   oscar::DecodeParams p{};
   p.q = (const uint16_t*)q;
@@ -521,13 +606,43 @@ oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_
   set_codebook(pool, p);
   p.n_casc = cp.n;
   for (int i = 0; i < cp.n; ++i) p.casc[i] = cp.units[i];
+  int grid = pl.grid;
+  oscar::PackedPlanArgs tables;
+  const oscar::PackedPlanArgs* tables_arg = nullptr;
+  if (packed) {
+    p.pages_per_chunk = pk.ppc;
+    p.part_lse = (float*)((char*)workspace + pk.off_lse);
+    p.part_o = (float*)((char*)workspace + pk.off_o);
+    grid = pk.grid;
+    // when every sequence has the same units and slots (one sequence, or
+    // equal lengths) the plan is uniform: the kernel then maps workgroups
+    // by arithmetic instead of reading the offset tables
+    const int hkv = c.num_kv_heads;
+    const int u0 = pk.wg_off[1] / hkv, s0 = pk.slot_off[1] / hkv;
+    bool same = true;
+    for (int i = 0; i < batch; ++i)
+      same = same && pk.wg_off[i + 1] - pk.wg_off[i] == hkv * u0 && pk.slot_off[i + 1] - pk.slot_off[i] == hkv * s0;
+    if (same) {
+      p.units_per_head = u0;
+      p.slots_per_head = s0;
+      p.max_chunks = u0 - pl.n_bf16_units;
+    } else {
+      for (int i = 0; i <= batch; ++i) {
+        tables.wg_off[i] = pk.wg_off[i];
+        tables.slot_off[i] = pk.slot_off[i];
+      }
+      for (int i = batch + 1; i <= oscar::kMaxPackedSeqs; ++i) tables.wg_off[i] = tables.slot_off[i] = pk.grid;
+      tables_arg = &tables;
+    }
+  }
   // prefix partials first (same stream): the decode launch's merge reads them
   if (cp.grid > 0) {
-    if (!oscar::launch_decode_prefix(p, c.head_dim, pool->n_groups, pool->gqa, cp.grid, (hipStream_t)stream))
+    if (!oscar::launch_decode_prefix(p, tables_arg, c.head_dim, pool->n_groups, pool->gqa, cp.grid,
+                                     (hipStream_t)stream))
       return fail(OSCAR_ERR_UNSUPPORTED, "no prefix decode kernel for this shape");
     if ((st = check_hip("prefix decode launch")) != OSCAR_OK) return st;
   }
-  if (!oscar::launch_decode(p, c.head_dim, pool->n_groups, pool->gqa, false, pl.grid, (hipStream_t)stream))
+  if (!oscar::launch_decode(p, tables_arg, c.head_dim, pool->n_groups, pool->gqa, false, grid, (hipStream_t)stream))
     return fail(OSCAR_ERR_UNSUPPORTED, "no decode kernel for this shape");
   return check_hip("decode launch");
 }
@@ -536,13 +651,13 @@ oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_
 extern "C" {
 
 oscar_status oscar_decode_attention(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
-                                    const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                    const int32_t* seq_lens, const int32_t* seq_lens_host, const int32_t* bf16_page_table,
                                     int32_t bf16_pt_stride, int32_t bf16_num_pages,
                                     const int32_t* int2_page_table, int32_t int2_pt_stride,
                                     int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
                                     const float* r_k, const float* r_v, void* out, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  return decode_impl(pool, batch, max_seq_len, q, seq_lens, bf16_page_table, bf16_pt_stride, bf16_num_pages,
+  return decode_impl(pool, batch, max_seq_len, q, seq_lens, seq_lens_host, bf16_page_table, bf16_pt_stride, bf16_num_pages,
                      int2_page_table, int2_pt_stride, int2_num_pages, bf16_pool, int2_pool, r_k, r_v, out, nullptr, 0,
                      workspace, workspace_bytes, stream);
 }
@@ -593,7 +708,7 @@ oscar_status current_scratch(hipStream_t stream, void** out) {
 extern "C" {
 
 oscar_status oscar_decode_attention_noalloc(const oscar_pool* pool, int32_t batch, int32_t max_seq_len, const void* q,
-                                            const int32_t* seq_lens, const int32_t* bf16_page_table,
+                                            const int32_t* seq_lens, const int32_t* seq_lens_host, const int32_t* bf16_page_table,
                                             int32_t bf16_pt_stride, int32_t bf16_num_pages,
                                             const int32_t* int2_page_table, int32_t int2_pt_stride,
                                             int32_t int2_num_pages, const void* bf16_pool, const void* int2_pool,
@@ -611,7 +726,7 @@ oscar_status oscar_decode_attention_noalloc(const oscar_pool* pool, int32_t batc
   void* ws = nullptr;
   const oscar_status st = current_scratch((hipStream_t)stream, &ws);
   if (st != OSCAR_OK) return st;
-  return decode_impl(pool, batch, max_seq_len, q, seq_lens, bf16_page_table, bf16_pt_stride, bf16_num_pages,
+  return decode_impl(pool, batch, max_seq_len, q, seq_lens, seq_lens_host, bf16_page_table, bf16_pt_stride, bf16_num_pages,
                      int2_page_table, int2_pt_stride, int2_num_pages, bf16_pool, int2_pool, r_k, r_v, out, nullptr, 0,
                      ws, OSCAR_NOALLOC_SCRATCH_BYTES, stream);
 }
@@ -635,14 +750,14 @@ oscar_status oscar_decode_cascade_workspace_bytes(const oscar_pool* pool, int32_
 }
 
 oscar_status oscar_decode_attention_cascade(const oscar_pool* pool, int32_t batch, int32_t max_seq_len,
-                                            const void* q, const int32_t* seq_lens,
+                                            const void* q, const int32_t* seq_lens, const int32_t* seq_lens_host,
                                             const int32_t* bf16_page_table, int32_t bf16_pt_stride,
                                             int32_t bf16_num_pages, const int32_t* int2_page_table,
                                             int32_t int2_pt_stride, int32_t int2_num_pages, const void* bf16_pool,
                                             const void* int2_pool, const float* r_k, const float* r_v, void* out,
                                             const oscar_prefix_group* groups, int32_t num_groups, void* workspace,
                                             size_t workspace_bytes, void* stream) {
-  return decode_impl(pool, batch, max_seq_len, q, seq_lens, bf16_page_table, bf16_pt_stride, bf16_num_pages,
+  return decode_impl(pool, batch, max_seq_len, q, seq_lens, seq_lens_host, bf16_page_table, bf16_pt_stride, bf16_num_pages,
                      int2_page_table, int2_pt_stride, int2_num_pages, bf16_pool, int2_pool, r_k, r_v, out, groups,
                      num_groups, workspace, workspace_bytes, stream);
 }
@@ -688,7 +803,7 @@ oscar_status oscar_bf16_decode_attention(const oscar_pool* pool, int32_t batch, 
   p.units_per_head = pl.units;
   p.slots_per_head = pl.slots;
   p.sm_log2 = pool->sm_scale * 1.4426950408889634f;
-  if (!oscar::launch_decode(p, c.head_dim, pool->n_groups, pool->gqa, true, pl.grid, (hipStream_t)stream))
+  if (!oscar::launch_decode(p, nullptr, c.head_dim, pool->n_groups, pool->gqa, true, pl.grid, (hipStream_t)stream))
     return fail(OSCAR_ERR_UNSUPPORTED, "no decode kernel for this shape");
   return check_hip("bf16 decode launch");
 }

@@ -75,7 +75,7 @@ def _share_tables(pools, seqs, groups):
     return dict(pools, int2_pt=pt)
 
 
-def _run(oscar, wl, seqs, q, pools, r_k, groups, r_v=None):
+def _run(oscar, wl, seqs, q, pools, r_k, groups, r_v=None, host_lens=None):
     pool = oscar.OscarPool(pool_config(wl, v_absorbed=r_v is None))
     dev = upload(pools)
     lens = torch.tensor([s.L for s in seqs], dtype=torch.int32, device="cuda")
@@ -86,7 +86,8 @@ def _run(oscar, wl, seqs, q, pools, r_k, groups, r_v=None):
     log(f"cascade decode: batch={len(seqs)} groups={groups}")
     rv = None if r_v is None else to_dev(r_v)
     oscar.oscar_decode_attention_cascade(pool, q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"],
-                                         dev["bf16_pool"], dev["int2_pool"], to_dev(r_k), out, ws, groups, r_v=rv)
+                                         dev["bf16_pool"], dev["int2_pool"], to_dev(r_k), out, ws, groups, r_v=rv,
+                                         seq_lens_host=host_lens)
     torch.cuda.synchronize()
     return out, (pool, dev, lens, ws, max_len)
 
@@ -197,3 +198,17 @@ def test_cascade_value_range_unclipped(gpu_lib, vscale):
     out, _ = _run(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k, groups)
     ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
     check_decode(out, ref, what=f"cascade, values x{vscale:g}, no value clip")
+
+
+@pytest.mark.parametrize("name", ["d128-gqa8", "d64-gqa2"])
+def test_cascade_host_length_plan(gpu_lib, name):
+    """The prefix-shared decode with the length-aware plan: each member's own
+    chunks and its prefix slots in the per-sequence partial layout."""
+    wl, groups = CASES[name]
+    inp = _prefix_inputs(wl, groups)
+    seqs = make_seqs(wl, inp)
+    pools = _share_tables(pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent,
+                                              seed=wl.seed), seqs, groups)
+    out, _ = _run(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k, groups, host_lens=[s.L for s in seqs])
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
+    check_decode(out, ref, what=f"cascade {name}, host-length plan")

@@ -31,30 +31,59 @@ CASES = {
 }
 
 
-def _decode(oscar, wl, seqs, q, pools, r_k, max_len=None, r_v=None):
+def _decode(oscar, wl, seqs, q, pools, r_k, max_len=None, r_v=None, host_lens=None):
     pool = oscar.OscarPool(pool_config(wl, v_absorbed=r_v is None))
     dev = upload(pools)
     lens = torch.tensor([s.L for s in seqs], dtype=torch.int32, device="cuda")
     max_len = max_len or max(s.L for s in seqs)
     out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
     ws = pool.alloc_workspace(len(seqs), max_len)
-    log(f"decode launch: batch={len(seqs)} max_len={max_len}")
+    log(f"decode launch: batch={len(seqs)} max_len={max_len} host lengths={host_lens is not None}")
     oscar.oscar_decode_attention(pool, q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"], dev["bf16_pool"],
-                                 dev["int2_pool"], to_dev(r_k), out, ws, r_v=None if r_v is None else to_dev(r_v))
+                                 dev["int2_pool"], to_dev(r_k), out, ws, r_v=None if r_v is None else to_dev(r_v),
+                                 seq_lens_host=host_lens)
     torch.cuda.synchronize()
     return out, (pool, dev, lens, ws, max_len)
 
 
+@pytest.mark.parametrize("plan", ["max-length", "host-lengths"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_decode_matches_oracle(gpu_lib, name):
+def test_decode_matches_oracle(gpu_lib, name, plan):
+    """Both split-K plans: every sequence planned for max_seq_len, and the
+    length-aware plan from the host copy of the lengths."""
     wl = CASES[name]
-    log(f"case {name}: {wl}")
+    log(f"case {name} ({plan} plan): {wl}")
     inp = draw_inputs(wl)
     seqs = make_seqs(wl, inp)
     pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
-    out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
+    host = list(wl.seq_lens) if plan == "host-lengths" else None
+    out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k, host_lens=host)
     ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
-    check_decode(out, ref, what=name)
+    check_decode(out, ref, what=f"{name} ({plan} plan)")
+
+
+def test_decode_host_lengths_longer_than_device(gpu_lib):
+    """Host lengths above the device ones plan more chunks than the device
+    lengths fill: the extra workgroups exit, the ticket counts only real
+    partials, and the result is the decode at the device lengths; repeated
+    calls are bit-identical and leave the tickets at zero."""
+    wl = CASES["d128-gqa4-ragged"]
+    inp = draw_inputs(wl)
+    seqs = make_seqs(wl, inp)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    host = [L + 700 for L in wl.seq_lens]
+    out, (pool, dev, lens, ws, max_len) = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k,
+                                                  max_len=max(host), host_lens=host)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
+    check_decode(out, ref, what="host lengths above device lengths")
+    rk = to_dev(inp.calib.r_k)
+    for _ in range(3):
+        o = torch.zeros_like(out)
+        gpu_lib.oscar_decode_attention(pool, inp.q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"],
+                                       dev["bf16_pool"], dev["int2_pool"], rk, o, ws, seq_lens_host=host)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), out.view(torch.int16))
+    assert int(ws[: 128 * wl.batch * wl.num_kv_heads].view(torch.int32).abs().sum()) == 0
 
 
 def test_decode_empty_sequences_give_zero_rows(gpu_lib):

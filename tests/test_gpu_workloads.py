@@ -157,8 +157,20 @@ def test_mixed_prefix_gqa8_full_size_sampled(gpu_lib):
                                            dev["int2_pt"], dev["bf16_pool"], dev["int2_pool"], r_k, out_c, cws,
                                            groups)
     torch.cuda.synchronize()
+    # both paths again with the length-aware plan (host copy of the lengths),
+    # the launch configuration bench.py times
+    out_h = torch.full(inp.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.oscar_decode_attention(pool, inp.q.contiguous(), lens, max(wl.seq_lens), dev["bf16_pt"], dev["int2_pt"],
+                                   dev["bf16_pool"], dev["int2_pool"], r_k, out_h, ws, seq_lens_host=wl.seq_lens)
+    out_ch = torch.full(inp.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.oscar_decode_attention_cascade(pool, inp.q.contiguous(), lens, max(wl.seq_lens), dev["bf16_pt"],
+                                           dev["int2_pt"], dev["bf16_pool"], dev["int2_pool"], r_k, out_ch, cws,
+                                           groups, seq_lens_host=wl.seq_lens)
+    torch.cuda.synchronize()
     seqs_idx, kv_heads = list(range(8)), [5]
     log(f"oracle write + decode of all 8 sequences, KV head {kv_heads}")
     ref, qh = _oracle(wl, inp, seqs_idx, kv_heads, dev)
     check_decode(out[seqs_idx][:, qh], ref, what="mixed prefix GQA8 (sampled)")
     check_decode(out_c[seqs_idx][:, qh], ref, what="mixed prefix GQA8, cascade (sampled)")
+    check_decode(out_h[seqs_idx][:, qh], ref, what="mixed prefix GQA8, host-length plan (sampled)")
+    check_decode(out_ch[seqs_idx][:, qh], ref, what="mixed prefix GQA8, cascade, host-length plan (sampled)")

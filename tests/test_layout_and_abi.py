@@ -163,23 +163,25 @@ def test_decode_validation_fails_before_launch():
     lib = oscar.load()
     p = oscar.OscarPool(_cfg())
     F = 1 << 20  # fake, aligned, never-dereferenced addresses
-    args = dict(q=F, lens=F, bpt=F, bs=8, bn=4, ipt=F, istr=8, inn=4, bpool=F, ipool=F, rk=F, rv=None, out=F,
-                ws=F, wsb=16, stream=None)
+    host = oscar.HostLengths([1000])
+    args = dict(q=F, lens=F, hlens=None, bpt=F, bs=8, bn=4, ipt=F, istr=8, inn=4, bpool=F, ipool=F, rk=F, rv=None,
+                out=F, ws=F, wsb=16, stream=None)
 
     def call(**kw):
         a = dict(args, **kw)
-        return lib.oscar_decode_attention(p.handle, 1, 1000, a["q"], a["lens"], a["bpt"], a["bs"], a["bn"], a["ipt"],
-                                          a["istr"], a["inn"], a["bpool"], a["ipool"], a["rk"], a["rv"], a["out"],
-                                          a["ws"], a["wsb"], a["stream"])
+        return lib.oscar_decode_attention(p.handle, 1, 1000, a["q"], a["lens"], a["hlens"], a["bpt"], a["bs"],
+                                          a["bn"], a["ipt"], a["istr"], a["inn"], a["bpool"], a["ipool"], a["rk"],
+                                          a["rv"], a["out"], a["ws"], a["wsb"], a["stream"])
     assert call(q=None) == oscar.OSCAR_ERR_INVALID
     assert call(ipool=F + 4) == oscar.OSCAR_ERR_INVALID  # misaligned
     assert call(bs=0) == oscar.OSCAR_ERR_INVALID
     assert call(rv=F) == oscar.OSCAR_ERR_INVALID  # r_v given although V is absorbed
     assert call() == oscar.OSCAR_ERR_WORKSPACE  # 16 bytes is too small
+    assert call(hlens=host.ptr) == oscar.OSCAR_ERR_WORKSPACE  # with host lengths too
     assert call(ws=F + 64, wsb=1 << 30) == oscar.OSCAR_ERR_WORKSPACE  # misaligned workspace
     assert b"workspace" in lib.oscar_last_error()
-    assert lib.oscar_decode_attention(p.handle, 0, 0, None, None, None, 0, 0, None, 0, 0, None, None, None, None,
-                                      None, None, 0, None) == oscar.OSCAR_OK  # empty batch
+    assert lib.oscar_decode_attention(p.handle, 0, 0, None, None, None, None, 0, 0, None, 0, 0, None, None, None,
+                                      None, None, None, 0, None) == oscar.OSCAR_OK  # empty batch
     assert lib.oscar_merge(4, 96, F, F, F, F, None) == oscar.OSCAR_ERR_UNSUPPORTED
     assert lib.oscar_merge(4, 128, None, F, F, F, None) == oscar.OSCAR_ERR_INVALID
     assert lib.oscar_quantize_pack(p.handle, 16, F, F, F, 0, F, F, None, F, F, None) == oscar.OSCAR_ERR_INVALID
@@ -190,8 +192,8 @@ def test_decode_validation_fails_before_launch():
     assert lib.oscar_append_demote(pn.handle, 1, F, F, F, F, 8, 4, F, 8, 4, F, F, F, None, F, F, None) == \
         oscar.OSCAR_ERR_INVALID
     assert lib.oscar_quantize_pack(pn.handle, 16, F, F, F, 4, F, F, None, F, F, None) == oscar.OSCAR_ERR_INVALID
-    assert lib.oscar_decode_attention(pn.handle, 1, 1000, F, F, F, 8, 4, F, 8, 4, F, F, F, None, F, F, 16, None) == \
-        oscar.OSCAR_ERR_INVALID
+    assert lib.oscar_decode_attention(pn.handle, 1, 1000, F, F, None, F, 8, 4, F, 8, 4, F, F, F, None, F, F, 16,
+                                      None) == oscar.OSCAR_ERR_INVALID
     assert lib.oscar_bf16_decode_attention(p.handle, 1, 100, F, F, F, 8, 4, F, F, F, 0, None) == \
         oscar.OSCAR_ERR_WORKSPACE
 
@@ -272,8 +274,8 @@ def test_cascade_validation_fails_before_launch():
     assert ws_bytes([(0, 2, 9000)]) == oscar.OSCAR_ERR_INVALID             # beyond the table
     assert ws_bytes([(0, 66, 10)], batch=66) == oscar.OSCAR_ERR_UNSUPPORTED  # 33 units of 2
     arr, ng = oscar._groups([(0, 4, 100)])
-    assert lib.oscar_decode_attention_cascade(p.handle, 8, 131072, F, F, F, 8, 4, F, 8192, 4, F, F, F, None, F,
+    assert lib.oscar_decode_attention_cascade(p.handle, 8, 131072, F, F, None, F, 8, 4, F, 8192, 4, F, F, F, None, F,
                                               ctypes.cast(arr, ctypes.c_void_p), ng, F, 16, None) == \
         oscar.OSCAR_ERR_WORKSPACE
-    assert lib.oscar_decode_attention_cascade(p.handle, 8, 131072, F, F, F, 8, 4, F, 8192, 4, F, F, F, None, F,
+    assert lib.oscar_decode_attention_cascade(p.handle, 8, 131072, F, F, None, F, 8, 4, F, 8192, 4, F, F, F, None, F,
                                               None, 2, F, 1 << 30, None) == oscar.OSCAR_ERR_INVALID
