@@ -713,13 +713,18 @@ template <bool PACKED>
 struct PlanArg {};
 template <>
 struct PlanArg<true> : PackedPlanArgs {};
+// The prefix-shared units for the CASC instantiations.
+template <bool CASC>
+struct CascArg {};
+template <>
+struct CascArg<true> : CascArgs {};
 
 template <int D, int NG, int GQA, bool BF16_ONLY, bool LUT, bool CASC, bool PACKED>
 __global__ void __launch_bounds__(kThreads)
     k_decode(const DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ bf16_pt_all,
              const int32_t* __restrict__ int2_pt_all, const uint8_t* __restrict__ bf16_pool,
              const uint8_t* __restrict__ int2_pool, const uint16_t* __restrict__ qin, const float* __restrict__ r_k,
-             const PlanArg<PACKED> pa) {
+             const CascArg<CASC> ca, const PlanArg<PACKED> pa) {
   using C = DC<D, NG, GQA>;
   __shared__ Smem<D, GQA> sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -794,9 +799,9 @@ __global__ void __launch_bounds__(kThreads)
   int S_u = 0, cch = 0;
   if constexpr (CASC) {
     for (int i = 0; i < p.n_casc; ++i)
-      if (b >= p.casc[i].first && b < p.casc[i].first + p.casc[i].count) {
-        S_u = p.casc[i].shared_pages;
-        cch = p.casc[i].chunks;
+      if (b >= ca.unit[i].first && b < ca.unit[i].first + ca.unit[i].count) {
+        S_u = ca.unit[i].shared_pages;
+        cch = ca.unit[i].chunks;
       }
   }
   constexpr int TPB = 64 / C::SLOTS;  // tiles whose page ids one VGPR holds
@@ -1432,7 +1437,8 @@ __device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores
 }
 
 template <int D, int NG, int GQA, bool LUT, bool PACKED>
-__global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p, const PlanArg<PACKED> pa) {
+__global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p, const CascArgs ca,
+                                                            const PlanArg<PACKED> pa) {
   constexpr int KW = D / 64, G = D / NG, BLK2 = 8 * D + 128 * NG;
   constexpr int MEMBERS = 16 / GQA;  // member sequences per unit (columns = members x heads)
   __shared__ PSmem<D, NG> sm;
@@ -1443,8 +1449,8 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
   // which unit, KV head and chunk
   int ui = 0;
   for (int i = 1; i < p.n_casc; ++i)
-    if (lin >= p.casc[i].wg_start) ui = i;
-  const CascUnit cu = p.casc[ui];
+    if (lin >= ca.unit[i].wg_start) ui = i;
+  const CascUnit cu = ca.unit[ui];
   const int rem = lin - cu.wg_start;
   const int kvh = rem / cu.chunks, c = rem % cu.chunks;
   const int hq = p.num_kv_heads * GQA;
@@ -1735,15 +1741,17 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
 }
 
 template <int D, int NG, int GQA>
-bool launch_prefix_t(const DecodeParams& p, const PackedPlanArgs* packed, int grid, hipStream_t stream) {
+bool launch_prefix_t(const DecodeParams& p, const CascArgs& casc, const PackedPlanArgs* packed, int grid,
+                     hipStream_t stream) {
   auto go = [&](auto lut) {
     constexpr bool L = decltype(lut)::value;
     if (packed) {
       PlanArg<true> pa;
       static_cast<PackedPlanArgs&>(pa) = *packed;
-      hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, L, true>), dim3(grid), dim3(kThreads), 0, stream, p, pa);
+      hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, L, true>), dim3(grid), dim3(kThreads), 0, stream, p, casc,
+                         pa);
     } else {
-      hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, L, false>), dim3(grid), dim3(kThreads), 0, stream, p,
+      hipLaunchKernelGGL((k_decode_prefix<D, NG, GQA, L, false>), dim3(grid), dim3(kThreads), 0, stream, p, casc,
                          PlanArg<false>{});
     }
   };
@@ -1784,17 +1792,21 @@ __global__ void __launch_bounds__(256) k_merge(const MergeParams p) {
 // the call has prefix units (CASC), the codebook operands only for a
 // codebook pool (LUT) and the plan tables only for a length-aware plan
 template <int D, int NG, int GQA, bool CASC>
-void launch_int2_t(const DecodeParams& p, const PackedPlanArgs* packed, int grid, hipStream_t stream) {
+void launch_int2_t(const DecodeParams& p, const CascArgs* casc, const PackedPlanArgs* packed, int grid,
+                   hipStream_t stream) {
+  CascArg<CASC> ca;
+  if constexpr (CASC) static_cast<CascArgs&>(ca) = *casc;
   auto go = [&](auto lut) {
     constexpr bool L = decltype(lut)::value;
     if (packed) {
       PlanArg<true> pa;
       static_cast<PackedPlanArgs&>(pa) = *packed;
       hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, true>), dim3(grid), dim3(kThreads), 0, stream, p,
-                         p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, pa);
+                         p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, ca, pa);
     } else {
       hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, false>), dim3(grid), dim3(kThreads), 0, stream, p,
-                         p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, PlanArg<false>{});
+                         p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, ca,
+                         PlanArg<false>{});
     }
   };
   if (p.lut)
@@ -1804,24 +1816,27 @@ void launch_int2_t(const DecodeParams& p, const PackedPlanArgs* packed, int grid
 }
 
 template <int D, int NG, int GQA>
-bool launch_decode_t(const DecodeParams& p, const PackedPlanArgs* packed, bool bf16_only, int grid,
-                     hipStream_t stream) {
+bool launch_decode_t(const DecodeParams& p, const CascArgs* casc, const PackedPlanArgs* packed, bool bf16_only,
+                     int grid, hipStream_t stream) {
   if (bf16_only)
     hipLaunchKernelGGL((k_decode<D, NG, GQA, true, false, false, false>), dim3(grid), dim3(kThreads), 0, stream, p,
-                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, PlanArg<false>{});
+                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, CascArg<false>{},
+                       PlanArg<false>{});
   else if (p.n_casc > 0)
-    launch_int2_t<D, NG, GQA, true>(p, packed, grid, stream);
+    launch_int2_t<D, NG, GQA, true>(p, casc, packed, grid, stream);
   else
-    launch_int2_t<D, NG, GQA, false>(p, packed, grid, stream);
+    launch_int2_t<D, NG, GQA, false>(p, nullptr, packed, grid, stream);
   return true;
 }
 
 }  // namespace
 
-bool launch_decode(const DecodeParams& p, const PackedPlanArgs* packed, int head_dim, int n_groups, int gqa,
-                   bool bf16_only, int grid, hipStream_t stream) {
-#define OSCAR_DEC(D, NG, G) \
-  if (head_dim == D && n_groups == NG && gqa == G) return launch_decode_t<D, NG, G>(p, packed, bf16_only, grid, stream);
+bool launch_decode(const DecodeParams& p, const CascArgs* casc, const PackedPlanArgs* packed, int head_dim,
+                   int n_groups, int gqa, bool bf16_only, int grid, hipStream_t stream) {
+  if (p.n_casc > 0 && !casc) return false;
+#define OSCAR_DEC(D, NG, G)                        \
+  if (head_dim == D && n_groups == NG && gqa == G) \
+    return launch_decode_t<D, NG, G>(p, casc, packed, bf16_only, grid, stream);
   OSCAR_DEC(128, 1, 2)
   OSCAR_DEC(128, 1, 4)
   OSCAR_DEC(128, 1, 8)
@@ -1835,11 +1850,12 @@ bool launch_decode(const DecodeParams& p, const PackedPlanArgs* packed, int head
   return false;
 }
 
-bool launch_decode_prefix(const DecodeParams& p, const PackedPlanArgs* packed, int head_dim, int n_groups, int gqa,
-                          int grid, hipStream_t stream) {
+bool launch_decode_prefix(const DecodeParams& p, const CascArgs& casc, const PackedPlanArgs* packed, int head_dim,
+                          int n_groups, int gqa, int grid, hipStream_t stream) {
   if (grid <= 0) return true;
-#define OSCAR_PRE(D, NG, G) \
-  if (head_dim == D && n_groups == NG && gqa == G) return launch_prefix_t<D, NG, G>(p, packed, grid, stream);
+#define OSCAR_PRE(D, NG, G)                        \
+  if (head_dim == D && n_groups == NG && gqa == G) \
+    return launch_prefix_t<D, NG, G>(p, casc, packed, grid, stream);
   OSCAR_PRE(128, 1, 2)
   OSCAR_PRE(128, 1, 4)
   OSCAR_PRE(128, 1, 8)

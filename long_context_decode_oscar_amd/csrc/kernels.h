@@ -57,7 +57,13 @@ struct DecodeParams {
   uint32_t lut_k;            // byte c: 32 L_K[c] (int8 score operand of code c)
   uint32_t lut_v;            // byte c: 64 L_V[c] (mantissa of the fp16 operand 16 + L_V[c])
   int32_t n_casc;            // prefix-shared units (0: plain decode)
-  CascUnit casc[kMaxCascUnits];
+};
+
+// The prefix-shared units of a decode with prefix groups: a separate kernel
+// argument of the instantiations that take prefix groups (the plain launch
+// keeps its argument block small: each launch copies it).
+struct CascArgs {
+  CascUnit unit[kMaxCascUnits];
 };
 
 // The length-aware plan's tables, a separate kernel argument of the packed
@@ -74,11 +80,13 @@ struct PackedPlanArgs {
 
 // Returns false if the (head_dim, n_groups, gqa) combination has no kernel.
 // packed: the length-aware plan's tables (null: the uniform plan).
-bool launch_decode(const DecodeParams& p, const PackedPlanArgs* packed, int head_dim, int n_groups, int gqa,
-                   bool bf16_only, int grid, hipStream_t stream);
-// The prefix workgroups of p.casc (grid = sum of Hkv * chunks over units).
-bool launch_decode_prefix(const DecodeParams& p, const PackedPlanArgs* packed, int head_dim, int n_groups, int gqa,
-                          int grid, hipStream_t stream);
+// casc: the prefix-shared units (p.n_casc of them; null when p.n_casc = 0).
+bool launch_decode(const DecodeParams& p, const CascArgs* casc, const PackedPlanArgs* packed, int head_dim,
+                   int n_groups, int gqa, bool bf16_only, int grid, hipStream_t stream);
+// The prefix workgroups of the units in casc (grid = sum of Hkv * chunks
+// over units).
+bool launch_decode_prefix(const DecodeParams& p, const CascArgs& casc, const PackedPlanArgs* packed, int head_dim,
+                          int n_groups, int gqa, int grid, hipStream_t stream);
 
 struct MergeParams {
   int32_t rows, head_dim;

@@ -605,7 +605,8 @@ oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_
   p.sm_log2 = pool->sm_scale * 1.4426950408889634f;
   set_codebook(pool, p);
   p.n_casc = cp.n;
-  for (int i = 0; i < cp.n; ++i) p.casc[i] = cp.units[i];
+  oscar::CascArgs casc{};
+  for (int i = 0; i < cp.n; ++i) casc.unit[i] = cp.units[i];
   int grid = pl.grid;
   oscar::PackedPlanArgs tables;
   const oscar::PackedPlanArgs* tables_arg = nullptr;
@@ -637,12 +638,13 @@ oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_
   }
   // prefix partials first (same stream): the decode launch's merge reads them
   if (cp.grid > 0) {
-    if (!oscar::launch_decode_prefix(p, tables_arg, c.head_dim, pool->n_groups, pool->gqa, cp.grid,
+    if (!oscar::launch_decode_prefix(p, casc, tables_arg, c.head_dim, pool->n_groups, pool->gqa, cp.grid,
                                      (hipStream_t)stream))
       return fail(OSCAR_ERR_UNSUPPORTED, "no prefix decode kernel for this shape");
     if ((st = check_hip("prefix decode launch")) != OSCAR_OK) return st;
   }
-  if (!oscar::launch_decode(p, tables_arg, c.head_dim, pool->n_groups, pool->gqa, false, grid, (hipStream_t)stream))
+  if (!oscar::launch_decode(p, cp.n > 0 ? &casc : nullptr, tables_arg, c.head_dim, pool->n_groups, pool->gqa, false,
+                            grid, (hipStream_t)stream))
     return fail(OSCAR_ERR_UNSUPPORTED, "no decode kernel for this shape");
   return check_hip("decode launch");
 }
@@ -803,7 +805,8 @@ oscar_status oscar_bf16_decode_attention(const oscar_pool* pool, int32_t batch, 
   p.units_per_head = pl.units;
   p.slots_per_head = pl.slots;
   p.sm_log2 = pool->sm_scale * 1.4426950408889634f;
-  if (!oscar::launch_decode(p, nullptr, c.head_dim, pool->n_groups, pool->gqa, true, pl.grid, (hipStream_t)stream))
+  if (!oscar::launch_decode(p, nullptr, nullptr, c.head_dim, pool->n_groups, pool->gqa, true, pl.grid,
+                            (hipStream_t)stream))
     return fail(OSCAR_ERR_UNSUPPORTED, "no decode kernel for this shape");
   return check_hip("bf16 decode launch");
 }
