@@ -427,23 +427,22 @@ __device__ __forceinline__ float score_int(int sa, int sb, int sc) {
   return (float)(sa * 256 + sb);
 }
 
-// P.V operands from packed value codes, without per-code shifts.  A value
-// word holds, for the lane's 4 tokens 4j+i and 4 channel blocks bb, the code
-// at bits 16*(i&1) + 2*(2*bb + (i>>1)).  One shift by 4*bb - 6 bits puts the
-// codes of tokens i = 0,1 at bits 6-7 of each 16-bit half and those of
-// i = 2,3 at bits 8-9; OR-ing in an fp16 exponent then gives exact fp16
-// values 16 + code (exponent 19) and 4 + code (exponent 17).  The biases 16
-// and 4 are removed through the per-token correction sum Z.
-template <int BB>
-__device__ __forceinline__ uint32_t v_shift(uint32_t x) {
-  if constexpr (BB == 0) return x << 6;
-  if constexpr (BB == 1) return x << 2;
-  if constexpr (BB == 2) return x >> 2;
-  return x >> 6;
-}
-constexpr uint32_t kMaskLo = 0x00C000C0u, kExpLo = 0x4C004C00u;  // tokens i = 0,1: 16 + code
-constexpr uint32_t kMaskHi = 0x03000300u, kExpHi = 0x44004400u;  // tokens i = 2,3: 4 + code
-constexpr float kBiasLo = 16.f, kBiasHi = 4.f;
+// P.V operands from packed value codes as fp16 subnormals.  A value word
+// holds, for the lane's 4 tokens 4j+i and 4 channel blocks bb, the code at
+// bits 16*(i&1) + 2*(2*bb + (i>>1)).  A 2-bit code masked in place at bit p
+// of a 16-bit half (exponent field zero) is the exact fp16 subnormal
+// code * 2^(p-24), and the matrix cores take subnormal operands exactly.
+// Blocks 0 and 1 take their codes from the word itself, blocks 2 and 3 from
+// the word shifted right by 8, so the codes of tokens i = 0,1 sit at
+// p = 4 (bb & 1) and those of i = 2,3 two bits higher; the weights of tokens
+// i = 2,3 enter the B operand divided by 4, and block bb's accumulator holds
+// sum w * code * 2^(4 (bb & 1) - 24), scaled back once in the epilogue.  The
+// zero-point term sum w * z is tracked in Z from the same rounded weights.
+constexpr uint32_t kSubMask = 0x00030003u;  // tokens i = 0,1 of an even block
+constexpr float kHiWeight = 0.25f;           // weight factor of tokens i = 2,3
+// 2^(24 - 4 (cblk & 1)): accumulator of channel block cblk to code units
+__device__ __forceinline__ constexpr float pv_unit_inv(int cblk) { return (cblk & 1) ? 1048576.f : 16777216.f; }
+constexpr float kBiasLut = 16.f;  // codebook operands: 16 + L[code]
 
 // With a codebook every operand is 16 + L[code] (bias 16 for all tokens):
 // the fp16 pattern 0x4C00 | 64 L[code], built by one byte permute per
@@ -457,8 +456,9 @@ __device__ __forceinline__ uint32_t lut_operand(uint32_t x, uint32_t lut_v) {
 
 template <int D, int NG, int W0, bool LUT>
 __device__ __forceinline__ void pv_block_pair(Acc<D, NG>& st, uint32_t x0, uint32_t x1, const v4i (&bw)[NG],
-                                              uint32_t exp_lo, uint32_t exp_hi, uint32_t lut_v) {
+                                              uint32_t lut_v) {
   constexpr int G = D / NG;
+  const uint32_t s0 = x0 >> 8, s1 = x1 >> 8;  // codes of blocks 2 and 3
   // the four channel blocks of this word pair, two pages per MFMA (k = 32)
   auto one = [&](auto bbc) {
     constexpr int BB = decltype(bbc)::value;
@@ -469,9 +469,9 @@ __device__ __forceinline__ void pv_block_pair(Acc<D, NG>& st, uint32_t x0, uint3
       a = v4i{(int)lut_operand<BB, 0>(x0, lut_v), (int)lut_operand<BB, 1>(x0, lut_v),
               (int)lut_operand<BB, 0>(x1, lut_v), (int)lut_operand<BB, 1>(x1, lut_v)};
     } else {
-      const uint32_t y0 = v_shift<BB>(x0), y1 = v_shift<BB>(x1);
-      a = v4i{(int)((y0 & kMaskLo) | exp_lo), (int)((y0 & kMaskHi) | exp_hi), (int)((y1 & kMaskLo) | exp_lo),
-              (int)((y1 & kMaskHi) | exp_hi)};
+      constexpr uint32_t mlo = kSubMask << (4 * (BB & 1)), mhi = mlo << 2;
+      const uint32_t y0 = BB < 2 ? x0 : s0, y1 = BB < 2 ? x1 : s1;
+      a = v4i{(int)(y0 & mlo), (int)(y0 & mhi), (int)(y1 & mlo), (int)(y1 & mhi)};
     }
     st.o[cblk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, bw[g]),
                                                         st.o[cblk], 0, 0, 0);
@@ -524,8 +524,10 @@ __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(lg[i] - st.ref);
   st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  // ---- fp16 weights w = p * s_V per group, and the correction
-  //      Z += sum w * (bias + z) with the rounded weights
+  // ---- fp16 weights w = p * s_V per group (tokens 2, 3 divided by 4
+  //      unless with a codebook), and the correction Z += sum w' * z' with
+  //      the rounded weights w' (z' = 4 z for tokens 2, 3; codebook
+  //      operands: z' = 16 + z)
   I2Weights<D, NG, GQA> W;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -534,7 +536,14 @@ __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, 
     for (int i = 0; i < 4; ++i) {
       const uint32_t sz = t.sc[4 * NG + i * NG + g];
       w[i] = pr[i] * sv[g][i];
-      zb[i] = bf16_hi(sz) + (LUT || i < 2 ? kBiasLo : kBiasHi);
+      if constexpr (LUT) {
+        zb[i] = bf16_hi(sz) + kBiasLut;
+      } else if (i >= 2) {
+        w[i] *= kHiWeight;
+        zb[i] = bf16_hi(sz) * (1.f / kHiWeight);
+      } else {
+        zb[i] = bf16_hi(sz);
+      }
     }
     const h2 w01 = __builtin_convertvector(f2{w[0], w[1]}, h2);
     const h2 w23 = __builtin_convertvector(f2{w[2], w[3]}, h2);
@@ -552,13 +561,12 @@ __device__ __forceinline__ I2Weights<D, NG, GQA> i2_softmax(const I2Tile<D, NG, 
 // P.V of one INT2 tile on the fp16 matrix cores, two pages per MFMA.
 template <int D, int NG, int GQA, bool LUT>
 __device__ __forceinline__ void i2_pv(const I2Tile<D, NG, GQA>& t, const I2Weights<D, NG, GQA>& W, Acc<D, NG>& st,
-                                      uint32_t exp_lo, uint32_t exp_hi, uint32_t lut_v) {
+                                      uint32_t lut_v) {
   using C = DC<D, NG, GQA>;
 #pragma unroll
   for (int pp = 0; pp < C::SLOTS / 2; ++pp) {
-    pv_block_pair<D, NG, 0, LUT>(st, t.vw[2 * pp][0], t.vw[2 * pp + 1][0], W.bw[pp], exp_lo, exp_hi, lut_v);
-    if constexpr (C::KW > 1)
-      pv_block_pair<D, NG, 1, LUT>(st, t.vw[2 * pp][1], t.vw[2 * pp + 1][1], W.bw[pp], exp_lo, exp_hi, lut_v);
+    pv_block_pair<D, NG, 0, LUT>(st, t.vw[2 * pp][0], t.vw[2 * pp + 1][0], W.bw[pp], lut_v);
+    if constexpr (C::KW > 1) pv_block_pair<D, NG, 1, LUT>(st, t.vw[2 * pp][1], t.vw[2 * pp + 1][1], W.bw[pp], lut_v);
   }
 }
 
@@ -667,8 +675,9 @@ __device__ __forceinline__ void b16_compute(const B16Tile<D, GQA>& t, Acc<D, 1>&
 // -------------------------------------------------------- wave epilogue --
 // Reduce a wave's column states to one (o, lse) per query head and store it
 // in sm.part[wave].  INT2: channel of o[cb][i] is cb*16 + 4j + i and the
-// numerator is acc - Z.  BF16: channel (4j + i) * D/16 + cb.
-template <int D, int NG, int GQA, bool INT2>
+// numerator is acc * unit_inv(cb) - Z (codebook: acc - Z).  BF16: channel
+// (4j + i) * D/16 + cb.
+template <int D, int NG, int GQA, bool INT2, bool LUT = false>
 __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, int wave, int lane) {
   constexpr int G = D / NG;
   const int n = lane & 15, j = lane >> 4;
@@ -693,7 +702,8 @@ __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, in
         int c;
         if constexpr (INT2) {
           const int g = (cbk * 16) / G;
-          o = (st.o[cbk][i] - st.Z[g]) * inv;
+          o = (LUT ? st.o[cbk][i] : st.o[cbk][i] * pv_unit_inv(cbk)) - st.Z[g];
+          o *= inv;
           c = cbk * 16 + 4 * j + i;
         } else {
           o = st.o[cbk][i] * inv;
@@ -1009,10 +1019,6 @@ __global__ void __launch_bounds__(kThreads)
     float sig[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) sig[g] = (float)(t3 ? sm.sig3[chd * NG + g] : sm.sig[chd * NG + g]);
-    // fp16 exponent patterns of the P.V operands, held in VGPRs so that each
-    // operand is one and-or (bitop3) of a shifted code word
-    uint32_t exp_lo = kExpLo, exp_hi = kExpHi;
-    asm volatile("" : "+v"(exp_lo), "+v"(exp_hi));
 
     Acc<D, NG> st;
     st.init(true);
@@ -1080,7 +1086,7 @@ __global__ void __launch_bounds__(kThreads)
           __builtin_amdgcn_s_setprio(0);
           S = scores(ring[(r + 1) % R]);
           __builtin_amdgcn_s_setprio(1);
-          i2_pv<D, NG, GQA, LUT>(ring[r], W, st, exp_lo, exp_hi, lut_v);
+          i2_pv<D, NG, GQA, LUT>(ring[r], W, st, lut_v);
           // slots r and r+1 hold arrived data (the loads of r+2 .. r+R-1 may
           // still be in flight and are left alone)
           ring[r].pin();
@@ -1101,7 +1107,7 @@ __global__ void __launch_bounds__(kThreads)
       else
         run(std::false_type{});
     }
-    wave_finish<D, NG, GQA, true>(st, sm, wave, lane);
+    wave_finish<D, NG, GQA, true, LUT>(st, sm, wave, lane);
   } else {
     // ------------------------------------------- BF16 unit (sink + recent)
     constexpr int SB = C::SLOTS_B;
@@ -1423,7 +1429,14 @@ __device__ __forceinline__ void pt_softmax(const PTile<D, NG>& t, const I2Scores
       for (int i = 0; i < 4; ++i) {
         const uint32_t sz = t.sc[s][4 * NG + i * NG + g];
         w[i] = pr[s][i] * bf16_lo(sz);
-        zb[i] = bf16_hi(sz) + (LUT || i < 2 ? kBiasLo : kBiasHi);
+        if constexpr (LUT) {
+          zb[i] = bf16_hi(sz) + kBiasLut;
+        } else if (i >= 2) {
+          w[i] *= kHiWeight;
+          zb[i] = bf16_hi(sz) * (1.f / kHiWeight);
+        } else {
+          zb[i] = bf16_hi(sz);
+        }
       }
       const h2 w01 = __builtin_convertvector(f2{w[0], w[1]}, h2);
       const h2 w23 = __builtin_convertvector(f2{w[2], w[3]}, h2);
@@ -1624,8 +1637,6 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
   float sig[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) sig[g] = (float)(t3 ? sm.sig3[n * NG + g] : sm.sig[n * NG + g]);
-  uint32_t exp_lo = kExpLo, exp_hi = kExpHi;
-  asm volatile("" : "+v"(exp_lo), "+v"(exp_hi));
   v4i bqr[2][KW];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -1672,9 +1683,8 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
         __builtin_amdgcn_s_setprio(0);
         scores(ring[(r + 1) % R], S);
         __builtin_amdgcn_s_setprio(1);
-        pv_block_pair<D, NG, 0, LUT>(st, ring[r].vw[0][0], ring[r].vw[1][0], bw, exp_lo, exp_hi, lut_v);
-        if constexpr (KW > 1)
-          pv_block_pair<D, NG, 1, LUT>(st, ring[r].vw[0][1], ring[r].vw[1][1], bw, exp_lo, exp_hi, lut_v);
+        pv_block_pair<D, NG, 0, LUT>(st, ring[r].vw[0][0], ring[r].vw[1][0], bw, lut_v);
+        if constexpr (KW > 1) pv_block_pair<D, NG, 1, LUT>(st, ring[r].vw[0][1], ring[r].vw[1][1], bw, lut_v);
         ring[r].pin();
         ring[(r + 1) % R].pin();
         ++i;
@@ -1701,7 +1711,8 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int g = (cbk * 16) / G;
-        sm.u.part[wave][n][cbk * 16 + 4 * j + i] = (st.o[cbk][i] - st.Z[g]) * inv;
+        const float acc = LUT ? st.o[cbk][i] : st.o[cbk][i] * pv_unit_inv(cbk);
+        sm.u.part[wave][n][cbk * 16 + 4 * j + i] = (acc - st.Z[g]) * inv;
       }
     if (j == 0) sm.u.part[wave][n][D] = st.l > 0.f ? st.ref + __log2f(st.l) : -INFINITY;
   }
