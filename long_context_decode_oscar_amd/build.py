@@ -32,6 +32,9 @@ def flags():
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",
+        # kernel arguments preloaded into scalar registers at wave launch (the
+        # code object carries the fallback loads for firmware without it)
+        "-mllvm", "-amdgpu-kernarg-preload-count=16",
         f"-I{os.path.join(HERE, '..', 'include')}",
     ]
 

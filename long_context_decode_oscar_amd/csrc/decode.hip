@@ -729,12 +729,17 @@ struct CascArg {};
 template <>
 struct CascArg<true> : CascArgs {};
 
+// The leading scalar arguments are everything the first page-table and R_K
+// requests depend on (16 dwords): the build preloads them into scalar
+// registers at wave launch, so those requests are issued without waiting for
+// the argument block.
 template <int D, int NG, int GQA, bool BF16_ONLY, bool LUT, bool CASC, bool PACKED>
 __global__ void __launch_bounds__(kThreads)
-    k_decode(const DecodeParams p, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ bf16_pt_all,
-             const int32_t* __restrict__ int2_pt_all, const uint8_t* __restrict__ bf16_pool,
-             const uint8_t* __restrict__ int2_pool, const uint16_t* __restrict__ qin, const float* __restrict__ r_k,
-             const CascArg<CASC> ca, const PlanArg<PACKED> pa) {
+    k_decode(const int32_t* __restrict__ int2_pt_all, const float* __restrict__ r_k, const uint16_t* __restrict__ qin,
+             const int32_t* __restrict__ seq_lens, int grid_n, int units_per_head, int num_kv_heads,
+             int n_bf16_units, int pages_per_chunk, int int2_pt_stride, int max_len, int int2_num_pages,
+             const DecodeParams p, const int32_t* __restrict__ bf16_pt_all, const uint8_t* __restrict__ bf16_pool,
+             const uint8_t* __restrict__ int2_pool, const CascArg<CASC> ca, const PlanArg<PACKED> pa) {
   using C = DC<D, NG, GQA>;
   __shared__ Smem<D, GQA> sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -742,7 +747,7 @@ __global__ void __launch_bounds__(kThreads)
   // tile prefetch is never serialized behind a vector-memory wait
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, j = lane >> 4;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int lin = xcd_remap(blockIdx.x, grid_n);
   // this workgroup's (sequence, KV head, unit), its head's units U and
   // partial slots [slot0, slot0 + head_slots)
   int U, u, kvh, b, head_slots, slot0;
@@ -783,22 +788,22 @@ __global__ void __launch_bounds__(kThreads)
       sb = pa.slot_off[b];
       se = pa.slot_off[b + 1];
     }
-    U = (we - wb) / p.num_kv_heads;
+    U = (we - wb) / num_kv_heads;
     const int local = lin - wb;
     kvh = local / U;
     u = local % U;
-    head_slots = (se - sb) / p.num_kv_heads;
+    head_slots = (se - sb) / num_kv_heads;
     slot0 = sb + kvh * head_slots;
   } else {
-    U = p.units_per_head;
+    U = units_per_head;
     u = lin % U;
-    kvh = (lin / U) % p.num_kv_heads;
-    b = lin / (U * p.num_kv_heads);
+    kvh = (lin / U) % num_kv_heads;
+    b = lin / (U * num_kv_heads);
     head_slots = p.slots_per_head;
-    slot0 = (b * p.num_kv_heads + kvh) * head_slots;
+    slot0 = (b * num_kv_heads + kvh) * head_slots;
   }
-  const int max_chunks = (!BF16_ONLY && PACKED) ? U - p.n_bf16_units : p.max_chunks;
-  const int hq = p.num_kv_heads * GQA;
+  const int max_chunks = (!BF16_ONLY && PACKED) ? U - n_bf16_units : p.max_chunks;
+  const int hq = num_kv_heads * GQA;
 
   // Loads that do not depend on the sequence length are issued before its
   // value arrives: for an INT2 chunk the page ids of its planned page range
@@ -817,17 +822,17 @@ __global__ void __launch_bounds__(kThreads)
   constexpr int TPB = 64 / C::SLOTS;  // tiles whose page ids one VGPR holds
   constexpr int CG = D / 4, RS = kThreads / CG, RPS = D / RS;
   const int cg = tid % CG, rs = tid / CG;
-  const bool int2_planned = !BF16_ONLY && u >= p.n_bf16_units;
-  const int c_int2 = u - p.n_bf16_units;
+  const bool int2_planned = !BF16_ONLY && u >= n_bf16_units;
+  const int c_int2 = u - n_bf16_units;
   int pid_raw = -1;
   float4 rr[RPS];
   uint32_t qq[GQA][RPS / 2];
   if (int2_planned) {
     // lane i*SLOTS + s: slot s of this wave's i-th tile, wave + i*kWaves
     const int i = lane / C::SLOTS, s = lane % C::SLOTS;
-    const int lp = S_u + c_int2 * p.pages_per_chunk + (wave + i * kWaves) * C::SLOTS + s;
-    const int pend = min(S_u + (c_int2 + 1) * p.pages_per_chunk, p.int2_pt_stride);
-    if (lp < pend) pid_raw = int2_pt_all[(size_t)b * p.int2_pt_stride + lp];
+    const int lp = S_u + c_int2 * pages_per_chunk + (wave + i * kWaves) * C::SLOTS + s;
+    const int pend = min(S_u + (c_int2 + 1) * pages_per_chunk, int2_pt_stride);
+    if (lp < pend) pid_raw = int2_pt_all[(size_t)b * int2_pt_stride + lp];
     // thread (rs, cg) owns rows [rs*RPS, rs*RPS + RPS) of R_K and output
     // channels 4cg .. 4cg+3 of q' = q R_K
     const float* rbase = r_k + (size_t)kvh * D * D + (size_t)(rs * RPS) * D + 4 * cg;
@@ -849,9 +854,9 @@ __global__ void __launch_bounds__(kThreads)
     }
   }
 
-  int L = min(max(L_in, 0), p.max_len);
+  int L = min(max(L_in, 0), max_len);
   L = min(L, kPage * p.bf16_pt_stride);
-  if (!BF16_ONLY) L = min(L, p.sink + p.recent + kPage * p.int2_pt_stride);
+  if (!BF16_ONLY) L = min(L, p.sink + p.recent + kPage * int2_pt_stride);
   const int r0 = max(p.sink, L - p.recent);
   const int hist_len = BF16_ONLY ? 0 : r0 - p.sink;
   const int hist_pages = (hist_len + kPage - 1) / kPage;
@@ -864,25 +869,25 @@ __global__ void __launch_bounds__(kThreads)
   const int n_rp = r0 < L ? (L + kPage - 1) / kPage - first_rp : 0;
   if (BF16_ONLY) {
     const int npages = (L + kPage - 1) / kPage;
-    const int chunks = max(1, min((npages + p.pages_per_chunk - 1) / p.pages_per_chunk, p.max_chunks));
+    const int chunks = max(1, min((npages + pages_per_chunk - 1) / pages_per_chunk, p.max_chunks));
     total = chunks;
     if (u >= chunks) return;
-    first = u * p.pages_per_chunk;
-    end = (u == chunks - 1) ? npages : min(first + p.pages_per_chunk, npages);
+    first = u * pages_per_chunk;
+    end = (u == chunks - 1) ? npages : min(first + pages_per_chunk, npages);
   } else {
     const int own_pages = max(hist_pages - S_u, 0);
-    const int chunks = min((own_pages + p.pages_per_chunk - 1) / p.pages_per_chunk, max_chunks);
-    total = p.n_bf16_units + chunks;
-    if (u < p.n_bf16_units) {
+    const int chunks = min((own_pages + pages_per_chunk - 1) / pages_per_chunk, max_chunks);
+    total = n_bf16_units + chunks;
+    if (u < n_bf16_units) {
       const int nlist = n_sp + n_rp;
       first = u * p.bf16_pages_per_unit;
-      end = (u == p.n_bf16_units - 1) ? nlist : min(first + p.bf16_pages_per_unit, nlist);
+      end = (u == n_bf16_units - 1) ? nlist : min(first + p.bf16_pages_per_unit, nlist);
     } else {
-      const int c = u - p.n_bf16_units;
+      const int c = u - n_bf16_units;
       if (c >= chunks) return;
       int2_unit = true;
-      first = S_u + c * p.pages_per_chunk;
-      end = (c == chunks - 1) ? hist_pages : min(first + p.pages_per_chunk, hist_pages);
+      first = S_u + c * pages_per_chunk;
+      end = (c == chunks - 1) ? hist_pages : min(first + pages_per_chunk, hist_pages);
     }
   }
 
@@ -894,7 +899,7 @@ __global__ void __launch_bounds__(kThreads)
     const int ntiles = (end - first + C::SLOTS - 1) / C::SLOTS;
     // tiles of this wave (at most TPB: the host bounds the chunk size)
     const int nt_w = wave < ntiles ? min((ntiles - 1 - wave) / kWaves + 1, TPB) : 0;
-    const size_t page_bytes = (size_t)p.num_kv_heads * C::BLK2;
+    const size_t page_bytes = (size_t)num_kv_heads * C::BLK2;
     const uint8_t* __restrict__ hpool = int2_pool + (size_t)kvh * C::BLK2;
     // physical page ids of this wave's tiles wave + i*kWaves: lane i*SLOTS + s
     // holds slot s of tile i, -1 when absent or outside the history
@@ -902,7 +907,7 @@ __global__ void __launch_bounds__(kThreads)
     {
       const int i = lane / C::SLOTS, s = lane % C::SLOTS;
       const int lp = first + (wave + i * kWaves) * C::SLOTS + s;
-      const bool ok = i < nt_w && lp < end && pid_raw >= 0 && pid_raw < p.int2_num_pages;
+      const bool ok = i < nt_w && lp < end && pid_raw >= 0 && pid_raw < int2_num_pages;
       pids = ok ? pid_raw : -1;
     }
 
@@ -1162,7 +1167,7 @@ __global__ void __launch_bounds__(kThreads)
   __syncthreads();
 
   // ---- merge the waves' partials into this workgroup's partial
-  const size_t head_base = (size_t)b * p.num_kv_heads + kvh;
+  const size_t head_base = (size_t)b * num_kv_heads + kvh;
   const size_t pidx = ((size_t)slot0 + u) * GQA;
   for (int idx = tid; idx < GQA * D; idx += kThreads) {
     const int h = idx / D, c = idx % D;
@@ -1268,8 +1273,8 @@ __global__ void __launch_bounds__(kThreads)
       if (idx < GQA * D) {
         const int h = idx / D, c = idx % D;
         float A2;
-        fold(h, c, 0, p.n_bf16_units, M1[k], S1[k], A1[k]);
-        fold(h, c, p.n_bf16_units, total + cch, M2[k], S2[k], A2);
+        fold(h, c, 0, n_bf16_units, M1[k], S1[k], A1[k]);
+        fold(h, c, n_bf16_units, total + cch, M2[k], S2[k], A2);
         a2[h * D + c] = A2;
       }
     }
@@ -1751,6 +1756,11 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
   }
 }
 
+// the leading scalar arguments of k_decode, in order
+#define DECODE_LEAD_ARGS(p, grid)                                                                           \
+  (p).int2_pt, (p).r_k, (p).q, (p).seq_lens, (grid), (p).units_per_head, (p).num_kv_heads, (p).n_bf16_units, \
+      (p).pages_per_chunk, (p).int2_pt_stride, (p).max_len, (p).int2_num_pages
+
 template <int D, int NG, int GQA>
 bool launch_prefix_t(const DecodeParams& p, const CascArgs& casc, const PackedPlanArgs* packed, int grid,
                      hipStream_t stream) {
@@ -1812,11 +1822,9 @@ void launch_int2_t(const DecodeParams& p, const CascArgs* casc, const PackedPlan
     if (packed) {
       PlanArg<true> pa;
       static_cast<PackedPlanArgs&>(pa) = *packed;
-      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, true>), dim3(grid), dim3(kThreads), 0, stream, p,
-                         p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, ca, pa);
+      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, true>), dim3(grid), dim3(kThreads), 0, stream, DECODE_LEAD_ARGS(p, grid), p, p.bf16_pt, p.bf16_pool, p.int2_pool, ca, pa);
     } else {
-      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, false>), dim3(grid), dim3(kThreads), 0, stream, p,
-                         p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, ca,
+      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, false>), dim3(grid), dim3(kThreads), 0, stream, DECODE_LEAD_ARGS(p, grid), p, p.bf16_pt, p.bf16_pool, p.int2_pool, ca,
                          PlanArg<false>{});
     }
   };
@@ -1830,8 +1838,7 @@ template <int D, int NG, int GQA>
 bool launch_decode_t(const DecodeParams& p, const CascArgs* casc, const PackedPlanArgs* packed, bool bf16_only,
                      int grid, hipStream_t stream) {
   if (bf16_only)
-    hipLaunchKernelGGL((k_decode<D, NG, GQA, true, false, false, false>), dim3(grid), dim3(kThreads), 0, stream, p,
-                       p.seq_lens, p.bf16_pt, p.int2_pt, p.bf16_pool, p.int2_pool, p.q, p.r_k, CascArg<false>{},
+    hipLaunchKernelGGL((k_decode<D, NG, GQA, true, false, false, false>), dim3(grid), dim3(kThreads), 0, stream, DECODE_LEAD_ARGS(p, grid), p, p.bf16_pt, p.bf16_pool, p.int2_pool, CascArg<false>{},
                        PlanArg<false>{});
   else if (p.n_casc > 0)
     launch_int2_t<D, NG, GQA, true>(p, casc, packed, grid, stream);
