@@ -100,7 +100,7 @@ def parse():
                     help="only run N eager decode steps over the cold pool copies, then one plain copy of "
                          "--probe-bytes (for rocprofv3 counters); prints no JSON")
     ap.add_argument("--probe-bytes", type=int, default=256 * 2**20)
-    ap.add_argument("--only", default="all", choices=["all", "headline", "bulk", "demote", "mixed", "calib"],
+    ap.add_argument("--only", default="all", choices=["all", "headline", "bulk", "demote", "mixed", "calib", "batch16"],
                     help="run one section only (the JSON line then holds what was measured)")
     return ap.parse_args()
 
@@ -120,7 +120,9 @@ class Decoder:
         self.host_lens = oscar.HostLengths(wl.seq_lens)
         hptr = self.host_lens.ptr if host_lengths else None
         self.args = []
-        for c in copies:
+        # r_k: one tensor for every copy, or one per copy (a layer's own R_K)
+        rks = r_k if isinstance(r_k, (list, tuple)) else [r_k] * len(copies)
+        for c, rk in zip(copies, rks):
             b16, i2 = c["bf16_pool"], c["int2_pool"]
             if bf16_only:
                 self.args.append((pool.handle, wl.batch, max(wl.seq_lens), q.data_ptr(), lens.data_ptr(),
@@ -130,7 +132,7 @@ class Decoder:
                 self.args.append((pool.handle, wl.batch, max(wl.seq_lens), q.data_ptr(), lens.data_ptr(), hptr,
                                   c["bf16_pt"].data_ptr(), c["bf16_pt"].shape[1], b16.shape[0],
                                   c["int2_pt"].data_ptr(), c["int2_pt"].shape[1], i2.shape[0],
-                                  b16.data_ptr(), i2.data_ptr(), r_k.data_ptr(), None,
+                                  b16.data_ptr(), i2.data_ptr(), rk.data_ptr(), None,
                                   out.data_ptr(), ws.data_ptr(), ws.numel()))
         self.fn = lib.oscar_bf16_decode_attention if bf16_only else lib.oscar_decode_attention
         if groups:
@@ -388,6 +390,48 @@ def bench_decode_workload(oscar, name, steps, warmup, repeats, cold_bytes, profi
     return res
 
 
+def bench_batch_comparator(oscar, name, steps, warmup, repeats, cold_bytes, min_bf16_copies=3):
+    """Decode only (no append/demote) of a batched workload, INT2 pool against
+    the BF16-only comparator on the same sequences, both timed like the
+    headline: HIP-graph replay over cold pool copies (the BF16 pools are
+    several GB each, so at least min_bf16_copies of them rotate)."""
+    import torch
+    from synthetic import CONFIGS, draw_inputs
+    wl = CONFIGS[name]
+    kv = wl.kv_bytes()
+    inp = draw_inputs(wl, gpu_calibration(oscar, wl), device="cuda")
+    pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
+                                            wl.sink, wl.recent, 1, 0.0))
+    q = inp.q.contiguous()
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    n2 = max(2, math.ceil(cold_bytes / kv["total"]))
+    copies, r_k = build_pools(oscar, pool, wl, inp, n2, seed=wl.seed + 5)
+    ws = pool.alloc_workspace(wl.batch, max(wl.seq_lens))
+    dec = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws)
+    ms2, _ = time_steps(dec, steps, warmup, repeats, use_graph=True)
+    del dec, copies, ws
+    torch.cuda.empty_cache()
+    n16 = max(min_bf16_copies, math.ceil(cold_bytes / kv["bf16_only_total"]))
+    bcopies, _ = build_pools(oscar, pool, wl, inp, n16, bf16_only=True, seed=wl.seed + 6)
+    bws = pool.alloc_workspace(wl.batch, max(wl.seq_lens), bf16_only=True)
+    bdec = Decoder(oscar, pool, wl, q, lens, bcopies, r_k, out, bws, bf16_only=True)
+    ms16, _ = time_steps(bdec, steps, warmup, repeats, use_graph=True)
+    del bdec, bcopies, bws, inp
+    torch.cuda.empty_cache()
+    log(f"{name} decode only: INT2 {ms2 * 1e3:.2f} us/step, BF16-only {ms16 * 1e3:.2f} us/step "
+        f"({ms16 / ms2:.2f}x)")
+    return {"workload": name, "batch": wl.batch, "context": f"{wl.batch} x {wl.seq_lens[0]}",
+            "decode_only": "no append/demote in the timed step",
+            "int2": {"us_per_step": round(ms2 * 1e3, 3), "kv_bytes_per_step": kv["total"],
+                     "GBps": round(kv["total"] / (ms2 * 1e-3) / 1e9, 2), "pool_copies": n2,
+                     "tokens_per_s": round(wl.batch / (ms2 * 1e-3), 1)},
+            "bf16_only": {"us_per_step": round(ms16 * 1e3, 3), "kv_bytes_per_step": kv["bf16_only_total"],
+                          "GBps": round(kv["bf16_only_total"] / (ms16 * 1e-3) / 1e9, 2), "pool_copies": n16,
+                          "tokens_per_s": round(wl.batch / (ms16 * 1e-3), 1)},
+            "int2_speedup": round(ms16 / ms2, 3)}
+
+
 def time_steps(step, n_steps, warmup, repeats, use_graph=True):
     """Median and min ms per step over `repeats` runs of n_steps steps."""
     import torch
@@ -471,11 +515,24 @@ def traffic_for(workload, files=DECODE_SOURCES):
     return t.get("hbm_bytes_per_launch")
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, repeats=3):
-    """The oracle's decode (R1-R3) of the whole step, timed on this host's
-    cores: every KV head of every sequence over its full context.  The
-    oracle's own calibration and write path build its inputs and pool first
-    (not timed), from the same seeded draws."""
+    """The oracle timed on this host's cores, the whole 100K-token step:
+    its write path (W1-W7: rotate, clip, quantize and pack every history
+    token of every KV head, the pool's prefill) once, and its decode (R1-R3:
+    dequantize, inverse-rotate, one softmax over the concatenated pool) with
+    all BLAS threads (median of `repeats`) and with one thread (one run).
+    Inputs come from the oracle's own calibration of the same seeded draws
+    (not timed)."""
     import oracle
     from synthetic import draw_calibration, draw_inputs, make_calibration
     draws = draw_calibration(wl.num_kv_heads, wl.gqa, wl.head_dim, wl.seed)
@@ -483,11 +540,16 @@ def cpu_baseline(wl, repeats=3):
     c = make_calibration(draws, oc["r_k"], oc["r_v"], oc["tau_k"], oc["tau_v"])
     inp = draw_inputs(wl, c, device="cpu")
     seqs = []
+    t_write = 0.0
+    hist_tokens = 0
     for b, L in enumerate(wl.seq_lens):
         k = inp.k[b][:L].float().cpu().numpy()
         v = inp.v[b][:L].float().cpu().numpy()
         s = oracle.SeqPool(wl.num_kv_heads, wl.head_dim, wl.group_size, wl.sink, wl.recent)
+        t0 = time.perf_counter()
         s.prefill(k, v, c.r_k, c.tau_k, c.tau_v)
+        t_write += time.perf_counter() - t0
+        hist_tokens += wl.hist_len(L)
         seqs.append(s)
     q = inp.q.float().cpu().numpy()
     times = []
@@ -497,16 +559,31 @@ def cpu_baseline(wl, repeats=3):
         times.append(time.perf_counter() - t0)
     dt = statistics.median(times)
     kv = wl.kv_bytes()
+    cores = os.cpu_count()
+    dt1 = None
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.decode_attention(seqs, q, c.r_k)
+            dt1 = time.perf_counter() - t0
     except Exception:
-        cores = os.cpu_count()
-    return {"value": round(kv["total"] / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"whole step: fp64 numpy oracle decode (dequantize, inverse-rotate, one softmax) of all "
-                      f"{wl.num_kv_heads} KV heads / {wl.num_q_heads} query heads of {wl.batch} sequence(s) at "
-                      f"{list(wl.seq_lens)[:4]} tokens; step KV bytes / median wall time of {repeats} runs "
-                      f"({dt:.2f} s); host has {os.cpu_count()} logical CPUs"}
+        pass
+    tok_heads = hist_tokens * wl.num_kv_heads
+    res = {"value": round(kv["total"] / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": f"whole step: fp64 numpy oracle decode (dequantize, inverse-rotate, one softmax) of all "
+                     f"{wl.num_kv_heads} KV heads / {wl.num_q_heads} query heads of {wl.batch} sequence(s) at "
+                     f"{list(wl.seq_lens)[:4]} tokens; step KV bytes / median wall time of {repeats} runs "
+                     f"({dt:.2f} s) with {cores} BLAS threads; host has {os.cpu_count()} logical CPUs",
+           "cpu_model": _cpu_model(),
+           "write_path": {"token_heads_per_s": round(tok_heads / t_write, 1), "s": round(t_write, 3),
+                          "sample": f"oracle W1-W7 of {hist_tokens} history tokens x {wl.num_kv_heads} KV heads "
+                                    f"(R_K rotation, clip, quantize, pack), one run"}}
+    if dt1 is not None:
+        res["single_thread"] = {"value": round(kv["total"] / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                "s": round(dt1, 3)}
+    return res
 
 
 def bench_bulk_quant(oscar, steps=10, warmup=3, repeats=5, profile_launches=0):
@@ -682,6 +759,10 @@ def main():
         print(json.dumps({args.only: bench_decode_workload(oscar, name, max(10, args.steps // 4), args.warmup,
                                                            args.repeats, args.cold_bytes)}), flush=True)
         return
+    if args.only == "batch16":
+        print(json.dumps({"batched_decode_vs_bf16": bench_batch_comparator(
+            oscar, "qwen3-8b-b32-l32k-demote", max(10, args.steps // 10), 5, 3, args.cold_bytes)}), flush=True)
+        return
     if args.only == "calib":
         if args.profile_steps:
             bench_calibration(oscar, profile_launches=args.profile_steps)
@@ -731,7 +812,14 @@ def main():
     pdec = Decoder(oscar, pool, wl, q, lens, pcopies, r_k, out, ws)
     ms_priv, _ = time_steps(pdec, args.steps, args.warmup, 3, use_graph=True)
     log(f"INT2 decode (graph, cold, private page table per copy): {ms_priv * 1e3:.2f} us/step")
-    del pdec, pcopies
+    # ... and a rotation matrix of its own per copy too, as each layer of a
+    # model has its own R_K (the pools hold the same codes; only where R_K
+    # sits in memory differs)
+    rk_copies = [r_k.clone() for _ in pcopies]
+    rdec = Decoder(oscar, pool, wl, q, lens, pcopies, rk_copies, out, ws)
+    ms_prk, _ = time_steps(rdec, args.steps, args.warmup, 3, use_graph=True)
+    log(f"INT2 decode (graph, cold, private page table and R_K per copy): {ms_prk * 1e3:.2f} us/step")
+    del pdec, rdec, pcopies, rk_copies
     torch.cuda.empty_cache()
 
     gbps = kv["total"] / (ms * 1e-3) / 1e9
@@ -751,6 +839,7 @@ def main():
         "eager_ms_per_step": round(ms_eager, 6),
         "warm_ms_per_step": round(ms_warm, 6),
         "private_tables_ms_per_step": round(ms_priv, 6),
+        "private_tables_and_rk_ms_per_step": round(ms_prk, 6),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_for(wl.name),
                      "kernel": "k_decode (INT2 split-K + BF16 sink/recent + LSE merge, one launch per step)"},
@@ -788,6 +877,8 @@ def main():
         result["other_workloads"] = {
             "batched_demote": bench_decode_workload(oscar, "qwen3-8b-b32-l32k-demote", max(10, args.steps // 4),
                                                     args.warmup, args.repeats, args.cold_bytes),
+            "batched_decode_vs_bf16": bench_batch_comparator(oscar, "qwen3-8b-b32-l32k-demote",
+                                                             max(10, args.steps // 10), 5, 3, args.cold_bytes),
             "mixed_prefix_gqa8": bench_decode_workload(oscar, "qwen3-32b-b8-mixed-prefix", max(10, args.steps // 4),
                                                        args.warmup, args.repeats, args.cold_bytes),
             "bulk_quantize": bench_bulk_quant(oscar),
@@ -795,7 +886,7 @@ def main():
         }
     result["copy_ceiling_GBps"] = round(copy_ceiling_gbps(), 1)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, repeats=7)
     print(json.dumps(result), flush=True)
 
 

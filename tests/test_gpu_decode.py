@@ -151,10 +151,24 @@ def test_decode_full_size_headline_sampled(gpu_lib):
     log("oracle quantization of 99,680 x 8 history tokens")
     seqs = make_seqs(wl, inp)
     pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
-    out, _ = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
+    out, (pool, dev, lens, ws, max_len) = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k,
+                                                  host_lens=list(wl.seq_lens))
     pairs = [(0, 0), (0, 5), (0, 13), (0, 22), (0, 31)]
     ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k, pairs=pairs)
     check_decode(out, ref, pairs=pairs, what="qwen3-8b-l100k sampled")
+    # the same launch ten times more: bitwise equal outputs (the fold order
+    # of the split-K partials does not depend on which workgroup ends last),
+    # and the per-head tickets back at zero after each call
+    rk = to_dev(inp.calib.r_k)
+    qd = inp.q.cuda()
+    n_tickets = 128 * wl.batch * wl.num_kv_heads // 4
+    for i in range(10):
+        o = torch.zeros_like(out)
+        gpu_lib.oscar_decode_attention(pool, qd, lens, max_len, dev["bf16_pt"], dev["int2_pt"], dev["bf16_pool"],
+                                       dev["int2_pool"], rk, o, ws, seq_lens_host=list(wl.seq_lens))
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), out.view(torch.int16)), f"call {i + 1} differs"
+        assert int(ws[: 4 * n_tickets].view(torch.int32).abs().sum()) == 0, f"tickets not reset after call {i + 1}"
 
 
 @pytest.mark.parametrize("name", ["tiny-d64-gqa2-l512", "d128-gqa4-ragged", "d128-g64-gqa8"])
