@@ -57,6 +57,19 @@ constexpr float kLazy = 8.0f;        // log2 slack before the running max is rai
 // dword 3 of a gfx9 buffer descriptor for raw (untyped) loads: 32-bit data
 // format, no swizzle; out-of-range offsets read as zero
 constexpr int kBufferFlags = 0x00020000;
+// History pages are read exactly once per step: their code and scale words
+// are loaded non-temporal (cache policy bit NT), so that they do not push
+// the page tables, R_K and q out of L2 (measured 0.5 us faster per
+// 100K-token step, 8 % at 32 x 32K, than with the default policy).  BF16
+// pages keep the default policy: their lanes read 16-byte pieces of lines
+// that the next loads of the same lanes use: NT loads there measured 1.6x
+// slower for the BF16-only kernel and 0.9 us slower for the 100K-token step.
+constexpr int kKvPolicy = 2;
+__device__ __forceinline__ uint4 nt_load(const uint4* p) {
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  const u4v x = __builtin_nontemporal_load((const u4v*)p);
+  return uint4{x[0], x[1], x[2], x[3]};
+}
 
 template <int D, int NG, int GQA>
 struct DC {
@@ -364,13 +377,13 @@ __device__ __forceinline__ void i2_fetch(I2Tile<D, NG, GQA>& t, const uint8_t* _
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(hpool + (size_t)max(ids[s], 0) * page_bytes), (short)0, C::BLK2, kBufferFlags);
     if constexpr (D == 128) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * C::REC, 0, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * C::REC, 0, kKvPolicy);
       t.kw[s][0] = x[0];
       t.kw[s][1] = x[1];
       t.vw[s][0] = x[2];
       t.vw[s][1] = x[3];
     } else {
-      const auto y = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * C::REC, 0, 0);
+      const auto y = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * C::REC, 0, kKvPolicy);
       t.kw[s][0] = y[0];
       t.vw[s][0] = y[1];
     }
@@ -380,7 +393,7 @@ __device__ __forceinline__ void i2_fetch(I2Tile<D, NG, GQA>& t, const uint8_t* _
   const uint4* sp = (const uint4*)(hpool + (size_t)max(mine, 0) * page_bytes + 8 * D + j * 32 * NG);
   uint4 sx[2 * NG];
 #pragma unroll
-  for (int i = 0; i < 2 * NG; ++i) sx[i] = sp[i];
+  for (int i = 0; i < 2 * NG; ++i) sx[i] = nt_load(sp + i);
 #pragma unroll
   for (int i = 0; i < 2 * NG; ++i) {
     t.sc[4 * i + 0] = sx[i].x;
@@ -1363,19 +1376,19 @@ __device__ __forceinline__ void pt_fetch(PTile<D, NG>& t, const uint8_t* __restr
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(hpool + (size_t)max(id, 0) * page_bytes), (short)0, id >= 0 ? BLK2 : 0, kBufferFlags);
     if constexpr (D == 128) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * REC, 0, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * REC, 0, kKvPolicy);
       t.kw[s][0] = x[0];
       t.kw[s][1] = x[1];
       t.vw[s][0] = x[2];
       t.vw[s][1] = x[3];
     } else {
-      const auto y = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * REC, 0, 0);
+      const auto y = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * REC, 0, kKvPolicy);
       t.kw[s][0] = y[0];
       t.vw[s][0] = y[1];
     }
 #pragma unroll
     for (int i = 0; i < 2 * NG; ++i) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, 8 * D + j * 32 * NG + 16 * i, 0, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, 8 * D + j * 32 * NG + 16 * i, 0, kKvPolicy);
 #pragma unroll
       for (int e = 0; e < 4; ++e) t.sc[s][4 * i + e] = x[e];
     }
