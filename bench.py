@@ -100,6 +100,9 @@ def parse():
                     help="only run N eager decode steps over the cold pool copies, then one plain copy of "
                          "--probe-bytes (for rocprofv3 counters); prints no JSON")
     ap.add_argument("--probe-bytes", type=int, default=256 * 2**20)
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="load the profiling build liboscar_stamps.so, replay the 100K-token step over cold pool "
+                         "copies and print its per-wave phase timeline (no JSON metric line)")
     ap.add_argument("--only", default="all", choices=["all", "headline", "bulk", "demote", "mixed", "calib", "batch16"],
                     help="run one section only (the JSON line then holds what was measured)")
     return ap.parse_args()
@@ -726,6 +729,64 @@ def bench_calibration(oscar, steps=10, warmup=2, repeats=5, profile_launches=0):
                                 "sum ||o - o^||^2 / sum ||o||^2"}
 
 
+PHASES = ["start", "first tiles requested", "q' partial barrier", "q' split barrier", "first score MFMAs issued",
+          "loop end", "wave merge barrier", "partial stores acknowledged", "ticket taken", "fold written"]
+
+
+def phase_timeline(steps, warmup):
+    """Per-wave phase times of one cold 100K-token step from the profiling
+    build (s_memrealtime at fixed points of k_decode, 100 MHz), relative to
+    the earliest workgroup start of the step."""
+    import numpy as np
+    import torch
+    import long_context_decode_oscar_amd as oscar
+    from long_context_decode_oscar_amd import build as obuild
+    from synthetic import CONFIGS, draw_inputs
+    oscar.load(obuild.STAMPS_LIB)
+    wl = CONFIGS["qwen3-8b-l100k"]
+    kv = wl.kv_bytes()
+    inp = draw_inputs(wl, gpu_calibration(oscar, wl), device="cuda")
+    pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
+                                            wl.sink, wl.recent, 1, 0.0))
+    n_copies = max(1, math.ceil(2 * 2**30 / kv["total"]))
+    copies, r_k = build_pools(oscar, pool, wl, inp, n_copies, seed=wl.seed)
+    q = inp.q.contiguous()
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = pool.alloc_workspace(wl.batch, max(wl.seq_lens))  # includes the stamp area in this build
+    slots, waves, wgs = 16, 8, 2048
+    area = ws[ws.numel() - wgs * waves * slots * 8:]
+    area.zero_()
+    dec = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws)
+    ms, _ = time_steps(dec, steps, warmup, 1, use_graph=True)
+    st = area.view(torch.int64).cpu().numpy().reshape(wgs, waves, slots).astype(np.float64)
+    used = st[:, :, 0] > 0
+    t0 = st[:, :, 0][used].min()
+    rel = (st - t0) * 1e-2  # 100 MHz ticks -> us
+    rows = []
+    for k, name in enumerate(PHASES):
+        v = rel[:, :, k][st[:, :, k] > 0]
+        if len(v):
+            rows.append({"point": k, "phase": name, "n": int(len(v)), "min": round(float(v.min()), 2),
+                         "median": round(float(np.median(v)), 2), "p90": round(float(np.percentile(v, 90)), 2),
+                         "max": round(float(v.max()), 2)})
+    folded = st[:, 0, 10] > 0
+    wg_used = used.any(axis=1)
+    loop_end = np.where(st[:, :, 5] > 0, rel[:, :, 5], np.nan)
+    res = {"workload": wl.name, "steps": steps, "step_us": round(ms * 1e3, 3), "phases": rows,
+           "fold_end_per_head_us": sorted(round(float(x), 2) for x in rel[folded, 0, 9]),
+           "wg_loop_end_us": {"min": round(float(np.nanmin(np.nanmax(loop_end[wg_used], axis=1))), 2),
+                              "median": round(float(np.nanmedian(np.nanmax(loop_end[wg_used], axis=1))), 2),
+                              "max": round(float(np.nanmax(loop_end[wg_used])), 2)},
+           "wave_loop_end_spread_in_wg_us": round(float(np.nanmedian(
+               np.nanmax(loop_end[wg_used], axis=1) - np.nanmin(loop_end[wg_used], axis=1))), 2)}
+    log(f"phase timeline of the last of {steps} cold graph steps ({ms * 1e3:.2f} us/step in this build)")
+    for r in rows:
+        log(f"  {r['point']} {r['phase']:28s} n={r['n']:5d} min {r['min']:6.2f} med {r['median']:6.2f} "
+            f"p90 {r['p90']:6.2f} max {r['max']:6.2f}")
+    return res
+
+
 def copy_probe(nbytes):
     """One plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -749,6 +810,9 @@ def main():
     import long_context_decode_oscar_amd as oscar
     from synthetic import CONFIGS, draw_inputs
 
+    if args.phase_stamps:
+        print(json.dumps({"phase_timeline": phase_timeline(args.steps, args.warmup)}), flush=True)
+        return
     oscar.load()
     if args.only in ("demote", "mixed"):
         name = "qwen3-8b-b32-l32k-demote" if args.only == "demote" else "qwen3-32b-b8-mixed-prefix"

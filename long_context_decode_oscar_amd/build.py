@@ -1,6 +1,7 @@
 """Build liboscar.so (HIP, gfx950) in-tree with hipcc.
 
     python -m long_context_decode_oscar_amd.build
+    python -m long_context_decode_oscar_amd.build --phase-stamps   # profiling variant
 
 Every source is compiled with packed-fp32 instruction selection disabled
 (``-target-feature -packed-fp32-ops``) and the objects are linked into one
@@ -39,14 +40,21 @@ def flags():
     ]
 
 
-def build(verbose: bool = False) -> str:
+STAMPS_LIB = os.path.join(HERE, "liboscar_stamps.so")
+
+
+def build(verbose: bool = False, phase_stamps: bool = False) -> str:
+    """Compiles every source and links liboscar.so.  phase_stamps=True builds
+    the profiling variant liboscar_stamps.so instead, whose plain decode
+    records a per-wave phase timeline (bench.py --phase-stamps reads it)."""
     cc = hipcc()
-    objdir = os.path.join(HERE, "_build")
+    objdir = os.path.join(HERE, "_build", "stamps" if phase_stamps else "")
     os.makedirs(objdir, exist_ok=True)
+    extra = ["-DOSCAR_PHASE_STAMPS=1"] if phase_stamps else []
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,14 +64,15 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    lib = STAMPS_LIB if phase_stamps else LIB
+    tmp = lib + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, phase_stamps="--phase-stamps" in sys.argv))

@@ -40,14 +40,8 @@
 namespace oscar {
 namespace {
 
-constexpr int kBufferFlags = 0x00020000;  // raw dword buffer: out-of-range loads read 0
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ void* uniform_ptr(const void* q) {
-  const uint64_t u = (uint64_t)q;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (void*)(((uint64_t)hi << 32) | lo);
-}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), (short)0, (int)bytes, kBufferFlags);
 }

@@ -45,6 +45,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
+// dword 3 of a gfx950 buffer descriptor for raw (untyped) access: 32-bit
+// data format, no swizzle; loads at offsets past num_records read zero and
+// stores there are dropped
+constexpr int kBufferFlags = 0x00020000;
+
+// a wave-uniform pointer held in scalar registers
+__device__ __forceinline__ void* uniform_ptr(const void* q) {
+  const uint64_t u = (uint64_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (void*)(((uint64_t)hi << 32) | lo);
+}
+
 // DPP row rotate (within 16-lane rows): lane i reads lane (i + n) % 16.
 template <int N>
 __device__ __forceinline__ float dpp_row_ror(float x) {

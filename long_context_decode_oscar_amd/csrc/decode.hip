@@ -54,9 +54,6 @@ constexpr int kRing = OSCAR_DECODE_RING;    // INT2 tiles held per wave (ring of
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1.0e30f;  // finite "no token yet" running max
 constexpr float kLazy = 8.0f;        // log2 slack before the running max is raised
-// dword 3 of a gfx9 buffer descriptor for raw (untyped) loads: 32-bit data
-// format, no swizzle; out-of-range offsets read as zero
-constexpr int kBufferFlags = 0x00020000;
 // History pages are read exactly once per step: their code and scale words
 // are loaded non-temporal (cache policy bit NT), so that they do not push
 // the page tables, R_K and q out of L2 (measured 0.5 us faster per
@@ -65,6 +62,34 @@ constexpr int kBufferFlags = 0x00020000;
 // that the next loads of the same lanes use: NT loads there measured 1.6x
 // slower for the BF16-only kernel and 0.9 us slower for the 100K-token step.
 constexpr int kKvPolicy = 2;
+// Phase timeline of the profiling build.  Point k of wave w of logical
+// workgroup lin lands in stamps[(lin * kWaves + w) * kStampSlots + k]:
+// 0 start, 1 first tiles requested, 2 q' partial barrier, 3 q' split
+// barrier, 4 first score MFMAs issued, 5 loop end, 6 wave merge barrier,
+// 7 partial stores acknowledged, 8 ticket taken, 9 fold written (last
+// workgroup only), 10: 1 for the workgroup that folded.  Empty otherwise.
+struct PhaseStamps {
+#if OSCAR_PHASE_STAMPS
+  uint64_t t[kStampSlots];
+  __device__ __forceinline__ PhaseStamps() {
+#pragma unroll
+    for (int k = 0; k < kStampSlots; ++k) t[k] = 0;
+  }
+  __device__ __forceinline__ void at(int k) { t[k] = __builtin_amdgcn_s_memrealtime(); }
+  __device__ __forceinline__ void set(int k, uint64_t v) { t[k] = v; }
+  __device__ __forceinline__ void flush(uint64_t* dst, int lin, int wave, int lane) const {
+    if (dst && lin < kStampWgs && lane == 0)
+#pragma unroll
+      for (int k = 0; k < kStampSlots; ++k) dst[((size_t)lin * kWaves + wave) * kStampSlots + k] = t[k];
+  }
+#else
+  __device__ __forceinline__ void at(int) {}
+  __device__ __forceinline__ void set(int, uint64_t) {}
+  __device__ __forceinline__ void flush(uint64_t*, int, int, int) const {}
+#endif
+};
+static_assert(kWaves == kStampWaves, "stamp area sized for the decode workgroup");
+
 __device__ __forceinline__ uint4 nt_load(const uint4* p) {
   typedef unsigned int u4v __attribute__((ext_vector_type(4)));
   const u4v x = __builtin_nontemporal_load((const u4v*)p);
@@ -761,6 +786,8 @@ __global__ void __launch_bounds__(kThreads)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, j = lane >> 4;
   const int lin = xcd_remap(blockIdx.x, grid_n);
+  PhaseStamps ps;
+  ps.at(0);
   // this workgroup's (sequence, KV head, unit), its head's units U and
   // partial slots [slot0, slot0 + head_slots)
   int U, u, kvh, b, head_slots, slot0;
@@ -934,6 +961,7 @@ __global__ void __launch_bounds__(kThreads)
     };
 #pragma unroll
     for (int r = 0; r < R - 1; ++r) fetch(ring[r], r);
+    ps.at(1);
 
     // ---- prologue: q' = q R_K (fp32), per-head int8 split, B operands
     {
@@ -971,6 +999,7 @@ __global__ void __launch_bounds__(kThreads)
         *(float4*)&sm.u.qpart[wave][h][4 * cg] = float4{qacc[h][0], qacc[h][1], qacc[h][2], qacc[h][3]};
     }
     __syncthreads();
+    ps.at(2);
     if (wave < GQA) {
       // wave h finishes query head h: lane owns channels CPL*lane + e
       const int h = wave;
@@ -1028,6 +1057,7 @@ __global__ void __launch_bounds__(kThreads)
       }
     }
     __syncthreads();
+    ps.at(3);
     // three-term mode for the whole workgroup when any of its heads needs it
     int any_dom = 0;
 #pragma unroll
@@ -1085,6 +1115,7 @@ __global__ void __launch_bounds__(kThreads)
         return r;
       };
       I2Scores<NG> S = scores(ring[0]);
+      ps.at(4);
       int i = 0;
       while (true) {
 #pragma unroll
@@ -1125,6 +1156,7 @@ __global__ void __launch_bounds__(kThreads)
       else
         run(std::false_type{});
     }
+    ps.at(5);
     wave_finish<D, NG, GQA, true, LUT>(st, sm, wave, lane);
   } else {
     // ------------------------------------------- BF16 unit (sink + recent)
@@ -1175,9 +1207,11 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int g = 0; g < NG; ++g) st2.Z[g] = 0.f;
     }
+    ps.at(5);
     wave_finish<D, NG, GQA, false>(st2, sm, wave, lane);
   }
   __syncthreads();
+  ps.at(6);
 
   // ---- merge the waves' partials into this workgroup's partial
   const size_t head_base = (size_t)b * num_kv_heads + kvh;
@@ -1215,6 +1249,7 @@ __global__ void __launch_bounds__(kThreads)
   // of its own.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
   __syncthreads();
+  ps.at(7);
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(p.counters + head_base * kCounterStride, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
@@ -1223,7 +1258,12 @@ __global__ void __launch_bounds__(kThreads)
     sm.last = last;
   }
   __syncthreads();
-  if (!sm.last) return;
+  ps.at(8);
+  if (!sm.last) {
+    ps.flush(p.stamps, lin, wave, lane);
+    return;
+  }
+  ps.set(10, 1);
   const size_t p0 = (size_t)slot0 * GQA;
   // Folds partials u0 .. u1-1 of head h, channel c into (M, S, A): the log2
   // max, the sum of weights and the weighted sum of normalized outputs.  h
@@ -1320,6 +1360,8 @@ __global__ void __launch_bounds__(kThreads)
   }
   if (tid == 0)
     __hip_atomic_store(p.counters + head_base * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  ps.at(9);
+  ps.flush(p.stamps, lin, wave, lane);
 }
 
 // ------------------------------------------------ prefix (cascade) unit --

@@ -57,7 +57,19 @@ struct DecodeParams {
   uint32_t lut_k;            // byte c: 32 L_K[c] (int8 score operand of code c)
   uint32_t lut_v;            // byte c: 64 L_V[c] (mantissa of the fp16 operand 16 + L_V[c])
   int32_t n_casc;            // prefix-shared units (0: plain decode)
+  uint64_t* stamps;          // phase timeline of the profiling build (null otherwise)
 };
+
+// Profiling build (-DOSCAR_PHASE_STAMPS=1): the plain decode records, per
+// wave, kStampSlots real-time counter values (100 MHz) for workgroups below
+// kStampWgs, in the last kStampBytes of the caller's workspace.
+#ifndef OSCAR_PHASE_STAMPS
+#define OSCAR_PHASE_STAMPS 0
+#endif
+constexpr int kStampSlots = 16;
+constexpr int kStampWgs = 2048;
+constexpr int kStampWaves = 8;
+constexpr size_t kStampBytes = (size_t)kStampWgs * kStampWaves * kStampSlots * sizeof(uint64_t);
 
 // The prefix-shared units of a decode with prefix groups: a separate kernel
 // argument of the instantiations that take prefix groups (the plain launch

@@ -525,7 +525,7 @@ oscar_status oscar_decode_workspace_bytes(const oscar_pool* pool, int32_t batch,
   }
   const Plan pl = make_plan(pool, batch, max_seq_len, bf16_only != 0);
   if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
-  *bytes = pl.bytes;
+  *bytes = pl.bytes + (OSCAR_PHASE_STAMPS ? oscar::kStampBytes : 0);
   return ok();
 }
 
@@ -569,10 +569,13 @@ oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_
     return fail(OSCAR_ERR_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes", pl.bytes);
   // the length-aware plan when host lengths are given and its partials fit
   // the workspace (sized for the uniform plan of max_seq_len)
+  // profiling build: the phase timeline takes the workspace's last bytes
+  const bool stamps = OSCAR_PHASE_STAMPS && num_groups == 0 && workspace_bytes >= pl.bytes + oscar::kStampBytes;
+  const size_t ws_plan = workspace_bytes - (stamps ? oscar::kStampBytes : 0);
   PackedPlan pk;
   const bool packed = plan_packed(pool, batch, max_seq_len, seq_lens_host, bf16_pt_stride, int2_pt_stride, pl, cp,
                                   &pk) &&
-                      pk.bytes <= workspace_bytes;
+                      pk.bytes <= ws_plan;
   const oscar_config& c = pool->cfg;
   oscar::DecodeParams p{};
   p.q = (const uint16_t*)q;
@@ -587,6 +590,7 @@ oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_
   p.counters = (uint32_t*)((char*)workspace + pl.off_counters);
   p.part_lse = (float*)((char*)workspace + pl.off_lse);
   p.part_o = (float*)((char*)workspace + pl.off_o);
+  if (stamps) p.stamps = (uint64_t*)((char*)workspace + ws_plan);
   p.bf16_pt_stride = bf16_pt_stride;
   p.bf16_num_pages = bf16_num_pages;
   p.int2_pt_stride = int2_pt_stride;

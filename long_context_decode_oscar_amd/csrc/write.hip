@@ -376,17 +376,6 @@ struct BulkPage {  // one page's global inputs, as loaded
   int id;                    // physical page (-1: none)
 };
 
-// buffer descriptor flags (gfx950 dword 3: raw buffer, 32-bit data format);
-// loads past num_records return zero
-constexpr int kBufferFlags = 0x00020000;
-
-// a wave-uniform pointer held in scalar registers
-__device__ __forceinline__ void* uniform_ptr(const void* q) {
-  const uint64_t u = (uint64_t)q;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (void*)(((uint64_t)hi << 32) | lo);
-}
-
 // Loads page `page` whose physical id (or -1) is `id`.  One buffer descriptor
 // per page, based at its first token, bounds the loads: slots past the last
 // token, and every slot of a page without a physical id, read as zero, with
