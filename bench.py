@@ -733,17 +733,18 @@ PHASES = ["start", "first tiles requested", "q' partial barrier", "q' split barr
           "loop end", "wave merge barrier", "partial stores acknowledged", "ticket taken", "fold written"]
 
 
-def phase_timeline(steps, warmup):
-    """Per-wave phase times of one cold 100K-token step from the profiling
-    build (s_memrealtime at fixed points of k_decode, 100 MHz), relative to
-    the earliest workgroup start of the step."""
+def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
+    """Per-wave phase times of one cold decode step (plain decode, host-length
+    plan) from the profiling build (s_memrealtime at fixed points of
+    k_decode, 100 MHz), relative to the earliest workgroup start of the
+    step."""
     import numpy as np
     import torch
     import long_context_decode_oscar_amd as oscar
     from long_context_decode_oscar_amd import build as obuild
     from synthetic import CONFIGS, draw_inputs
     oscar.load(obuild.STAMPS_LIB)
-    wl = CONFIGS["qwen3-8b-l100k"]
+    wl = CONFIGS[workload]
     kv = wl.kv_bytes()
     inp = draw_inputs(wl, gpu_calibration(oscar, wl), device="cuda")
     pool = oscar.OscarPool(oscar.PoolConfig(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.group_size, 16,
@@ -773,7 +774,13 @@ def phase_timeline(steps, warmup):
     folded = st[:, 0, 10] > 0
     wg_used = used.any(axis=1)
     loop_end = np.where(st[:, :, 5] > 0, rel[:, :, 5], np.nan)
-    res = {"workload": wl.name, "steps": steps, "step_us": round(ms * 1e3, 3), "phases": rows,
+    per_wg = {"wgs": int(wg_used.sum()), "wg_duration_us": None}
+    starts = np.where(st[:, :, 0] > 0, rel[:, :, 0], np.nan)
+    ends = np.where(st[:, :, 8] > 0, rel[:, :, 8], np.nan)
+    dur_wg = np.nanmax(ends[wg_used], axis=1) - np.nanmin(starts[wg_used], axis=1)
+    per_wg["wg_duration_us"] = {"min": round(float(np.nanmin(dur_wg)), 2), "median": round(float(np.nanmedian(dur_wg)), 2),
+                                "max": round(float(np.nanmax(dur_wg)), 2)}
+    res = {"workload": wl.name, "steps": steps, "step_us": round(ms * 1e3, 3), "phases": rows, "workgroups": per_wg,
            "fold_end_per_head_us": sorted(round(float(x), 2) for x in rel[folded, 0, 9]),
            "wg_loop_end_us": {"min": round(float(np.nanmin(np.nanmax(loop_end[wg_used], axis=1))), 2),
                               "median": round(float(np.nanmedian(np.nanmax(loop_end[wg_used], axis=1))), 2),
@@ -811,7 +818,7 @@ def main():
     from synthetic import CONFIGS, draw_inputs
 
     if args.phase_stamps:
-        print(json.dumps({"phase_timeline": phase_timeline(args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"phase_timeline": phase_timeline(args.steps, args.warmup, args.workload)}), flush=True)
         return
     oscar.load()
     if args.only in ("demote", "mixed"):

@@ -322,8 +322,11 @@ __device__ __forceinline__ float split_query(const float (&x)[CPL], int (&a)[CPL
   amax = wave_max(amax);
   ss = wave_sum(ss);
   dom = amax * amax > kDominant * kDominant * ss * (1.f / (64 * CPL));
-  const float sq = amax > 0.f ? amax / 127.f : 1.f;
-  const float inv_sq = 1.f / sq;
+  // sq and its reciprocal need not be correctly rounded: the terms are
+  // formed from y = x / sq (to within 1 ulp) and the dot is scaled by sq
+  // itself, so only the rounding of the terms enters the result
+  const float sq = amax > 0.f ? amax * (1.f / 127.f) : 1.f;
+  const float inv_sq = __builtin_amdgcn_rcpf(sq);
 #pragma unroll
   for (int e = 0; e < CPL; ++e) {
     const float y = x[e] * inv_sq;
@@ -731,7 +734,7 @@ __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.o[cbk][i] = slot_sum<GQA>(st.o[cbk][i]);
   if (n < GQA) {
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    const float inv = st.l > 0.f ? __builtin_amdgcn_rcpf(st.l) : 0.f;
 #pragma unroll
     for (int cbk = 0; cbk < D / 16; ++cbk) {
 #pragma unroll
@@ -1230,7 +1233,7 @@ __global__ void __launch_bounds__(kThreads)
         sw += e;
         so += e * sm.u.part[w][h][c];
       }
-      o = so / sw;
+      o = so * __builtin_amdgcn_rcpf(sw);
       lse = mx + __log2f(sw);  // log2 units
     }
     // device-scope stores write through the XCD's L2, so no L2 write-back
@@ -1311,7 +1314,7 @@ __global__ void __launch_bounds__(kThreads)
       const int h = idx / D, c = idx % D;
       float M, S, A;
       fold(h, c, 0, total + cch, M, S, A);
-      outp[h * D + c] = (uint16_t)f32_to_bf16(S > 0.f ? A / S : 0.f);
+      outp[h * D + c] = (uint16_t)f32_to_bf16(S > 0.f ? A * __builtin_amdgcn_rcpf(S) : 0.f);
     }
   } else {
     // Values not absorbed: the INT2 partials hold V R_V.  Their merge is
@@ -1765,7 +1768,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
 #pragma unroll
   for (int g = 0; g < NG; ++g) st.Z[g] = col_sum(st.Z[g]);
   {
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    const float inv = st.l > 0.f ? __builtin_amdgcn_rcpf(st.l) : 0.f;
 #pragma unroll
     for (int cbk = 0; cbk < D / 16; ++cbk)
 #pragma unroll
@@ -1795,7 +1798,7 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
         sw += e;
         so += e * sm.u.part[w][col][ch];
       }
-      o = so / sw;
+      o = so * __builtin_amdgcn_rcpf(sw);
       lse = mx + __log2f(sw);
     }
     int oc = 0, s0 = 0;
