@@ -103,7 +103,7 @@ def parse():
     ap.add_argument("--phase-stamps", action="store_true",
                     help="load the profiling build liboscar_stamps.so, replay the 100K-token step over cold pool "
                          "copies and print its per-wave phase timeline (no JSON metric line)")
-    ap.add_argument("--only", default="all", choices=["all", "headline", "bulk", "demote", "mixed", "calib", "batch16"],
+    ap.add_argument("--only", default="all", choices=["all", "headline", "bulk", "demote", "mixed", "calib", "batch-bf16"],
                     help="run one section only (the JSON line then holds what was measured)")
     return ap.parse_args()
 
@@ -830,7 +830,7 @@ def main():
         print(json.dumps({args.only: bench_decode_workload(oscar, name, max(10, args.steps // 4), args.warmup,
                                                            args.repeats, args.cold_bytes)}), flush=True)
         return
-    if args.only == "batch16":
+    if args.only == "batch-bf16":
         print(json.dumps({"batched_decode_vs_bf16": bench_batch_comparator(
             oscar, "qwen3-8b-b32-l32k-demote", max(10, args.steps // 10), 5, 3, args.cold_bytes)}), flush=True)
         return
