@@ -730,7 +730,8 @@ def bench_calibration(oscar, steps=10, warmup=2, repeats=5, profile_launches=0):
 
 
 PHASES = ["start", "first tiles requested", "q' partial barrier", "q' split barrier", "first score MFMAs issued",
-          "loop end", "wave merge barrier", "partial stores acknowledged", "ticket taken", "fold written"]
+          "loop end", "wave merge barrier", "partial stores acknowledged", "ticket taken", "fold written", None,
+          "q' FMAs done (R_K arrived)", "q' split written"]
 
 
 def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
@@ -766,6 +767,8 @@ def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
     rel = (st - t0) * 1e-2  # 100 MHz ticks -> us
     rows = []
     for k, name in enumerate(PHASES):
+        if name is None:
+            continue
         v = rel[:, :, k][st[:, :, k] > 0]
         if len(v):
             rows.append({"point": k, "phase": name, "n": int(len(v)), "min": round(float(v.min()), 2),

@@ -67,7 +67,9 @@ constexpr int kKvPolicy = 2;
 // 0 start, 1 first tiles requested, 2 q' partial barrier, 3 q' split
 // barrier, 4 first score MFMAs issued, 5 loop end, 6 wave merge barrier,
 // 7 partial stores acknowledged, 8 ticket taken, 9 fold written (last
-// workgroup only), 10: 1 for the workgroup that folded.  Empty otherwise.
+// workgroup only), 10: 1 for the workgroup that folded, 11 q' FMAs done
+// (R_K arrived), 12 q' split written (waves of the query heads only).
+// Empty otherwise.
 struct PhaseStamps {
 #if OSCAR_PHASE_STAMPS
   uint64_t t[kStampSlots];
@@ -987,6 +989,7 @@ __global__ void __launch_bounds__(kThreads)
         qacc[h][3] = fmaf(qv, rr[i].w, qacc[h][3]);
       }
     }
+    ps.at(11);
     // sum the row segments held by this wave (lanes with equal cg)
     static_assert(CG == 16 || CG == 32, "one or two row segments per 32 lanes");
 #pragma unroll
@@ -1058,6 +1061,7 @@ __global__ void __launch_bounds__(kThreads)
         sm.kap3[h] = p.sm_log2 * sq * (1.f / 65536.f);
         sm.dom[h] = dom ? 1 : 0;
       }
+      ps.at(12);
     }
     __syncthreads();
     ps.at(3);
