@@ -324,9 +324,46 @@ __device__ __forceinline__ void scale_zero_recip(float mn, float mx, uint32_t& s
 // 3(1 + 2^-8) because s is within 2^-9 of (max - min)/3, and z is within
 // 2^-9 |z| <= 0.251 of -min/s; so the clamp to [0, 3] never acts.  Other
 // groups take the IEEE division, round and clamp.
+// The fast path of group_codes below without a branch: every operation of
+// its common case, computed unconditionally, and `ok` set when this lane's
+// group meets all the conditions under which that case is the one taken
+// (d and |min| in [2^-100, 2^100] and [2^-100, 2^56], s in [2^-70, 2^70],
+// |max| <= 2^56, |z| <= 128).  Where ok holds, the result is bit for bit
+// that of group_codes.
+template <int N>
+__device__ __forceinline__ uint32_t group_codes_nb(const float (&x)[N], float mn, float mx, uint32_t (&words)[N / 4],
+                                                   bool& ok) {
+  const float d = mx - mn;
+  const uint32_t s_bits = f32_to_bf16(div_bf16(d, 3.0f, 0x1.555556p-2f));
+  const float s = bf16_to_f32(s_bits);
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  const float y = __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0);
+  const uint32_t z_bits = f32_to_bf16(div_bf16(-mn, s, y));
+  const float z = bf16_to_f32(z_bits);
+  const float amn = fabsf(mn);
+  ok = d >= 0x1p-100f && d <= 0x1p100f && s >= 0x1p-70f && s <= 0x1p70f && amn >= 0x1p-100f && amn <= 0x1p56f &&
+       fabsf(mx) <= 0x1p56f && fabsf(z) <= 128.f;
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      word = __builtin_amdgcn_cvt_pk_u8_f32(__fadd_rn(div_bf16(x[4 * q + e], s, y), z), e, word);
+    words[q] = word;
+  }
+  return s_bits | (z_bits << 16);
+}
+
 template <int N, bool LUT>
 __device__ __forceinline__ uint32_t group_codes(const float (&x)[N], float mn, float mx, uint32_t (&words)[N / 4],
                                                 const Thr& th) {
+  if constexpr (!LUT) {
+    // the common case without a branch; the whole wave takes the general
+    // code below only when one of its groups is outside that case
+    bool ok;
+    const uint32_t sz = group_codes_nb<N>(x, mn, mx, words, ok);
+    if (__builtin_amdgcn_ballot_w64(!ok) == 0) return sz;
+  }
   uint32_t sb, zb;
   float s, z, y;
   scale_zero_recip(mn, mx, sb, zb, s, z, y);
