@@ -729,6 +729,9 @@ def bench_calibration(oscar, steps=10, warmup=2, repeats=5, profile_launches=0):
                                 "sum ||o - o^||^2 / sum ||o||^2"}
 
 
+# the profiling build's stamp area (kStampSlots, kStampWaves, kStampWgs in
+# the library's kernels.h): slots per wave, waves per workgroup, workgroups
+STAMP_SLOTS, STAMP_WAVES, STAMP_WGS = 16, 8, 2048
 PHASES = ["start", "first tiles requested", "q' partial barrier", "q' split barrier", "first score MFMAs issued",
           "loop end", "wave merge barrier", "partial stores acknowledged", "ticket taken", "fold written", None,
           "q' FMAs done (R_K arrived)", "q' split written"]
@@ -756,7 +759,7 @@ def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
     lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     ws = pool.alloc_workspace(wl.batch, max(wl.seq_lens))  # includes the stamp area in this build
-    slots, waves, wgs = 16, 8, 2048
+    slots, waves, wgs = STAMP_SLOTS, STAMP_WAVES, STAMP_WGS
     area = ws[ws.numel() - wgs * waves * slots * 8:]
     area.zero_()
     dec = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws)
