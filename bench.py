@@ -747,6 +747,8 @@ def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
     import long_context_decode_oscar_amd as oscar
     from long_context_decode_oscar_amd import build as obuild
     from synthetic import CONFIGS, draw_inputs
+    if not os.path.exists(obuild.STAMPS_LIB):
+        raise SystemExit("the profiling build is missing: python -m long_context_decode_oscar_amd.build --phase-stamps")
     oscar.load(obuild.STAMPS_LIB)
     wl = CONFIGS[workload]
     kv = wl.kv_bytes()
