@@ -1619,12 +1619,24 @@ __global__ void __launch_bounds__(kThreads) k_decode_prefix(const DecodeParams p
 #pragma unroll
         for (int e = 0; e < 4; ++e) qacc[h][e] = 0.f;
       if (m < cu.count) {
+        // the thread's RPS consecutive q channels of each head in one load
         const uint16_t* qb = p.q + ((size_t)(cu.first + m) * hq + kvh * GQA) * D + rs * RPS;
 #pragma unroll
         for (int h = 0; h < GQA; ++h) {
+          uint32_t qw[RPS / 2];
+          if constexpr (RPS == 8) {
+            const uint4 x = *(const uint4*)(qb + h * D);
+            qw[0] = x.x;
+            qw[1] = x.y;
+            qw[2] = x.z;
+            qw[3] = x.w;
+          } else {
+            static_assert(RPS == 2, "row split");
+            qw[0] = *(const uint32_t*)(qb + h * D);
+          }
 #pragma unroll
           for (int i = 0; i < RPS; ++i) {
-            const float qv = bf16_to_f32(qb[h * D + i]);
+            const float qv = (i & 1) ? bf16_hi(qw[i >> 1]) : bf16_lo(qw[i >> 1]);
             qacc[h][0] = fmaf(qv, rr[i].x, qacc[h][0]);
             qacc[h][1] = fmaf(qv, rr[i].y, qacc[h][1]);
             qacc[h][2] = fmaf(qv, rr[i].z, qacc[h][2]);
