@@ -762,7 +762,9 @@ def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
     out = torch.empty_like(q)
     ws = pool.alloc_workspace(wl.batch, max(wl.seq_lens))  # includes the stamp area in this build
     slots, waves, wgs = STAMP_SLOTS, STAMP_WAVES, STAMP_WGS
-    area = ws[ws.numel() - wgs * waves * slots * 8:]
+    nbytes = wgs * waves * slots * 8
+    off = (ws.numel() - nbytes) // 256 * 256  # where the library puts the stamp area
+    area = ws[off:off + nbytes]
     area.zero_()
     dec = Decoder(oscar, pool, wl, q, lens, copies, r_k, out, ws)
     ms, _ = time_steps(dec, steps, warmup, 1, use_graph=True)

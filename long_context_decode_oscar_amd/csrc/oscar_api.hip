@@ -525,7 +525,7 @@ oscar_status oscar_decode_workspace_bytes(const oscar_pool* pool, int32_t batch,
   }
   const Plan pl = make_plan(pool, batch, max_seq_len, bf16_only != 0);
   if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
-  *bytes = pl.bytes + (OSCAR_PHASE_STAMPS ? oscar::kStampBytes : 0);
+  *bytes = pl.bytes + (OSCAR_PHASE_STAMPS ? oscar::kStampBytes + 256 : 0);
   return ok();
 }
 
@@ -567,11 +567,12 @@ oscar_status decode_impl(const oscar_pool* pool, int32_t batch, int32_t max_seq_
   if (!pl.fits) return fail(OSCAR_ERR_UNSUPPORTED, "max_seq_len %d needs more than %d split-K chunks", max_seq_len, kMaxChunks);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes)
     return fail(OSCAR_ERR_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes", pl.bytes);
+  // profiling build: the phase timeline takes the workspace's last bytes
+  // (from a 256-byte boundary)
+  const bool stamps = OSCAR_PHASE_STAMPS && num_groups == 0 && workspace_bytes >= pl.bytes + oscar::kStampBytes + 256;
+  const size_t ws_plan = stamps ? (workspace_bytes - oscar::kStampBytes) & ~(size_t)255 : workspace_bytes;
   // the length-aware plan when host lengths are given and its partials fit
   // the workspace (sized for the uniform plan of max_seq_len)
-  // profiling build: the phase timeline takes the workspace's last bytes
-  const bool stamps = OSCAR_PHASE_STAMPS && num_groups == 0 && workspace_bytes >= pl.bytes + oscar::kStampBytes;
-  const size_t ws_plan = workspace_bytes - (stamps ? oscar::kStampBytes : 0);
   PackedPlan pk;
   const bool packed = plan_packed(pool, batch, max_seq_len, seq_lens_host, bf16_pt_stride, int2_pt_stride, pl, cp,
                                   &pk) &&
