@@ -734,7 +734,8 @@ def bench_calibration(oscar, steps=10, warmup=2, repeats=5, profile_launches=0):
 STAMP_SLOTS, STAMP_WAVES, STAMP_WGS = 16, 8, 2048
 PHASES = ["start", "first tiles requested", "q' partial barrier", "q' split barrier", "first score MFMAs issued",
           "loop end", "wave merge barrier", "partial stores acknowledged", "ticket taken", "fold written", None,
-          "q' FMAs done (R_K arrived)", "q' split written"]
+          "q' FMAs done (R_K arrived)", "q' split written", "wave epilogue written to LDS",
+          "ticket returned (wave 0)", "acquire done (wave 0)"]
 
 
 def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
@@ -797,10 +798,19 @@ def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
                               "max": round(float(np.nanmax(loop_end[wg_used])), 2)},
            "wave_loop_end_spread_in_wg_us": round(float(np.nanmedian(
                np.nanmax(loop_end[wg_used], axis=1) - np.nanmin(loop_end[wg_used], axis=1))), 2)}
+    # the last workgroup of each head: its latest wave at every point
+    fold_pts = {}
+    for k in (0, 1, 4, 5, 13, 6, 7, 14, 15, 8, 9):
+        v = np.where(st[folded, :, k] > 0, rel[folded, :, k], np.nan)
+        if np.isfinite(v).any():
+            fold_pts[k] = round(float(np.nanmedian(np.nanmax(v, axis=1))), 2)
+    res["fold_wg_points_us"] = fold_pts
     log(f"phase timeline of the last of {steps} cold graph steps ({ms * 1e3:.2f} us/step in this build)")
     for r in rows:
         log(f"  {r['point']} {r['phase']:28s} n={r['n']:5d} min {r['min']:6.2f} med {r['median']:6.2f} "
             f"p90 {r['p90']:6.2f} max {r['max']:6.2f}")
+    log("  last workgroups (median over heads of the latest wave): " +
+        ", ".join(f"{k}: {v:.2f}" for k, v in fold_pts.items()))
     return res
 
 

@@ -117,8 +117,12 @@ template <int D, int GQA>
 struct Smem {
   static constexpr int SLOTS = (16 / GQA) < 4 ? (16 / GQA) : 4;
   union {
-    float part[kWaves][GQA][D + 1];  // per-wave partials, [D] = lse (log2)
-    float qpart[kWaves][GQA][D];     // prologue: per-wave partial sums of q R_K
+    struct {
+      float part[kWaves][GQA][D + 1];  // per-wave partials, [D] = lse (log2)
+      float raw[kWaves][16][D + 4];    // INT2 epilogue: a wave's accumulators per column
+      float lz[kWaves][16][4];         // INT2 epilogue: per column l, Z[0], Z[1], reference
+    } f;
+    float qpart[kWaves][GQA][D];  // prologue: per-wave partial sums of q R_K
   } u;
   v4i bq[SLOTS][3][D / 64][64];      // int8 q' B operands per lane (terms a, b, c; shared by the waves)
   float kap[GQA];                    // logit factor sm * log2(e) * sq / 256 per query head
@@ -377,10 +381,11 @@ struct I2Tile {
 // Loads one tile: SLOTS consecutive logical history pages of one KV head,
 // starting at logical page lp0.  The physical ids come from lanes idx0 ..
 // idx0+SLOTS-1 of `pids` (-1 = absent; idx0 < 0: no page at all), so every
-// code address is a uniform base plus the lane's record offset.  Records of absent pages are read from
-// physical page 0 (never used: their scales are zero and their logits
-// -inf); scale words of tokens that are not history tokens are zeroed, so
-// stale bits can never reach the arithmetic.
+// code address is a uniform base plus the lane's record offset.  Code records
+// of absent pages are not read (a zero-size buffer descriptor returns zeros);
+// their scale words are read from physical page 0 and, like those of tokens
+// that are not history tokens, zeroed, so stale bits can never reach the
+// arithmetic (an absent page's logits are -inf).
 template <int D, int NG, int GQA>
 __device__ __forceinline__ void i2_fetch(I2Tile<D, NG, GQA>& t, const uint8_t* __restrict__ hpool,
                                          size_t page_bytes, int pids, int idx0, int lp0, int hist_len, int my_slot,
@@ -405,7 +410,7 @@ __device__ __forceinline__ void i2_fetch(I2Tile<D, NG, GQA>& t, const uint8_t* _
 #pragma unroll
   for (int s = 0; s < C::SLOTS; ++s) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(hpool + (size_t)max(ids[s], 0) * page_bytes), (short)0, C::BLK2, kBufferFlags);
+        (void*)(hpool + (size_t)max(ids[s], 0) * page_bytes), (short)0, ids[s] >= 0 ? C::BLK2 : 0, kBufferFlags);
     if constexpr (D == 128) {
       const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * C::REC, 0, kKvPolicy);
       t.kw[s][0] = x[0];
@@ -716,21 +721,71 @@ __device__ __forceinline__ void b16_compute(const B16Tile<D, GQA>& t, Acc<D, 1>&
 }
 
 // -------------------------------------------------------- wave epilogue --
-// Reduce a wave's column states to one (o, lse) per query head and store it
-// in sm.part[wave].  INT2: channel of o[cb][i] is cb*16 + 4j + i and the
-// numerator is acc * unit_inv(cb) - Z (codebook: acc - Z).  BF16: channel
-// (4j + i) * D/16 + cb.
-template <int D, int NG, int GQA, bool INT2, bool LUT = false>
-__device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, int wave, int lane) {
-  constexpr int G = D / NG;
+// INT2 units: one (o, lse) per query head h from the wave's columns
+// s*GQA + h, which share one reference and so add without rescaling.  The
+// sum over slots goes through LDS (fewer instructions on the wave's critical
+// path than row rotations of every accumulator): each lane stores its raw
+// accumulators (column n, channels 16 cb + 4j .. +3) and its column's l, Z
+// and reference; then lane L sums and normalizes OPL consecutive channels of
+// head L / (64 / GQA).  The numerator is acc * unit_inv(cb) - Z (codebook:
+// acc - Z).  A wave's LDS accesses complete in issue order, so its own
+// stores are visible to its later loads; the wavefront fence only keeps the
+// compiler from reordering them.
+template <int D, int NG, int GQA, bool LUT>
+__device__ __forceinline__ void wave_finish_i2(Acc<D, NG>& st, Smem<D, GQA>& sm, int wave, int lane) {
+  using C = DC<D, NG, GQA>;
+  constexpr int G = D / NG, LPH = 64 / GQA, OPL = D / LPH, VW = OPL % 4 == 0 ? 4 : 2;
+  static_assert(OPL % VW == 0 && G % OPL == 0 && OPL <= 16, "outputs per lane within one scale group");
   const int n = lane & 15, j = lane >> 4;
   st.l = col_sum(st.l);
 #pragma unroll
   for (int g = 0; g < NG; ++g) st.Z[g] = col_sum(st.Z[g]);
-  const float mh = st.ref;  // shared by the head's columns (update_ref<GQA> / update_max<GQA>)
-  st.l = slot_sum<GQA>(st.l);
+  auto& F = sm.u.f;
+  if (n < C::COLS) {
 #pragma unroll
-  for (int g = 0; g < NG; ++g) st.Z[g] = slot_sum<GQA>(st.Z[g]);
+    for (int cbk = 0; cbk < D / 16; ++cbk) *(v4f*)&F.raw[wave][n][cbk * 16 + 4 * j] = st.o[cbk];
+    if (j == 0) {
+      F.lz[wave][n][0] = st.l;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) F.lz[wave][n][1 + g] = st.Z[g];
+      F.lz[wave][n][3] = st.ref;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const int h = lane / LPH, c0 = (lane % LPH) * OPL;
+  float l = 0.f, z = 0.f, acc[OPL];
+#pragma unroll
+  for (int s = 0; s < C::SLOTS; ++s) {
+    const int col = s * GQA + h;
+    l += F.lz[wave][col][0];
+    z += F.lz[wave][col][1 + c0 / G];
+#pragma unroll
+    for (int e = 0; e < OPL; e += VW) {
+      if constexpr (VW == 4) {
+        const v4f x = *(const v4f*)&F.raw[wave][col][c0 + e];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[e + k] = s ? acc[e + k] + x[k] : x[k];
+      } else {
+        const float2 x = *(const float2*)&F.raw[wave][col][c0 + e];
+        acc[e] = s ? acc[e] + x.x : x.x;
+        acc[e + 1] = s ? acc[e + 1] + x.y : x.y;
+      }
+    }
+  }
+  const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+  const float a = (LUT ? 1.f : pv_unit_inv(c0 / 16)) * inv, zb = z * inv;
+#pragma unroll
+  for (int e = 0; e < OPL; ++e) F.part[wave][h][c0 + e] = fmaf(acc[e], a, -zb);
+  if (lane % LPH == 0) F.part[wave][h][D] = l > 0.f ? F.lz[wave][h][3] + __log2f(l) : -INFINITY;
+}
+
+// BF16 units: the same reduction with row rotations; channel of o[cb][i] is
+// (4j + i) * D/16 + cb.
+template <int D, int GQA>
+__device__ __forceinline__ void wave_finish_b16(Acc<D, 1>& st, Smem<D, GQA>& sm, int wave, int lane) {
+  const int n = lane & 15, j = lane >> 4;
+  st.l = slot_sum<GQA>(col_sum(st.l));
+  const float mh = st.ref;  // shared by the head's columns (update_max<GQA>)
 #pragma unroll
   for (int cbk = 0; cbk < D / 16; ++cbk)
 #pragma unroll
@@ -738,24 +793,10 @@ __device__ __forceinline__ void wave_finish(Acc<D, NG>& st, Smem<D, GQA>& sm, in
   if (n < GQA) {
     const float inv = st.l > 0.f ? __builtin_amdgcn_rcpf(st.l) : 0.f;
 #pragma unroll
-    for (int cbk = 0; cbk < D / 16; ++cbk) {
+    for (int cbk = 0; cbk < D / 16; ++cbk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float o;
-        int c;
-        if constexpr (INT2) {
-          const int g = (cbk * 16) / G;
-          o = (LUT ? st.o[cbk][i] : st.o[cbk][i] * pv_unit_inv(cbk)) - st.Z[g];
-          o *= inv;
-          c = cbk * 16 + 4 * j + i;
-        } else {
-          o = st.o[cbk][i] * inv;
-          c = (4 * j + i) * (D / 16) + cbk;
-        }
-        sm.u.part[wave][n][c] = o;
-      }
-    }
-    if (j == 0) sm.u.part[wave][n][D] = st.l > 0.f ? mh + __log2f(st.l) : -INFINITY;
+      for (int i = 0; i < 4; ++i) sm.u.f.part[wave][n][(4 * j + i) * (D / 16) + cbk] = st.o[cbk][i] * inv;
+    if (j == 0) sm.u.f.part[wave][n][D] = st.l > 0.f ? mh + __log2f(st.l) : -INFINITY;
   }
 }
 
@@ -1164,7 +1205,8 @@ __global__ void __launch_bounds__(kThreads)
         run(std::false_type{});
     }
     ps.at(5);
-    wave_finish<D, NG, GQA, true, LUT>(st, sm, wave, lane);
+    wave_finish_i2<D, NG, GQA, LUT>(st, sm, wave, lane);
+    ps.at(13);
   } else {
     // ------------------------------------------- BF16 unit (sink + recent)
     constexpr int SB = C::SLOTS_B;
@@ -1200,22 +1242,9 @@ __global__ void __launch_bounds__(kThreads)
       cur = nt;
       tile = nxt;
     }
-    Acc<D, NG> st2;  // widen to the common epilogue type
-    if constexpr (NG == 1) {
-      st2 = st;
-    } else {
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i) st2.o[i] = st.o[i];
-      st2.m = st.m;
-      st2.l = st.l;
-      st2.E = st.E;
-      st2.ref = st.ref;
-      st2.slim = st.slim;
-#pragma unroll
-      for (int g = 0; g < NG; ++g) st2.Z[g] = 0.f;
-    }
     ps.at(5);
-    wave_finish<D, NG, GQA, false>(st2, sm, wave, lane);
+    wave_finish_b16<D, GQA>(st, sm, wave, lane);
+    ps.at(13);
   }
   __syncthreads();
   ps.at(6);
@@ -1227,15 +1256,15 @@ __global__ void __launch_bounds__(kThreads)
     const int h = idx / D, c = idx % D;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.u.part[w][h][D]);
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.u.f.part[w][h][D]);
     float o = 0.f, lse = -INFINITY;
     if (mx > -INFINITY) {
       float sw = 0.f, so = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float e = __builtin_amdgcn_exp2f(sm.u.part[w][h][D] - mx);
+        const float e = __builtin_amdgcn_exp2f(sm.u.f.part[w][h][D] - mx);
         sw += e;
-        so += e * sm.u.part[w][h][c];
+        so += e * sm.u.f.part[w][h][c];
       }
       o = so * __builtin_amdgcn_rcpf(sw);
       lse = mx + __log2f(sw);  // log2 units
@@ -1261,7 +1290,10 @@ __global__ void __launch_bounds__(kThreads)
     const uint32_t prev = __hip_atomic_fetch_add(p.counters + head_base * kCounterStride, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == (uint32_t)(total - 1);
+    asm volatile("" ::"v"(last) : "memory");  // the ticket has returned before the stamp
+    ps.at(14);
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    ps.at(15);
     sm.last = last;
   }
   __syncthreads();
@@ -1278,12 +1310,13 @@ __global__ void __launch_bounds__(kThreads)
   // head).  Per batch of 32 partials the lane's 32 partial values and the
   // head's 32 lse values (lane k holds partial ub + k) are requested
   // together, one memory round trip; max, weights and sum then come from
-  // wave reductions and each weight reaches every lane by readlane.  Partial
+  // wave reductions and each weight reaches every lane through LDS.  Partial
   // rows are read through a buffer descriptor with the partial's offset in
   // the scalar operand.  Entries past the range carry weight 0 and re-read
   // the last partial, in bounds.
   auto fold = [&](int h_lane, int c, int u0, int u1, float& M, float& S, float& A) {
     const int h = __builtin_amdgcn_readfirstlane(h_lane);
+    float* wb = &sm.u.f.lz[wave][0][0];       // 32 weights of the current batch
     const float* lsrc = p.part_lse + p0 + h;  // partial u at lsrc[u * GQA]
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.part_o + (p0 + h) * D), (short)0, (head_slots * GQA - h) * D * 4, kBufferFlags);
@@ -1305,9 +1338,17 @@ __global__ void __launch_bounds__(kThreads)
         const float w = __builtin_amdgcn_exp2f(e - mb);  // 0 past the range
         S = S * f + wave_sum(w);
         A *= f;
+        // the 32 weights reach every lane through the wave's own LDS words
+        // (broadcast reads), in the order of a per-weight readlane
+        if (lane < 32) wb[lane] = w;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-        for (int k = 0; k < 32; ++k)
-          A = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k)), o[k], A);
+        for (int k = 0; k < 32; k += 4) {
+          const v4f wk = *(const v4f*)&wb[k];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) A = fmaf(wk[i], o[k + i], A);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         M = mb;
       }
     }
@@ -1326,7 +1367,7 @@ __global__ void __launch_bounds__(kThreads)
     // then merged with the BF16 units' partials, which hold V itself.
     constexpr int PER = (GQA * D + kThreads - 1) / kThreads;
     float M1[PER], S1[PER], A1[PER], M2[PER], S2[PER];
-    float* a2 = &sm.u.part[0][0][0];  // [GQA][D] INT2 merge, rotated basis
+    float* a2 = &sm.u.f.part[0][0][0];  // [GQA][D] INT2 merge, rotated basis
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int idx = tid + k * kThreads;
