@@ -738,6 +738,30 @@ PHASES = ["start", "first tiles requested", "q' partial barrier", "q' split barr
           "ticket returned (wave 0)", "acquire done (wave 0)"]
 
 
+def int2_workgroup_phases(st, rel, wg_used):
+    """Medians over the INT2 workgroups of a stamped step, each on its own
+    clock (the workgroups of a plan with several rounds start at different
+    times): first tile request, first score MFMA, loop end and ticket, in us
+    after the workgroup's start, and the share of the workgroup's life spent
+    before its first score MFMA and after its loop."""
+    import warnings
+    import numpy as np
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", RuntimeWarning)  # rows of unused workgroups are all NaN
+
+        def pt(k):
+            return np.where(st[:, :, k] > 0, rel[:, :, k], np.nan)
+        wstart = np.nanmin(pt(0), axis=1)
+        int2 = wg_used & np.isfinite(pt(4)).any(axis=1)
+
+        def med(k, reduce):
+            v = reduce(pt(k), axis=1) - wstart
+            return round(float(np.nanmedian(v[int2])), 2)
+        mfma, lend, tick = med(4, np.nanmedian), med(5, np.nanmax), med(8, np.nanmax)
+        return {"workgroups": int(int2.sum()), "first_request": med(1, np.nanmedian), "first_score_mfma": mfma,
+                "loop_end": lend, "ticket": tick, "fixed_share": round((mfma + tick - lend) / tick, 3)}
+
+
 def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
     """Per-wave phase times of one cold decode step (plain decode, host-length
     plan) from the profiling build (s_memrealtime at fixed points of
@@ -791,6 +815,7 @@ def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
     dur_wg = np.nanmax(ends[wg_used], axis=1) - np.nanmin(starts[wg_used], axis=1)
     per_wg["wg_duration_us"] = {"min": round(float(np.nanmin(dur_wg)), 2), "median": round(float(np.nanmedian(dur_wg)), 2),
                                 "max": round(float(np.nanmax(dur_wg)), 2)}
+    per_wg["int2_workgroup_us"] = int2_workgroup_phases(st, rel, wg_used)
     res = {"workload": wl.name, "steps": steps, "step_us": round(ms * 1e3, 3), "phases": rows, "workgroups": per_wg,
            "fold_end_per_head_us": sorted(round(float(x), 2) for x in rel[folded, 0, 9]),
            "wg_loop_end_us": {"min": round(float(np.nanmin(np.nanmax(loop_end[wg_used], axis=1))), 2),
@@ -811,6 +836,10 @@ def phase_timeline(steps, warmup, workload="qwen3-8b-l100k"):
             f"p90 {r['p90']:6.2f} max {r['max']:6.2f}")
     log("  last workgroups (median over heads of the latest wave): " +
         ", ".join(f"{k}: {v:.2f}" for k, v in fold_pts.items()))
+    w = per_wg["int2_workgroup_us"]
+    log(f"  INT2 workgroups on their own clocks ({w['workgroups']}, medians): first request {w['first_request']:.2f}, "
+        f"first score MFMA {w['first_score_mfma']:.2f}, loop end {w['loop_end']:.2f}, ticket {w['ticket']:.2f} us; "
+        f"start-to-first-MFMA plus loop-end-to-ticket = {100 * w['fixed_share']:.1f} % of the workgroup's life")
     return res
 
 
