@@ -1,5 +1,6 @@
 """CPU tests of bench.py's host side: the one-GPU guard, the oracle baseline
-record it prints, and the profiling build's stamp layout it reads."""
+record it prints, the profiling build's stamp layout it reads and the
+per-workgroup phase figures it derives from the stamps."""
 
 import os
 import re
@@ -37,3 +38,24 @@ def test_stamp_layout_matches_the_library():
     assert vals == {"kStampSlots": bench.STAMP_SLOTS, "kStampWgs": bench.STAMP_WGS, "kStampWaves": bench.STAMP_WAVES}
     # every named phase point fits the per-wave slots
     assert len(bench.PHASES) <= bench.STAMP_SLOTS
+
+
+def test_workgroup_phases_on_own_clocks():
+    # two INT2 workgroups starting 30 us apart and one BF16 workgroup (no
+    # score MFMA stamp): medians are taken on each workgroup's own clock
+    import numpy as np
+    wgs, waves, slots = 4, bench.STAMP_WAVES, bench.STAMP_SLOTS
+    st = np.zeros((wgs, waves, slots))
+    for w, t0 in ((0, 100.0), (1, 3100.0)):  # 100 MHz ticks
+        st[w, :, 0] = t0 + np.arange(waves)   # wave starts
+        st[w, :, 1] = t0 + 200                # first request at +2 us
+        st[w, :, 4] = t0 + 500                # first score MFMA at +5 us
+        st[w, :, 5] = t0 + 2000 + np.arange(waves) * 10  # loop end, latest at +20.7 us
+        st[w, :, 8] = t0 + 2300               # ticket at +23 us
+    st[2, :, 0], st[2, :, 5], st[2, :, 8] = 150, 700, 800  # a BF16 unit
+    used = st[:, :, 0] > 0
+    rel = (st - st[:, :, 0][used].min()) * 1e-2
+    r = bench.int2_workgroup_phases(st, rel, used.any(axis=1))
+    assert r["workgroups"] == 2
+    assert (r["first_request"], r["first_score_mfma"], r["loop_end"], r["ticket"]) == (2.0, 5.0, 20.7, 23.0)
+    assert r["fixed_share"] == round((5.0 + 23.0 - 20.7) / 23.0, 3)
