@@ -498,7 +498,9 @@ constexpr float kBiasLut = 16.f;  // codebook operands: 16 + L[code]
 constexpr uint32_t kLutHigh = 0x4C4C4C4Cu, kLutSel = 0x04000400u;
 template <int BB, int I>
 __device__ __forceinline__ uint32_t lut_operand(uint32_t x, uint32_t lut_v) {
-  const uint32_t sel = ((x >> (4 * BB + 2 * I)) & 0x00030003u) | kLutSel;
+  // selector (x >> shift) & 0x00030003 | kLutSel in one three-input bit
+  // operation (truth table 0xEA: (a & b) | c)
+  const uint32_t sel = __builtin_amdgcn_bitop3_b32(x >> (4 * BB + 2 * I), 0x00030003u, kLutSel, 0xEA);
   return __builtin_amdgcn_perm(kLutHigh, lut_v, sel);
 }
 
