@@ -143,6 +143,32 @@ def test_decode_deterministic_and_workspace_reusable(gpu_lib):
     assert int(ws[: 128 * wl.batch * wl.num_kv_heads].view(torch.int32).abs().sum()) == 0
 
 
+@pytest.mark.parametrize("bf16_pages_per_unit", [None, "8"])
+@pytest.mark.parametrize("name", ["d64-gqa8-ragged", "d128-gqa4-ragged", "d128-gqa4-long"])
+def test_decode_multi_round_plan(gpu_lib, name, bf16_pages_per_unit, monkeypatch):
+    """A plan of 340-620 workgroups (the planner aimed at 1,024), i.e. more
+    than the GPU's CUs: the workgroup order that runs each XCD's INT2 chunks
+    before its BF16 units, with one or three BF16 units per (sequence, KV
+    head) and, in the ragged cases, chunks past a sequence's own history that
+    exit at once.  Repeated calls are bitwise equal."""
+    monkeypatch.setenv("OSCAR_TARGET_WGS", "1024")
+    if bf16_pages_per_unit:
+        monkeypatch.setenv("OSCAR_BF16_PAGES_PER_UNIT", bf16_pages_per_unit)
+    wl = CASES[name]
+    log(f"case {name}: multi-round plan, BF16 pages per unit {bf16_pages_per_unit or 'default'}")
+    inp = draw_inputs(wl)
+    seqs = make_seqs(wl, inp)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    out, (pool, dev, lens, ws, max_len) = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
+    check_decode(out, ref, what=f"{name} (multi-round plan)")
+    again = torch.zeros_like(out)
+    gpu_lib.oscar_decode_attention(pool, inp.q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"],
+                                   dev["bf16_pool"], dev["int2_pool"], to_dev(inp.calib.r_k), again, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+
+
 def test_decode_full_size_headline_sampled(gpu_lib):
     """Qwen3-8B-shaped layer at 100,000 tokens, in the launch configuration
     bench.py times; the oracle computes a sample of query heads."""
