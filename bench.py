@@ -93,6 +93,8 @@ def parse():
     ap.add_argument("--workload", default="qwen3-8b-l100k")
     ap.add_argument("--cold-bytes", type=float, default=2 * 2**30)
     ap.add_argument("--repeats", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=1e3 * SETTLE_S,
+                    help="untimed back-to-back runs of the timed steps before each measurement")
     ap.add_argument("--no-bf16", action="store_true", help="skip the BF16-only comparator")
     ap.add_argument("--no-codebook", action="store_true", help="skip the four-level codebook variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -435,8 +437,17 @@ def bench_batch_comparator(oscar, name, steps, warmup, repeats, cold_bytes, min_
             "int2_speedup": round(ms16 / ms2, 3)}
 
 
+SETTLE_S = 0.05
+
+
 def time_steps(step, n_steps, warmup, repeats, use_graph=True):
-    """Median and min ms per step over `repeats` runs of n_steps steps."""
+    """Median and min ms per step over `repeats` runs of n_steps steps.
+
+    After the `warmup` eager steps (and the graph capture) the same n_steps
+    steps run untimed, back to back, for SETTLE_S seconds before the timed
+    runs: the first ~10 ms of decode work after the GPU idled (pool building
+    is mostly host work) run up to 7 % slower than the steady state that a
+    serving loop sees, whatever the number of steps per replay."""
     import torch
     stream = torch.cuda.current_stream()
     for i in range(warmup):
@@ -452,8 +463,19 @@ def time_steps(step, n_steps, warmup, repeats, use_graph=True):
                 for i in range(n_steps):
                     step(warmup + i)
         torch.cuda.synchronize()
-        graph.replay()
+    t_end = time.perf_counter() + SETTLE_S
+    n_settle = 0
+    while True:
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(n_steps):
+                step(warmup + i)
         torch.cuda.synchronize()
+        n_settle += 1
+        if time.perf_counter() >= t_end:
+            break
+    log(f"timing: {warmup} warm-up steps, {n_settle} untimed runs of {n_steps} steps, {repeats} timed runs")
     times = []
     for _ in range(repeats):
         a = torch.cuda.Event(enable_timing=True)
@@ -857,7 +879,9 @@ def copy_probe(nbytes):
 
 
 def main():
+    global SETTLE_S
     args = parse()
+    SETTLE_S = args.settle_ms * 1e-3
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -951,7 +975,8 @@ def main():
                    "head_dim": wl.head_dim, "group_size": wl.group_size, "context": list(wl.seq_lens)[:4],
                    "sink": wl.sink, "recent": wl.recent, "page_size": 16, "pool_copies": n_copies,
                    "timing": "HIP-graph replay of the timed steps, cold cache: rotating over per-layer pool "
-                             "copies that share the sequence's page tables"},
+                             "copies that share the sequence's page tables; the same replay runs untimed, back "
+                             f"to back, for {args.settle_ms:g} ms before the timed replays"},
         "tokens_per_s": round(wl.batch / (ms * 1e-3), 1),
         "kv_tokens_scanned_per_s": round(sum(wl.seq_lens) / (ms * 1e-3), 1),
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
