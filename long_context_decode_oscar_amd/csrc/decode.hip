@@ -815,6 +815,14 @@ struct CascArg {};
 template <>
 struct CascArg<true> : CascArgs {};
 
+// x / d for 0 <= x < 2^24 and 1 <= d < 2^24: the masks let the compiler use
+// its short division (a float reciprocal and one correction) in place of the
+// full 32-bit sequence; the workgroup's unit decoding sits on the path to its
+// first page-table request
+__device__ __forceinline__ int div24(int x, int d) {
+  return (int)(((uint32_t)x & 0xFFFFFFu) / ((uint32_t)d & 0xFFFFFFu));
+}
+
 #ifndef OSCAR_LPT_MIN
 #define OSCAR_LPT_MIN 256
 #endif
@@ -826,7 +834,7 @@ struct CascArg<true> : CascArgs {};
 // CUs that finish early (measured 127-130 against 132-136 us per step of a
 // 32 x 32K-token batch, whose 1,024 chunks and 256 BF16 units run in five
 // rounds).  Returns the logical unit of workgroup bid for n units, U per
-// (sequence, KV head), the first nb of them BF16 units.
+// (sequence, KV head), the first nb of them BF16 units; n < 2^24.
 __device__ __forceinline__ int longest_first(int bid, int n, int U, int nb) {
   constexpr int kXcd = 8;
   const int q = n / kXcd, r = n % kXcd;
@@ -837,15 +845,15 @@ __device__ __forceinline__ int longest_first(int bid, int n, int U, int nb) {
   if (nb <= 0 || C <= 0) return a + idx;
   // INT2 units among the units [0, x)
   auto count_int2 = [&](int x) {
-    const int pq = x / U;
+    const int pq = div24(x, U);
     return pq * C + max(x - pq * U - nb, 0);
   };
   const int ia = count_int2(a), ni = count_int2(a + len) - ia;
   if (idx < ni) {
-    const int rk = ia + idx, pq = rk / C;
+    const int rk = ia + idx, pq = div24(rk, C);
     return pq * U + nb + (rk - pq * C);
   }
-  const int rb = (a - ia) + idx - ni, pq = rb / nb;
+  const int rb = (a - ia) + idx - ni, pq = div24(rb, nb);
   return pq * U + (rb - pq * nb);
 }
 // The leading scalar arguments are everything the first page-table and R_K
@@ -917,10 +925,18 @@ __global__ void __launch_bounds__(kThreads)
     slot0 = sb + kvh * head_slots;
   } else {
     U = units_per_head;
-    if (!BF16_ONLY && grid_n > OSCAR_LPT_MIN) lin = longest_first(blockIdx.x, grid_n, U, n_bf16_units);
-    u = lin % U;
-    kvh = (lin / U) % num_kv_heads;
-    b = lin / (U * num_kv_heads);
+    if (!BF16_ONLY && grid_n > OSCAR_LPT_MIN && grid_n < (1 << 24))
+      lin = longest_first(blockIdx.x, grid_n, U, n_bf16_units);
+    if (grid_n < (1 << 24)) {
+      const int pair = div24(lin, U);
+      u = lin - pair * U;
+      b = div24(pair, num_kv_heads);
+      kvh = pair - b * num_kv_heads;
+    } else {
+      u = lin % U;
+      kvh = (lin / U) % num_kv_heads;
+      b = lin / (U * num_kv_heads);
+    }
     head_slots = p.slots_per_head;
     slot0 = (b * num_kv_heads + kvh) * head_slots;
   }
@@ -998,7 +1014,9 @@ __global__ void __launch_bounds__(kThreads)
     end = (u == chunks - 1) ? npages : min(first + pages_per_chunk, npages);
   } else {
     const int own_pages = max(hist_pages - S_u, 0);
-    const int chunks = min((own_pages + pages_per_chunk - 1) / pages_per_chunk, max_chunks);
+    const int chunks = min(own_pages < (1 << 23) ? div24(own_pages + pages_per_chunk - 1, pages_per_chunk)
+                                                 : (own_pages + pages_per_chunk - 1) / pages_per_chunk,
+                           max_chunks);
     total = n_bf16_units + chunks;
     if (u < n_bf16_units) {
       const int nlist = n_sp + n_rp;
@@ -1359,43 +1377,61 @@ __global__ void __launch_bounds__(kThreads)
     M = -INFINITY;
     S = 0.f;
     A = 0.f;
-    for (int ub = u0; ub < u1; ub += 32) {
+    auto batch = [&](int ub) {
+      // the lse values first (every lane loads, in range), so that the
+      // weights are formed while the rows arrive
+      const int uu = ub + lane;
+      const float ev = lsrc[(size_t)min(uu, u1 - 1) * GQA];
+      // -inf past the range: an add rather than a select, which the
+      // compiler would turn into a branch that the load sinks into
+      const float e = ev + ((lane < 32 && uu < u1) ? 0.f : -INFINITY);
       float o[32];
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
         const int ui = min(ub + k, u1 - 1);
         o[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ors, c * 4, ui * GQA * D * 4, 0));
       }
-      const int uu = ub + lane;
-      const float e = (lane < 32 && uu < u1) ? lsrc[(size_t)uu * GQA] : -INFINITY;
+      // no branch on an empty batch (its weights are all 0), so that the
+      // row loads stay ahead of the weights instead of sinking behind them
       const float mb = fmaxf(M, wave_max(e));
-      if (mb > -INFINITY) {
-        const float f = __builtin_amdgcn_exp2f(M - mb);  // 0 while M = -inf
-        const float w = __builtin_amdgcn_exp2f(e - mb);  // 0 past the range
-        S = S * f + wave_sum(w);
-        A *= f;
-        // the 32 weights reach every lane through the wave's own LDS words
-        // (broadcast reads), in the order of a per-weight readlane
-        if (lane < 32) wb[lane] = w;
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const float ref = mb > -INFINITY ? mb : 0.f;
+      const float f = __builtin_amdgcn_exp2f(M - ref);  // 0 while M = -inf
+      const float w = __builtin_amdgcn_exp2f(e - ref);  // 0 past the range
+      S = S * f + wave_sum(w);
+      A *= f;
+      // the 32 weights reach every lane through the wave's own LDS words
+      // (broadcast reads), in the order of a per-weight readlane
+      if (lane < 32) wb[lane] = w;
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-        for (int k = 0; k < 32; k += 4) {
-          const v4f wk = *(const v4f*)&wb[k];
+      for (int k = 0; k < 32; k += 4) {
+        const v4f wk = *(const v4f*)&wb[k];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) A = fmaf(wk[i], o[k + i], A);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        M = mb;
+        for (int i = 0; i < 4; ++i) A = fmaf(wk[i], o[k + i], A);
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      M = mb;
+    };
+    // one batch (the common case) as straight-line code: a loop would make
+    // the compiler wait for the lse load before issuing the rows
+    if (u1 - u0 > 32) {
+      for (int ub = u0; ub < u1; ub += 32) batch(ub);
+    } else if (u1 > u0) {
+      batch(u0);
     }
   };
   uint16_t* outp = p.out + ((size_t)b * hq + kvh * GQA) * D;
   if (BF16_ONLY || p.r_v == nullptr) {
-    for (int idx = tid; idx < GQA * D; idx += kThreads) {
+    auto fold_out = [&](int idx) {
       const int h = idx / D, c = idx % D;
       float M, S, A;
       fold(h, c, 0, total + cch, M, S, A);
       outp[h * D + c] = (uint16_t)f32_to_bf16(S > 0.f ? A * __builtin_amdgcn_rcpf(S) : 0.f);
+    };
+    if constexpr (GQA * D == kThreads) {
+      fold_out(tid);
+    } else {
+      for (int idx = tid; idx < GQA * D; idx += kThreads) fold_out(idx);
     }
   } else {
     // Values not absorbed: the INT2 partials hold V R_V.  Their merge is
