@@ -131,6 +131,7 @@ struct Smem {
   int sig3[GQA * 2];                 // sum(65536 a + 256 b + c) per head and group
   int dom[GQA];                      // 1: the head's q' has a dominant channel (three terms)
   int last;
+  uint32_t qsync;                    // q' partials written (waves of the q' prologue)
 };
 
 // ---------------------------------------------------------------- helpers --
@@ -877,6 +878,14 @@ __global__ void __launch_bounds__(kThreads)
   int lin = xcd_remap(blockIdx.x, grid_n);
   PhaseStamps ps;
   ps.at(0);
+  // With GQA <= kWaves / 2 the q' prologue runs on waves 0 .. kWaves/2 - 1
+  // only, which meet at an LDS counter instead of a workgroup barrier; the
+  // counter starts at zero before any wave can reach it.
+  constexpr bool kQHalf = !BF16_ONLY && GQA <= kWaves / 2;
+  if constexpr (kQHalf) {
+    if (tid == 0) sm.qsync = 0u;
+    __syncthreads();
+  }
   // this workgroup's (sequence, KV head, unit), its head's units U and
   // partial slots [slot0, slot0 + head_slots)
   int U, u, kvh, b, head_slots, slot0;
@@ -958,8 +967,12 @@ __global__ void __launch_bounds__(kThreads)
       }
   }
   constexpr int TPB = 64 / C::SLOTS;  // tiles whose page ids one VGPR holds
-  constexpr int CG = D / 4, RS = kThreads / CG, RPS = D / RS;
+  // threads of the q' prologue: thread (rs, cg) owns rows [rs*RPS, rs*RPS +
+  // RPS) of R_K and output channels 4cg .. 4cg+3 of q' = q R_K
+  constexpr int QWAVES = kQHalf ? kWaves / 2 : kWaves;
+  constexpr int CG = D / 4, RS = 64 * QWAVES / CG, RPS = D / RS;
   const int cg = tid % CG, rs = tid / CG;
+  const bool qwave = wave < QWAVES;
   const bool int2_planned = !BF16_ONLY && u >= n_bf16_units;
   const int c_int2 = u - n_bf16_units;
   int pid_raw = -1;
@@ -971,23 +984,31 @@ __global__ void __launch_bounds__(kThreads)
     const int lp = S_u + c_int2 * pages_per_chunk + (wave + i * kWaves) * C::SLOTS + s;
     const int pend = min(S_u + (c_int2 + 1) * pages_per_chunk, int2_pt_stride);
     if (lp < pend) pid_raw = int2_pt_all[(size_t)b * int2_pt_stride + lp];
-    // thread (rs, cg) owns rows [rs*RPS, rs*RPS + RPS) of R_K and output
-    // channels 4cg .. 4cg+3 of q' = q R_K
-    const float* rbase = r_k + (size_t)kvh * D * D + (size_t)(rs * RPS) * D + 4 * cg;
+    if (qwave) {
+      const float* rbase = r_k + (size_t)kvh * D * D + (size_t)(rs * RPS) * D + 4 * cg;
 #pragma unroll
-    for (int r = 0; r < RPS; ++r) rr[r] = *(const float4*)(rbase + (size_t)r * D);
-    const uint16_t* qb = qin + ((size_t)b * hq + kvh * GQA) * D + rs * RPS;
+      for (int r = 0; r < RPS; ++r) rr[r] = *(const float4*)(rbase + (size_t)r * D);
+      // the thread's RPS consecutive q channels of each head
+      const uint16_t* qb = qin + ((size_t)b * hq + kvh * GQA) * D + rs * RPS;
 #pragma unroll
-    for (int h = 0; h < GQA; ++h) {
-      if constexpr (RPS == 8) {
-        const uint4 x = *(const uint4*)(qb + h * D);
-        qq[h][0] = x.x;
-        qq[h][1] = x.y;
-        qq[h][2] = x.z;
-        qq[h][3] = x.w;
-      } else {
-        static_assert(RPS == 2, "row split");
-        qq[h][0] = *(const uint32_t*)(qb + h * D);
+      for (int h = 0; h < GQA; ++h) {
+        if constexpr (RPS % 8 == 0) {
+#pragma unroll
+          for (int k = 0; k < RPS / 8; ++k) {
+            const uint4 x = *(const uint4*)(qb + h * D + 8 * k);
+            qq[h][4 * k] = x.x;
+            qq[h][4 * k + 1] = x.y;
+            qq[h][4 * k + 2] = x.z;
+            qq[h][4 * k + 3] = x.w;
+          }
+        } else if constexpr (RPS == 4) {
+          const uint2 x = *(const uint2*)(qb + h * D);
+          qq[h][0] = x.x;
+          qq[h][1] = x.y;
+        } else {
+          static_assert(RPS == 2, "row split");
+          qq[h][0] = *(const uint32_t*)(qb + h * D);
+        }
       }
     }
   }
@@ -1068,38 +1089,53 @@ __global__ void __launch_bounds__(kThreads)
       v4i* bqz = &sm.bq[0][0][0][0];
       for (int x = tid; x < C::SLOTS * 3 * C::KW * 64; x += kThreads) bqz[x] = v4i{0, 0, 0, 0};
     }
-    float qacc[GQA][4];
-#pragma unroll
-    for (int h = 0; h < GQA; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qacc[h][e] = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPS; ++i) {
-#pragma unroll
-      for (int h = 0; h < GQA; ++h) {
-        const float qv = (i & 1) ? bf16_hi(qq[h][i >> 1]) : bf16_lo(qq[h][i >> 1]);
-        qacc[h][0] = fmaf(qv, rr[i].x, qacc[h][0]);
-        qacc[h][1] = fmaf(qv, rr[i].y, qacc[h][1]);
-        qacc[h][2] = fmaf(qv, rr[i].z, qacc[h][2]);
-        qacc[h][3] = fmaf(qv, rr[i].w, qacc[h][3]);
-      }
-    }
-    ps.at(11);
-    // sum the row segments held by this wave (lanes with equal cg)
-    static_assert(CG == 16 || CG == 32, "one or two row segments per 32 lanes");
-#pragma unroll
-    for (int h = 0; h < GQA; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (CG == 16) qacc[h][e] = xor16_add(qacc[h][e]);
-        qacc[h][e] = xor32_add(qacc[h][e]);
-      }
-    if (lane < CG) {
+    if (qwave) {
+      float qacc[GQA][4];
 #pragma unroll
       for (int h = 0; h < GQA; ++h)
-        *(float4*)&sm.u.qpart[wave][h][4 * cg] = float4{qacc[h][0], qacc[h][1], qacc[h][2], qacc[h][3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qacc[h][e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPS; ++i) {
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) {
+          const float qv = (i & 1) ? bf16_hi(qq[h][i >> 1]) : bf16_lo(qq[h][i >> 1]);
+          qacc[h][0] = fmaf(qv, rr[i].x, qacc[h][0]);
+          qacc[h][1] = fmaf(qv, rr[i].y, qacc[h][1]);
+          qacc[h][2] = fmaf(qv, rr[i].z, qacc[h][2]);
+          qacc[h][3] = fmaf(qv, rr[i].w, qacc[h][3]);
+        }
+      }
+      ps.at(11);
+      // sum the row segments held by this wave (lanes with equal cg)
+      static_assert(CG == 16 || CG == 32, "one or two row segments per 32 lanes");
+#pragma unroll
+      for (int h = 0; h < GQA; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (CG == 16) qacc[h][e] = xor16_add(qacc[h][e]);
+          qacc[h][e] = xor32_add(qacc[h][e]);
+        }
+      if (lane < CG) {
+#pragma unroll
+        for (int h = 0; h < GQA; ++h)
+          *(float4*)&sm.u.qpart[wave][h][4 * cg] = float4{qacc[h][0], qacc[h][1], qacc[h][2], qacc[h][3]};
+      }
     }
-    __syncthreads();
+    if constexpr (kQHalf) {
+      // waves 0 .. QWAVES-1 meet here; the others go on to the split barrier
+      // (their tile requests, scalar work queued behind that of the lower
+      // waves, no longer hold the q' sums back)
+      if (qwave) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) __hip_atomic_fetch_add(&sm.qsync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        while (__hip_atomic_load(&sm.qsync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (uint32_t)QWAVES)
+          __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      }
+    } else {
+      __syncthreads();
+    }
     ps.at(2);
     if (wave < GQA) {
       // wave h finishes query head h: lane owns channels CPL*lane + e
@@ -1110,7 +1146,7 @@ __global__ void __launch_bounds__(kThreads)
       for (int e = 0; e < CPL; ++e) {
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) v += sm.u.qpart[w][h][CPL * lane + e];
+        for (int w = 0; w < QWAVES; ++w) v += sm.u.qpart[w][h][CPL * lane + e];
         x[e] = v;
       }
       int ta[CPL], tb[CPL], tc[CPL];
