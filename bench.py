@@ -754,7 +754,7 @@ def bench_calibration(oscar, steps=10, warmup=2, repeats=5, profile_launches=0):
 # the profiling build's stamp area (kStampSlots, kStampWaves, kStampWgs in
 # the library's kernels.h): slots per wave, waves per workgroup, workgroups
 STAMP_SLOTS, STAMP_WAVES, STAMP_WGS = 16, 8, 2048
-PHASES = ["start", "first tiles requested", "q' partial barrier", "q' split barrier", "first score MFMAs issued",
+PHASES = ["start", "first tiles requested", "q' partials ready", "q' split barrier", "first score MFMAs issued",
           "loop end", "wave merge barrier", "partial stores acknowledged", "ticket taken", "fold written", None,
           "q' FMAs done (R_K arrived)", "q' split written", "wave epilogue written to LDS",
           "ticket returned (wave 0)", "acquire done (wave 0)"]

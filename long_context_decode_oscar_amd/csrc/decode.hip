@@ -64,7 +64,7 @@ constexpr float kLazy = 8.0f;        // log2 slack before the running max is rai
 constexpr int kKvPolicy = 2;
 // Phase timeline of the profiling build.  Point k of wave w of logical
 // workgroup lin lands in stamps[(lin * kWaves + w) * kStampSlots + k]:
-// 0 start, 1 first tiles requested, 2 q' partial barrier, 3 q' split
+// 0 start, 1 first tiles requested, 2 q' partials ready, 3 q' split
 // barrier, 4 first score MFMAs issued, 5 loop end, 6 wave merge barrier,
 // 7 partial stores acknowledged, 8 ticket taken, 9 fold written (last
 // workgroup only), 10: 1 for the workgroup that folded, 11 q' FMAs done
