@@ -1155,20 +1155,57 @@ __global__ void __launch_bounds__(kThreads)
       int sg = 0, sg3 = 0;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
-        const int c = CPL * lane + e;
         sg += 256 * ta[e] + tb[e];
         sg3 += 65536 * ta[e] + 256 * tb[e] + tc[e];
-        // byte of channel c inside the transposed 16-byte operand of lane
-        // group c%64/16 (the unpacked K codes hold channel 4*b + k at byte
-        // 4*k + b)
-        const int w = c / 64, jj = (c % 64) / 16, m = c % 16;
-        const int byte = 4 * (m % 4) + m / 4;
+      }
+      // The B operand of lane group jj of 64-channel block w holds channels
+      // c = 64w + 16jj + m in transposed order, channel 4b + k at byte 4k + b
+      // (the order of the unpacked K codes), once per slot s at lane
+      // 16jj + s*GQA + h.
+      if constexpr (kQHalf) {
+        // the terms in channel order to LDS (the q' rows of waves
+        // QWAVES.. are unused), then one lane per (term, w, jj) block reads
+        // its 16 channels, transposes the 4 x 4 bytes and writes the block
+        // to every slot: no byte writes to shared 4-byte words
+        int8_t* stage = (int8_t*)&sm.u.qpart[QWAVES + h][0][0];
+        auto put = [&](int t, const int (&v)[CPL]) {
+          if constexpr (CPL == 2)
+            *(uint16_t*)&stage[t * D + 2 * lane] = (uint16_t)((v[0] & 0xff) | ((v[1] & 0xff) << 8));
+          else
+            stage[t * D + lane] = (int8_t)v[0];
+        };
+        put(0, ta);
+        put(1, tb);
+        put(2, tc);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        if (lane < 3 * C::KW * 4) {
+          const int t = lane / (C::KW * 4), w = (lane / 4) % C::KW, jj = lane % 4;
+          const v4i x = *(const v4i*)&stage[t * D + 64 * w + 16 * jj];
+          // x[i] holds channels 4i .. 4i+3; out[k] = bytes k of x[0..3]
+          const uint32_t lo01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
+          const uint32_t hi01 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
+          const uint32_t lo23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+          const uint32_t hi23 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+          const v4i blk = {(int)__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                           (int)__builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                           (int)__builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                           (int)__builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
 #pragma unroll
-        for (int s = 0; s < C::SLOTS; ++s) {
-          const int l = 16 * jj + s * GQA + h;
-          ((int8_t*)&sm.bq[s][0][w][l])[byte] = (int8_t)ta[e];
-          ((int8_t*)&sm.bq[s][1][w][l])[byte] = (int8_t)tb[e];
-          ((int8_t*)&sm.bq[s][2][w][l])[byte] = (int8_t)tc[e];
+          for (int s = 0; s < C::SLOTS; ++s) sm.bq[s][t][w][16 * jj + s * GQA + h] = blk;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          const int c = CPL * lane + e;
+          const int w = c / 64, jj = (c % 64) / 16, m = c % 16;
+          const int byte = 4 * (m % 4) + m / 4;
+#pragma unroll
+          for (int s = 0; s < C::SLOTS; ++s) {
+            const int l = 16 * jj + s * GQA + h;
+            ((int8_t*)&sm.bq[s][0][w][l])[byte] = (int8_t)ta[e];
+            ((int8_t*)&sm.bq[s][1][w][l])[byte] = (int8_t)tb[e];
+            ((int8_t*)&sm.bq[s][2][w][l])[byte] = (int8_t)tc[e];
+          }
         }
       }
       if constexpr (NG == 1) {
