@@ -24,6 +24,8 @@ CASES = {
                                                seed=5),
     "d64-gqa8-ragged": make_workload(TINY, num_q_heads=16, batch=2, seq_lens=(3000, 50), seed=6),
     "d128-gqa4-ragged": make_workload(QWEN, num_q_heads=8, num_kv_heads=2, batch=3, seq_lens=(1000, 5000, 333), seed=7),
+    "d128-g64-gqa4": make_workload(QWEN, num_q_heads=8, num_kv_heads=2, group_size=64, batch=2, seq_lens=(3100, 520),
+                                   seed=12),
     "d128-g64-gqa8": make_workload(QWEN, num_q_heads=16, num_kv_heads=2, group_size=64, batch=2, seq_lens=(4100, 700),
                                    seed=8),
     "d128-gqa2": make_workload(QWEN, num_q_heads=4, num_kv_heads=2, batch=1, seq_lens=(2500,), seed=9),
@@ -108,7 +110,7 @@ def test_decode_empty_sequences_give_zero_rows(gpu_lib):
     check_decode(out[[1, 3]], ref, what="non-empty sequences of a batch with empty ones")
 
 
-@pytest.mark.parametrize("name", ["d64-gqa2-boundary-lengths", "d128-gqa4-ragged", "d128-g64-gqa8"])
+@pytest.mark.parametrize("name", ["d64-gqa2-boundary-lengths", "d128-gqa4-ragged", "d128-g64-gqa4", "d128-g64-gqa8"])
 def test_decode_values_not_absorbed(gpu_lib, name):
     """v_absorbed = 0: the BF16 segments hold V, the history V R_V; decode
     rotates the merged history partial back by R_V^T."""
