@@ -861,7 +861,7 @@ __device__ __forceinline__ int longest_first(int bid, int n, int U, int nb) {
 // requests depend on (16 dwords): the build preloads them into scalar
 // registers at wave launch, so those requests are issued without waiting for
 // the argument block.
-template <int D, int NG, int GQA, bool BF16_ONLY, bool LUT, bool CASC, bool PACKED>
+template <int D, int NG, int GQA, bool BF16_ONLY, bool LUT, bool CASC, bool PACKED, bool IDS2 = false>
 __global__ void __launch_bounds__(kThreads)
     k_decode(const int32_t* __restrict__ int2_pt_all, const float* __restrict__ r_k, const uint16_t* __restrict__ qin,
              const int32_t* __restrict__ seq_lens, int grid_n, int units_per_head, int num_kv_heads,
@@ -967,6 +967,7 @@ __global__ void __launch_bounds__(kThreads)
       }
   }
   constexpr int TPB = 64 / C::SLOTS;  // tiles whose page ids one VGPR holds
+  static_assert((TPB & (TPB - 1)) == 0, "tiles per id batch: a power of two");
   // threads of the q' prologue: thread (rs, cg) owns rows [rs*RPS, rs*RPS +
   // RPS) of R_K and output channels 4cg .. 4cg+3 of q' = q R_K
   constexpr int QWAVES = kQHalf ? kWaves / 2 : kWaves;
@@ -975,7 +976,10 @@ __global__ void __launch_bounds__(kThreads)
   const bool qwave = wave < QWAVES;
   const bool int2_planned = !BF16_ONLY && u >= n_bf16_units;
   const int c_int2 = u - n_bf16_units;
-  int pid_raw = -1;
+  // IDS2: chunks of up to 2 * kIdBatch pages; a wave then holds the page
+  // ids of its tiles TPB .. 2*TPB-1 in a second register
+  constexpr int kIdBatch = 64 * kWaves;  // pages whose ids one register per wave holds
+  int pid_raw = -1, pid2_raw = -1;
   float4 rr[RPS];
   uint32_t qq[GQA][RPS / 2];
   if (int2_planned) {
@@ -984,6 +988,9 @@ __global__ void __launch_bounds__(kThreads)
     const int lp = S_u + c_int2 * pages_per_chunk + (wave + i * kWaves) * C::SLOTS + s;
     const int pend = min(S_u + (c_int2 + 1) * pages_per_chunk, int2_pt_stride);
     if (lp < pend) pid_raw = int2_pt_all[(size_t)b * int2_pt_stride + lp];
+    if constexpr (IDS2) {
+      if (lp + kIdBatch < pend) pid2_raw = int2_pt_all[(size_t)b * int2_pt_stride + lp + kIdBatch];
+    }
     if (qwave) {
       const float* rbase = r_k + (size_t)kvh * D * D + (size_t)(rs * RPS) * D + 4 * cg;
 #pragma unroll
@@ -1058,26 +1065,39 @@ __global__ void __launch_bounds__(kThreads)
     const int my_slot = (n < C::COLS) ? n / GQA : C::SLOTS;
     const int chd = n % GQA;
     const int ntiles = (end - first + C::SLOTS - 1) / C::SLOTS;
-    // tiles of this wave (at most TPB: the host bounds the chunk size)
-    const int nt_w = wave < ntiles ? min((ntiles - 1 - wave) / kWaves + 1, TPB) : 0;
+    // tiles of this wave (at most TPB, or 2 * TPB with IDS2: the host bounds
+    // the chunk size)
+    const int nt_w = wave < ntiles ? min((ntiles - 1 - wave) / kWaves + 1, IDS2 ? 2 * TPB : TPB) : 0;
     const size_t page_bytes = (size_t)num_kv_heads * C::BLK2;
     const uint8_t* __restrict__ hpool = int2_pool + (size_t)kvh * C::BLK2;
     // physical page ids of this wave's tiles wave + i*kWaves: lane i*SLOTS + s
     // holds slot s of tile i, -1 when absent or outside the history
-    int pids;
+    int pids, pids2 = -1;
     {
       const int i = lane / C::SLOTS, s = lane % C::SLOTS;
       const int lp = first + (wave + i * kWaves) * C::SLOTS + s;
       const bool ok = i < nt_w && lp < end && pid_raw >= 0 && pid_raw < int2_num_pages;
       pids = ok ? pid_raw : -1;
+      if constexpr (IDS2) {
+        const bool ok2 = i + TPB < nt_w && lp + kIdBatch < end && pid2_raw >= 0 && pid2_raw < int2_num_pages;
+        pids2 = ok2 ? pid2_raw : -1;
+      }
     }
 
     // ring of tiles in flight: the first R-1 tiles are requested before the
     // prologue computes q', so HBM is busy from the start
     I2Tile<D, NG, GQA> ring[R];
     auto fetch = [&](I2Tile<D, NG, GQA>& t, int i) {
+      // lane of the first id of tile i in `pids`
+      int id_lane = i * C::SLOTS;
+      if constexpr (IDS2) {
+        // the second batch of ids takes the place of the first once its
+        // last tile has been requested (tiles are requested in order)
+        if (i == TPB) pids = pids2;
+        id_lane = (i % TPB) * C::SLOTS;
+      }
       // tiles past this wave's last one read no page (all ids -1)
-      i2_fetch<D, NG, GQA>(t, hpool, page_bytes, pids, i < nt_w ? i * C::SLOTS : -1,
+      i2_fetch<D, NG, GQA>(t, hpool, page_bytes, pids, i < nt_w ? id_lane : -1,
                            first + (wave + i * kWaves) * C::SLOTS, hist_len, my_slot, lane);
     };
 #pragma unroll
@@ -2069,6 +2089,9 @@ __global__ void __launch_bounds__(256) k_merge(const MergeParams p) {
   for (int q = 0; q < PER; ++q) p.out[(size_t)row * D + lane * PER + q] = (uint16_t)f32_to_bf16(acc[q] * inv);
 }
 
+template <int D, int NG>
+constexpr bool kLongChunks = D == 128 && NG == 1;
+
 // the INT2 decode, with the prefix-unit bookkeeping compiled in only when
 // the call has prefix units (CASC), the codebook operands only for a
 // codebook pool (LUT) and the plan tables only for a length-aware plan
@@ -2077,21 +2100,32 @@ void launch_int2_t(const DecodeParams& p, const CascArgs* casc, const PackedPlan
                    hipStream_t stream) {
   CascArg<CASC> ca;
   if constexpr (CASC) static_cast<CascArgs&>(ca) = *casc;
-  auto go = [&](auto lut) {
-    constexpr bool L = decltype(lut)::value;
+  auto go = [&](auto lut, auto ids2) {
+    constexpr bool L = decltype(lut)::value, I2 = decltype(ids2)::value;
     if (packed) {
       PlanArg<true> pa;
       static_cast<PackedPlanArgs&>(pa) = *packed;
-      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, true>), dim3(grid), dim3(kThreads), 0, stream, DECODE_LEAD_ARGS(p, grid), p, p.bf16_pt, p.bf16_pool, p.int2_pool, ca, pa);
+      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, true, I2>), dim3(grid), dim3(kThreads), 0, stream, DECODE_LEAD_ARGS(p, grid), p, p.bf16_pt, p.bf16_pool, p.int2_pool, ca, pa);
     } else {
-      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, false>), dim3(grid), dim3(kThreads), 0, stream, DECODE_LEAD_ARGS(p, grid), p, p.bf16_pt, p.bf16_pool, p.int2_pool, ca,
+      hipLaunchKernelGGL((k_decode<D, NG, GQA, false, L, CASC, false, I2>), dim3(grid), dim3(kThreads), 0, stream, DECODE_LEAD_ARGS(p, grid), p, p.bf16_pt, p.bf16_pool, p.int2_pool, ca,
                          PlanArg<false>{});
     }
   };
-  if (p.lut)
-    go(std::true_type{});
-  else
-    go(std::false_type{});
+  auto go_lut = [&](auto ids2) {
+    if (p.lut)
+      go(std::true_type{}, ids2);
+    else
+      go(std::false_type{}, ids2);
+  };
+  // chunks longer than one batch of page ids per wave (the planner allows
+  // them at D = 128 with one scale group per head)
+  if constexpr (kLongChunks<D, NG>) {
+    if (p.pages_per_chunk > 64 * kWaves) {
+      go_lut(std::true_type{});
+      return;
+    }
+  }
+  go_lut(std::false_type{});
 }
 
 template <int D, int NG, int GQA>

@@ -77,6 +77,13 @@ struct Plan {
 
 int slots_for(int gqa) { return (16 / gqa) < 4 ? 16 / gqa : 4; }
 
+// Longest INT2 chunk in pages: a decode wave holds the page ids of up to 64
+// pages in one VGPR, 64 * kDecodeWaves per chunk; the D = 128, one-group
+// kernels take a second batch in a second VGPR.
+int chunk_cap(const oscar_config& c) {
+  return (c.head_dim == 128 && c.group_size == 128 ? 128 : 64) * kDecodeWaves;
+}
+
 // Split-K plan.  Every (sequence, KV head) gets n_bf16_units workgroups for
 // its sink + recent pages and up to max_chunks INT2 chunks of
 // pages_per_chunk history pages; the chunk size is uniform so that shorter
@@ -115,9 +122,7 @@ Plan make_plan(const oscar_pool* pool, int batch, int max_len, bool bf16_only) {
     int ppc = (hist_pages + want - 1) / want;
     ppc = ((ppc + slots - 1) / slots) * slots;
     if (ppc < slots) ppc = slots;
-    // a wave holds the page ids of its (at most 64 / slots) tiles in one
-    // VGPR: at most 64 * kDecodeWaves pages per chunk
-    if (ppc > 64 * kDecodeWaves) ppc = 64 * kDecodeWaves;
+    if (ppc > chunk_cap(c)) ppc = chunk_cap(c);
     pl.pages_per_chunk = ppc;
     pl.max_chunks = (hist_pages + ppc - 1) / ppc;
   }
@@ -240,7 +245,7 @@ Plan cascade_plan(const oscar_pool* pool, int batch, int max_len, const CascPlan
 // ---- length-aware ("packed") split-K plan ----
 // With the host-side lengths the planner sizes every sequence's chunks from
 // its own history: one common chunk size ppc (a multiple of the tile, at most
-// 64 * kDecodeWaves pages) is chosen as the smallest that lets all units,
+// chunk_cap pages) is chosen as the smallest that lets all units,
 // BF16 units included, fit in R whole rounds of `target` workgroups, for the
 // smallest R that can hold them.  Sequence b then has n_bf16_units +
 // ceil(own_pages_b / ppc) units per KV head (own pages: its history past a
@@ -260,7 +265,7 @@ bool plan_packed(const oscar_pool* pool, int batch, int max_len, const int32_t* 
   const oscar_config& c = pool->cfg;
   const int hkv = c.num_kv_heads, slots = slots_for(pool->gqa), nb = base.n_bf16_units;
   const int target = env_int("OSCAR_TARGET_WGS", num_cus());
-  const int cap = 64 * kDecodeWaves;
+  const int cap = chunk_cap(c);
   int own[oscar::kMaxPackedSeqs], cch[oscar::kMaxPackedSeqs];
   for (int b = 0; b < batch; ++b) {
     // the kernel's clamps of the length

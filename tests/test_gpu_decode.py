@@ -171,6 +171,38 @@ def test_decode_multi_round_plan(gpu_lib, name, bf16_pages_per_unit, monkeypatch
     assert torch.equal(again.view(torch.int16), out.view(torch.int16))
 
 
+LONG_CHUNK_CASES = {
+    "d128-gqa4-long": CASES["d128-gqa4-long"],
+    "d128-gqa8-long": make_workload(QWEN, num_q_heads=16, num_kv_heads=2, batch=2, seq_lens=(20000, 9000), seed=13),
+    "d128-gqa2-long": make_workload(QWEN, num_q_heads=4, num_kv_heads=2, batch=1, seq_lens=(18000,), seed=14),
+}
+
+
+@pytest.mark.parametrize("plan", ["max-length", "host-lengths"])
+@pytest.mark.parametrize("name", list(LONG_CHUNK_CASES))
+def test_decode_long_chunks(gpu_lib, name, plan, monkeypatch):
+    """Chunks of up to 1,024 history pages (the planner aimed at 4
+    workgroups): each wave takes the ids of its tiles past the first 64 pages
+    from a second batch.  Sequences of 9,000-20,000 tokens give one full
+    chunk and a shorter last one; repeated calls are bitwise equal."""
+    monkeypatch.setenv("OSCAR_TARGET_WGS", "4")
+    wl = LONG_CHUNK_CASES[name]
+    log(f"case {name} ({plan} plan): chunks of up to 1,024 pages")
+    inp = draw_inputs(wl)
+    seqs = make_seqs(wl, inp)
+    pools = pool_io.build_pools(seqs, wl.num_kv_heads, wl.head_dim, wl.n_groups, wl.sink, wl.recent, seed=wl.seed)
+    host = list(wl.seq_lens) if plan == "host-lengths" else None
+    out, (pool, dev, lens, ws, max_len) = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k, host_lens=host)
+    ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
+    check_decode(out, ref, what=f"{name} ({plan} plan, long chunks)")
+    again = torch.zeros_like(out)
+    gpu_lib.oscar_decode_attention(pool, inp.q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"],
+                                   dev["bf16_pool"], dev["int2_pool"], to_dev(inp.calib.r_k), again, ws,
+                                   seq_lens_host=host)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+
+
 def test_decode_full_size_headline_sampled(gpu_lib):
     """Qwen3-8B-shaped layer at 100,000 tokens, in the launch configuration
     bench.py times; the oracle computes a sample of query heads."""
