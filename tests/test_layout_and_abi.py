@@ -141,16 +141,19 @@ def test_workspace_bytes_grows_with_batch_and_length():
     assert p.workspace_bytes(1, 100_000, bf16_only=True) > 0
 
 
-def test_decode_plan_chunk_limit():
+@pytest.mark.parametrize("group_size,chunk_pages", [(128, 1024), (64, 512)])
+def test_decode_plan_chunk_limit(group_size, chunk_pages):
     """The split-K planner gives one (sequence, KV head) at most 1024 INT2
-    chunks of at most 512 pages: a history of exactly 1024 x 512 pages fits,
-    one page more is rejected as unsupported before any launch."""
+    chunks, of at most 1024 pages at D = 128 with one scale group per head
+    (two batches of page ids per decode wave) and 512 pages otherwise: a
+    history of exactly 1024 chunks fits, one page more is rejected as
+    unsupported before any launch."""
     import ctypes
     import long_context_decode_oscar_amd as oscar
     lib = oscar.load()
-    p = oscar.OscarPool(_cfg())
+    p = oscar.OscarPool(_cfg(group_size=group_size))
     n = ctypes.c_size_t()
-    at_limit = 64 + 256 + 1024 * 512 * 16  # sink + recent + history tokens
+    at_limit = 64 + 256 + 1024 * chunk_pages * 16  # sink + recent + history tokens
     assert lib.oscar_decode_workspace_bytes(p.handle, 1, at_limit, 0, ctypes.byref(n)) == oscar.OSCAR_OK
     assert n.value > 0
     assert lib.oscar_decode_workspace_bytes(p.handle, 1, at_limit + 16, 0, ctypes.byref(n)) == \
