@@ -1105,9 +1105,13 @@ __global__ void __launch_bounds__(kThreads)
     ps.at(1);
 
     // ---- prologue: q' = q R_K (fp32), per-head int8 split, B operands
-    {
+    // (each slot's B operand is zero outside its own columns). With the q'
+    // prologue on waves 0 .. QWAVES-1 only those waves clear it: their LDS
+    // counter then orders every clear before the blocks written below; a
+    // clear by a later wave could land on a block already written.
+    if (qwave) {
       v4i* bqz = &sm.bq[0][0][0][0];
-      for (int x = tid; x < C::SLOTS * 3 * C::KW * 64; x += kThreads) bqz[x] = v4i{0, 0, 0, 0};
+      for (int x = tid; x < C::SLOTS * 3 * C::KW * 64; x += 64 * QWAVES) bqz[x] = v4i{0, 0, 0, 0};
     }
     if (qwave) {
       float qacc[GQA][4];
