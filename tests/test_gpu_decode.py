@@ -152,7 +152,7 @@ def test_decode_multi_round_plan(gpu_lib, name, bf16_pages_per_unit, monkeypatch
     than the GPU's CUs: the workgroup order that runs each XCD's INT2 chunks
     before its BF16 units, with one or three BF16 units per (sequence, KV
     head) and, in the ragged cases, chunks past a sequence's own history that
-    exit at once.  Repeated calls are bitwise equal."""
+    exit at once.  Nine calls are bitwise equal."""
     monkeypatch.setenv("OSCAR_TARGET_WGS", "1024")
     if bf16_pages_per_unit:
         monkeypatch.setenv("OSCAR_BF16_PAGES_PER_UNIT", bf16_pages_per_unit)
@@ -164,11 +164,16 @@ def test_decode_multi_round_plan(gpu_lib, name, bf16_pages_per_unit, monkeypatch
     out, (pool, dev, lens, ws, max_len) = _decode(gpu_lib, wl, seqs, inp.q, pools, inp.calib.r_k)
     ref, _ = oracle.decode_attention(seqs, inp.q.float().numpy(), inp.calib.r_k)
     check_decode(out, ref, what=f"{name} (multi-round plan)")
-    again = torch.zeros_like(out)
-    gpu_lib.oscar_decode_attention(pool, inp.q.cuda(), lens, max_len, dev["bf16_pt"], dev["int2_pt"],
-                                   dev["bf16_pool"], dev["int2_pool"], to_dev(inp.calib.r_k), again, ws)
-    torch.cuda.synchronize()
-    assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+    # several calls: with GQA <= 4 the q' prologue's waves meet at an LDS
+    # counter rather than a workgroup barrier, and a shared-memory write
+    # left outside that ordering shows as an occasional differing call
+    rk, qd = to_dev(inp.calib.r_k), inp.q.cuda()
+    for i in range(8):
+        again = torch.zeros_like(out)
+        gpu_lib.oscar_decode_attention(pool, qd, lens, max_len, dev["bf16_pt"], dev["int2_pt"],
+                                       dev["bf16_pool"], dev["int2_pool"], rk, again, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16)), f"call {i + 2} differs"
 
 
 LONG_CHUNK_CASES = {
